@@ -1,0 +1,211 @@
+"""CPU oracle for DyRA's one-step dynamic residual approximation (float64, numpy).
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the CPU
+baseline leg of the benchmark may import this module.  The product path
+(the HIP library and its Python binding) never calls it and shares no code
+with it.
+
+Source: "DyRA: Dynamic Residual Approximation for Efficient Matrix
+Multiplication in DNNs" (Chae, Chung, Lee, Kim).  Every function below follows
+one passage of that paper, cited by section / equation / algorithm.  The code
+is deliberately plain: each step of the algorithm is one numpy expression in
+the paper's order, in float64, with no blocking or fusion, so that it can be
+checked against the paper by eye.  Library routines (SVD, linear solve,
+least squares) serve as single steps.
+
+Notation (the paper's §2.2-2.4 / Algorithm 1 letters):
+    X      [n, c1]   activations of one instance (n tokens)
+    W      [c1, c2]  dense weight, product X @ W
+    W_hat            structured (here: rank-r_w truncated SVD) approximation of W
+    W_res            W - W_hat
+    R0     [r_c, c2] fixed initial right factor R^(0)
+    P_L    [c1, r_c] precomputed left projection (Eq. 7)
+    L1, R1           the one-step ALS factors L^(1), R^(1)
+The static rank is called ``r_w`` here and the correction rank ``r_c``; the
+paper's §2.2-2.4 calls the correction rank r, and Proposition 1 calls the
+static rank k.
+
+Readings taken where the paper is silent (all listed with the design notes):
+  * The structured approximation is the truncated SVD W_hat = U_r S_r V_r^T
+    (Appendix B, low-rank case); Sigma is folded into the left factor.
+  * R^(0) is the top-r_c right singular vectors of W_res (Appendix D default),
+    obtained here from an SVD of W_res itself.
+  * One lambda >= 0 per layer, used in both ridge Gram matrices (§2.2
+    footnote 2; Algorithm 1 lines 5 and 12).
+  * Where lambda = 0 and L^(1)'s Gram is singular (fewer tokens than the
+    correction rank), L^(1) R^(1) is taken as its lambda -> 0+ limit, the
+    minimum-norm least-squares solution, which is unique as a product.
+  * No bias and no output scale (Eq. 6 and Algorithm 1 carry neither).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+
+@dataclasses.dataclass
+class OraclePlan:
+    """Output of Algorithm 1's Offline Preparation for one layer (float64)."""
+    W: np.ndarray        # [c1, c2] the dense weight, as given (upcast)
+    W_hat: np.ndarray    # [c1, c2] structured approximation
+    W_res: np.ndarray    # [c1, c2] residual weight W - W_hat
+    A_s: np.ndarray      # [c1, r_w] left static factor U_r S_r
+    V_s: np.ndarray      # [c2, r_w] right static factor V_r
+    R0: np.ndarray       # [r_c, c2] fixed initial right factor
+    P_L: np.ndarray      # [c1, r_c] precomputed left projection
+    lam: float
+    r_w: int
+    r_c: int
+
+
+def truncated_svd(W: np.ndarray, r: int):
+    """Rank-r truncated SVD of W as (L, R) = (U_r S_r, V_r^T).
+
+    DyRA paper, Appendix B (Low-Rank Approximation): W_hat = U_r S_r V_r^T,
+    the best rank-r approximation in Frobenius norm, with L = U_r S_r and
+    R = V_r^T.
+    """
+    U, S, Vt = np.linalg.svd(np.asarray(W, dtype=np.float64), full_matrices=False)
+    return U[:, :r] * S[:r], Vt[:r, :]
+
+
+def offline_preparation(W: np.ndarray, r_w: int, r_c: int, lam: float = 0.0,
+                        R0: Optional[np.ndarray] = None) -> OraclePlan:
+    """Algorithm 1, procedure Offline Preparation(W, k, r, lambda).
+
+    1. structured approximation W_hat of W (Appendix B truncated SVD, rank r_w);
+    2. W_res <- W - W_hat                                   (§2.1 Eq. 1);
+    3. fix R^(0): by default the top-r_c right singular vectors of W_res
+       (Appendix D); a caller may pass another R^(0) (§2.2 uses a Gaussian one);
+    4. P_L <- (W_res R0^T)(R0 R0^T + lambda I)^-1           (Eq. 7, Alg. 1 l.5).
+    """
+    W = np.asarray(W, dtype=np.float64)
+    c1, c2 = W.shape
+    if not (r_w >= 0 and r_c >= 0 and r_w + r_c <= min(c1, c2)):
+        raise ValueError("ranks out of range")
+    if r_w > 0:
+        A_s, Vt_s = truncated_svd(W, r_w)
+    else:
+        A_s, Vt_s = np.zeros((c1, 0)), np.zeros((0, c2))
+    W_hat = A_s @ Vt_s
+    W_res = W - W_hat
+    if R0 is None:
+        if r_c > 0:
+            _, _, Vt_res = np.linalg.svd(W_res, full_matrices=False)
+            R0 = Vt_res[:r_c, :]
+        else:
+            R0 = np.zeros((0, c2))
+    R0 = np.asarray(R0, dtype=np.float64)
+    gram = R0 @ R0.T + lam * np.eye(r_c)
+    # P_L = (W_res R0^T) gram^-1, written as a solve against gram^T = gram
+    P_L = np.linalg.solve(gram.T, (W_res @ R0.T).T).T if r_c > 0 else np.zeros((c1, 0))
+    return OraclePlan(W=W, W_hat=W_hat, W_res=W_res, A_s=A_s, V_s=Vt_s.T.copy(), R0=R0,
+                      P_L=P_L, lam=float(lam), r_w=r_w, r_c=r_c)
+
+
+def right_factor(L1: np.ndarray, X: np.ndarray, W_res: np.ndarray, lam: float) -> np.ndarray:
+    """R^(1) <- (L1^T L1 + lambda I)^-1 (L1^T X) W_res   (Eq. 5, Alg. 1 line 12).
+
+    The product (L1^T X) W_res is formed in the algorithm's order (the input is
+    first projected onto L1, then multiplied by W_res; §2.2).  For lambda = 0
+    and a singular Gram matrix the minimum-norm least-squares solution of
+    min ||X W_res - L1 R|| is returned (the lambda -> 0+ limit).
+    """
+    r_c = L1.shape[1]
+    gram = L1.T @ L1 + lam * np.eye(r_c)
+    rhs = (L1.T @ X) @ W_res
+    if lam == 0.0 and np.linalg.matrix_rank(L1) < r_c:
+        return np.linalg.lstsq(L1, X @ W_res, rcond=None)[0]
+    return np.linalg.solve(gram, rhs)
+
+
+def inference_instance(X: np.ndarray, plan: OraclePlan) -> np.ndarray:
+    """Algorithm 1, procedure Inference, for one instance X [n, c1].
+
+    line 10: Y_base <- X W_hat
+    line 11: L1 <- X P_L                             (Eq. 7)
+    line 12: R1 <- (L1^T L1 + lambda I)^-1 (L1^T X) W_res   (Eq. 5)
+    line 13: Y <- Y_base + L1 R1                     (Eq. 6)
+    """
+    X = np.asarray(X, dtype=np.float64)
+    Y_base = X @ plan.W_hat
+    if plan.r_c == 0:
+        return Y_base
+    L1 = X @ plan.P_L
+    R1 = right_factor(L1, X, plan.W_res, plan.lam)
+    return Y_base + L1 @ R1
+
+
+def inference(X: np.ndarray, B: int, n: int, plan: OraclePlan) -> np.ndarray:
+    """Algorithm 1 Inference over B independent instances of n tokens.
+
+    X is [B*n, c1] with instance b in rows [b*n, (b+1)*n).  The paper solves the
+    r x r system "for each batch instance" (§2.4), so every instance gets its
+    own L1, R1.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    if X.shape[0] != B * n:
+        raise ValueError("X rows must equal B*n")
+    Y = np.empty((B * n, plan.W.shape[1]))
+    for b in range(B):
+        rows = slice(b * n, (b + 1) * n)
+        Y[rows] = inference_instance(X[rows], plan)
+    return Y
+
+
+def factors_instance(X: np.ndarray, plan: OraclePlan):
+    """(L1, R1) of one instance, for tests that look inside the correction."""
+    X = np.asarray(X, dtype=np.float64)
+    L1 = X @ plan.P_L
+    return L1, right_factor(L1, X, plan.W_res, plan.lam)
+
+
+def als(X: np.ndarray, W_res: np.ndarray, R0: np.ndarray, lam: float, half_steps: int):
+    """Alternating least squares on min ||X W_res - L R||_F^2 (Eq. 3-5).
+
+    Starting from R^(0), alternate the L update (Eq. 4) and the R update
+    (Eq. 5), each with the ridge term of footnote 2; ``half_steps`` counts
+    single updates, so 2 = one ALS iteration (t = 1), 3 = t 1.5 (L, R, L),
+    4 = t 2 (§3.3 ablation).  Returns (L, R) after the last update; R is the
+    last R computed (R^(0) if none).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    r_c = R0.shape[0]
+    R = np.asarray(R0, dtype=np.float64)
+    L = None
+    for h in range(half_steps):
+        if h % 2 == 0:
+            gram = R @ R.T + lam * np.eye(r_c)
+            L = X @ np.linalg.solve(gram.T, (W_res @ R.T).T).T
+        else:
+            R = right_factor(L, X, W_res, lam)
+    return L, R
+
+
+def dense_product(X: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """The exact product X W that DyRA approximates (§2.1 Eq. 2)."""
+    return np.asarray(X, dtype=np.float64) @ np.asarray(W, dtype=np.float64)
+
+
+def rel_fro(A: np.ndarray, B: np.ndarray) -> float:
+    """||A - B||_F / ||B||_F (the normalised Frobenius error of §2.3 / App. E.4)."""
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    return float(np.linalg.norm(A - B) / np.linalg.norm(B))
+
+
+def weight_only(X: np.ndarray, plan: OraclePlan) -> np.ndarray:
+    """The static approximation X W_hat alone (§2.1, conventional methods)."""
+    return np.asarray(X, dtype=np.float64) @ plan.W_hat
+
+
+def optimal_rank_error(P: np.ndarray, r: int) -> float:
+    """||P - [P]_r||_F for the best rank-r approximation [P]_r (Eckart-Young, §2.2).
+
+    The optimum of Eq. 3 is the truncated SVD of the realised product; its
+    error is the root-sum-square of the discarded singular values.
+    """
+    s = np.linalg.svd(np.asarray(P, dtype=np.float64), compute_uv=False)
+    return float(np.sqrt(np.sum(s[r:] ** 2)))

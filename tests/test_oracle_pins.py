@@ -1,0 +1,366 @@
+"""Pins of the CPU oracle against what the DyRA paper and linear algebra fix.
+
+Each test ties the oracle (oracle/dyra_oracle.py) to something other than its
+own formulas: a hand-worked example, a closed form printed by the paper
+(Proposition 1 / Eq. 8 / Eq. 16), a theorem (Eckart-Young, least-squares
+optimality), a known construction (W with a prescribed SVD) or brute force on
+tiny shapes.  The checks are chosen so that a dropped ridge term, a wrong R0
+slice, a swapped operand or a wrong sign fails at least one of them.
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as orc
+from structured_rank_matmul_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------ helpers
+
+def known_svd_weight(c1, c2, s, seed):
+    """W = Q1 diag(s) Q2^T with known Haar factors (independent of any SVD routine)."""
+    rng = synth.rng_for(seed, 77, c1 * 1000 + c2, 0)
+    m = min(c1, c2)
+    q1 = synth.haar_orthogonal(rng, c1, m)
+    q2 = synth.haar_orthogonal(rng, c2, m)
+    return (q1 * s) @ q2.T, q1, q2
+
+
+def gaussian(shape, seed, scale=1.0):
+    rng = synth.rng_for(seed, 78, shape[0] * 1000 + shape[1], 1)
+    return scale * rng.standard_normal(shape)
+
+
+def qr_lstsq(A, B):
+    """Least squares min ||A Z - B||_F via Householder QR (numpy.linalg.qr) and back-substitution."""
+    Q, R = np.linalg.qr(A, mode="reduced")
+    rhs = Q.T @ B
+    n = R.shape[1]
+    Z = np.zeros((n, B.shape[1]))
+    for i in range(n - 1, -1, -1):
+        Z[i] = (rhs[i] - R[i, i + 1:] @ Z[i + 1:]) / R[i, i]
+    return Z
+
+
+def read_golden(name):
+    blocks, cur = {}, None
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            tok = line.split()
+            if tok[0].isalpha() or "_" in tok[0]:
+                key = tok[0]
+                if len(tok) == 2:
+                    blocks[key] = int(tok[1])
+                    cur = None
+                else:
+                    blocks[key] = []
+                    cur = key
+            else:
+                blocks[cur].append([Fraction(t) for t in tok])
+    return {k: (np.array([[float(x) for x in row] for row in v]) if isinstance(v, list) else v)
+            for k, v in blocks.items()}
+
+
+# ------------------------------------------------------------------ golden hand example
+
+@pytest.mark.parametrize("lam,key", [(0.0, "Y_lam0"), (1.0, "Y_lam1")])
+def test_hand_worked_example(lam, key):
+    g = read_golden("hand_permuted3.txt")
+    plan = orc.offline_preparation(g["W"], g["r_w"], g["r_c"], lam)
+    Y = orc.inference(g["X"], 1, 2, plan)
+    np.testing.assert_allclose(Y, g[key], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(orc.dense_product(g["X"], g["W"]), g["XW"], atol=0)
+    if lam == 0.0:
+        assert abs(np.linalg.norm(Y - g["XW"]) - np.sqrt(2.0)) < 1e-13
+
+
+# ------------------------------------------------------------------ P1 full rank
+
+@pytest.mark.parametrize("c1,c2", [(7, 5), (5, 7), (12, 12)])
+def test_full_rank_static_is_exact(c1, c2):
+    W = gaussian((c1, c2), 1)
+    X = gaussian((9, c1), 2)
+    plan = orc.offline_preparation(W, min(c1, c2), 0)
+    Y = orc.inference(X, 3, 3, plan)
+    assert orc.rel_fro(Y, X @ W) < 1e-13
+
+
+# ------------------------------------------------------------------ P2 isotropic / Eq. 16
+
+@pytest.mark.parametrize("c1,c2,r_w,r_c", [(8, 10, 2, 3), (10, 6, 1, 2), (12, 12, 4, 4)])
+def test_isotropic_input_reduces_to_static_rank_sum(c1, c2, r_w, r_c):
+    """Proposition 1, isotropic case (App. C Eq. 16): X^T X = I gives R1 = V_{k+1:k+r}^T,
+    so DyRA equals the static rank-(r_w + r_c) truncated SVD."""
+    m = min(c1, c2)
+    s = np.arange(m, 0, -1, dtype=float) + 0.5
+    W, q1, q2 = known_svd_weight(c1, c2, s, 3)
+    X = np.linalg.qr(gaussian((20, c1), 4))[0]        # orthonormal columns, X^T X = I
+    plan = orc.offline_preparation(W, r_w, r_c, 0.0)
+    L1, R1 = orc.factors_instance(X, plan)
+    V_next = q2[:, r_w:r_w + r_c].T
+    # R1 equals V_{r_w+1:r_w+r_c}^T row by row up to the sign of each singular pair
+    for i in range(r_c):
+        assert min(np.abs(R1[i] - V_next[i]).max(), np.abs(R1[i] + V_next[i]).max()) < 1e-10
+    W_sum = (q1[:, :r_w + r_c] * s[:r_w + r_c]) @ q2[:, :r_w + r_c].T
+    np.testing.assert_allclose(orc.inference(X, 1, 20, plan), X @ W_sum, atol=1e-10)
+
+
+# ------------------------------------------------------------------ P3 Eq. 8 closed form
+
+@pytest.mark.parametrize("lam_zero", [True])
+@pytest.mark.parametrize("n,c1,c2,r_w,r_c", [(30, 12, 9, 3, 2), (16, 10, 14, 2, 4)])
+def test_prop1_closed_form(n, c1, c2, r_w, r_c, lam_zero):
+    """Proposition 1, Eq. 8: one-step DyRA = X [A_k, A_r][V_k^T; R1] with
+    R1 = (A_r^T X^T X A_r)^-1 A_r^T X^T X W_res and A_r = U_{k+1:k+r} S_{k+1:k+r}."""
+    m = min(c1, c2)
+    s = 2.0 ** (-np.arange(m) / 2.0)
+    W, q1, q2 = known_svd_weight(c1, c2, s, 5)
+    X = gaussian((n, c1), 6) * np.exp(gaussian((1, c1), 7))
+    A_k = q1[:, :r_w] * s[:r_w]
+    A_r = q1[:, r_w:r_w + r_c] * s[r_w:r_w + r_c]
+    W_res = (q1[:, r_w:] * s[r_w:]) @ q2[:, r_w:].T
+    XtX = X.T @ X
+    R1 = np.linalg.inv(A_r.T @ XtX @ A_r) @ (A_r.T @ XtX @ W_res)
+    Y_closed = X @ np.hstack([A_k, A_r]) @ np.vstack([q2[:, :r_w].T, R1])
+    plan = orc.offline_preparation(W, r_w, r_c, 0.0)
+    np.testing.assert_allclose(orc.inference(X, 1, n, plan), Y_closed, rtol=0,
+                               atol=1e-10 * np.abs(Y_closed).max())
+
+
+# ------------------------------------------------------------------ P4 Eckart-Young
+
+def _floor_eigh(P, r):
+    """Best rank-r error of P from the eigenvalues of P^T P (an independent routine)."""
+    ev = np.sort(np.clip(np.linalg.eigvalsh(P.T @ P), 0, None))[::-1]
+    return np.sqrt(np.sum(ev[r:]))
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.3])
+def test_correction_never_beats_eckart_young(lam):
+    c1, c2, r_w, r_c, B, n = 16, 20, 4, 3, 5, 12
+    W = synth.random_weight(c1, c2, 11).astype(np.float64)
+    X = synth.x_logcols(synth.rng_for(0, 79, 0, 1), B * n, c1)
+    plan = orc.offline_preparation(W, r_w, r_c, lam)
+    for b in range(B):
+        Xb = X[b * n:(b + 1) * n]
+        P = Xb @ plan.W_res
+        L1, R1 = orc.factors_instance(Xb, plan)
+        err = np.linalg.norm(P - L1 @ R1)
+        assert err >= _floor_eigh(P, r_c) * (1 - 1e-12) - 1e-12
+        # the whole output is rank <= r_w + r_c: it cannot beat that floor for X W either
+        Yb = orc.inference_instance(Xb, plan)
+        assert np.linalg.norm(Xb @ W - Yb) >= _floor_eigh(Xb @ W, r_w + r_c) * (1 - 1e-12) - 1e-12
+
+
+def test_oracle_floor_matches_independent_routine():
+    P = gaussian((13, 9), 12)
+    for r in range(0, 9):
+        assert abs(orc.optimal_rank_error(P, r) - _floor_eigh(P, r)) < 1e-10
+
+
+def test_als_error_is_monotone_and_approaches_floor():
+    """Each ALS half-step is an exact least-squares minimisation at lambda = 0,
+    so the error cannot increase; with enough steps it reaches the rank-r_c
+    floor (Fig. 2 / App. E.3 behaviour, here on synthetic data)."""
+    c1, c2, r_w, r_c, n = 24, 30, 6, 4, 40
+    W = synth.random_weight(c1, c2, 13).astype(np.float64)
+    X = gaussian((n, c1), 14) * np.exp(2 * gaussian((1, c1), 15))
+    plan = orc.offline_preparation(W, r_w, r_c, 0.0)
+    P = X @ plan.W_res
+    errs = []
+    for h in range(2, 41, 2):
+        L, R = orc.als(X, plan.W_res, plan.R0, 0.0, h)
+        errs.append(np.linalg.norm(P - L @ R))
+    assert all(b <= a * (1 + 1e-10) for a, b in zip(errs, errs[1:]))
+    assert errs[-1] <= _floor_eigh(P, r_c) * (1 + 1e-3)
+    # one ALS iteration (two half-steps) is exactly what Inference computes
+    L, R = orc.als(X, plan.W_res, plan.R0, 0.0, 2)
+    np.testing.assert_allclose(orc.inference_instance(X, plan), X @ plan.W_hat + L @ R, atol=1e-10)
+
+
+# ------------------------------------------------------------------ P5 never worse than weight-only
+
+@pytest.mark.parametrize("lam", [0.0, 1e-3, 1.0, 100.0])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_dyra_not_worse_than_weight_only(lam, seed):
+    c1, c2, r_w, r_c, B, n = 32, 24, 5, 4, 4, 10
+    W = synth.random_weight(c1, c2, 20 + seed).astype(np.float64)
+    X = gaussian((B * n, c1), 21 + seed) * np.exp(gaussian((1, c1), 22))
+    plan = orc.offline_preparation(W, r_w, r_c, lam)
+    XW = X @ W
+    for b in range(B):
+        rows = slice(b * n, (b + 1) * n)
+        e_dyra = np.linalg.norm(XW[rows] - orc.inference_instance(X[rows], plan))
+        e_w = np.linalg.norm(XW[rows] - orc.weight_only(X[rows], plan))
+        assert e_dyra <= e_w * (1 + 1e-12)
+
+
+# ------------------------------------------------------------------ P6 single token
+
+@pytest.mark.parametrize("lam", [0.0, 0.5])
+def test_single_token_sherman_morrison(lam):
+    c1, c2, r_w, r_c = 20, 14, 3, 5
+    W = synth.random_weight(c1, c2, 30).astype(np.float64)
+    x = gaussian((1, c1), 31)
+    plan = orc.offline_preparation(W, r_w, r_c, lam)
+    l = x @ plan.P_L
+    ll = (l @ l.T).item()
+    s = ll / (lam + ll)
+    expect = x @ plan.W_hat + s * (x @ plan.W_res)
+    np.testing.assert_allclose(orc.inference_instance(x, plan), expect, atol=1e-12)
+    if lam == 0.0:  # the correction restores the exact product
+        np.testing.assert_allclose(orc.inference_instance(x, plan), x @ W, atol=1e-12)
+
+
+# ------------------------------------------------------------------ P7 fewer tokens than rank: dual form
+
+@pytest.mark.parametrize("n", [2, 3, 5])
+def test_primal_equals_push_through_dual(n):
+    c1, c2, r_w, r_c, lam = 18, 16, 3, 6, 0.25
+    W = synth.random_weight(c1, c2, 40).astype(np.float64)
+    X = gaussian((n, c1), 41 + n)
+    plan = orc.offline_preparation(W, r_w, r_c, lam)
+    L1 = X @ plan.P_L
+    dual = L1 @ L1.T @ np.linalg.inv(L1 @ L1.T + lam * np.eye(n)) @ (X @ plan.W_res)
+    np.testing.assert_allclose(orc.inference_instance(X, plan), X @ plan.W_hat + dual, atol=1e-11)
+
+
+def test_lambda_zero_underdetermined_is_projection():
+    """lambda = 0, n < r_c: L1 R1 is the projection of X W_res onto span(L1) (min-norm LS)."""
+    c1, c2, r_w, r_c, n = 18, 16, 3, 6, 4
+    W = synth.random_weight(c1, c2, 42).astype(np.float64)
+    X = gaussian((n, c1), 43)
+    plan = orc.offline_preparation(W, r_w, r_c, 0.0)
+    L1 = X @ plan.P_L
+    Q = np.linalg.qr(L1)[0]
+    proj = Q @ (Q.T @ (X @ plan.W_res))
+    np.testing.assert_allclose(orc.inference_instance(X, plan), X @ plan.W_hat + proj, atol=1e-11)
+
+
+# ------------------------------------------------------------------ P8 exact low-rank W
+
+def test_exact_when_rank_equals_r_w_plus_r_c():
+    c1, c2, r_w, r_c = 14, 11, 3, 4
+    s = np.zeros(11)
+    s[:r_w + r_c] = np.linspace(5, 1, r_w + r_c)
+    W, _, _ = known_svd_weight(c1, c2, s, 50)
+    X = gaussian((3 * 9, c1), 51)
+    plan = orc.offline_preparation(W, r_w, r_c, 0.0)
+    assert orc.rel_fro(orc.inference(X, 3, 9, plan), X @ W) < 1e-12
+
+
+# ------------------------------------------------------------------ P9 invariants
+
+def test_instances_independent_and_equivariant():
+    c1, c2, r_w, r_c, B, n = 16, 12, 3, 2, 3, 7
+    W = synth.random_weight(c1, c2, 60).astype(np.float64)
+    X = gaussian((B * n, c1), 61)
+    plan = orc.offline_preparation(W, r_w, r_c, 0.0)
+    Y = orc.inference(X, B, n, plan)
+    X2 = X.copy()
+    X2[n:2 * n] = gaussian((n, c1), 62)                      # change instance 1 only
+    Y2 = orc.inference(X2, B, n, plan)
+    np.testing.assert_array_equal(Y[:n], Y2[:n])
+    np.testing.assert_array_equal(Y[2 * n:], Y2[2 * n:])
+    perm = np.random.default_rng(0).permutation(n)
+    Yp = orc.inference(X[perm], 1, n, plan)
+    np.testing.assert_allclose(Yp, Y[:n][perm], atol=1e-12)
+    np.testing.assert_allclose(orc.inference(3.5 * X, B, n, plan), 3.5 * Y, rtol=1e-11, atol=1e-11)
+    plan2 = orc.offline_preparation(-2.0 * W, r_w, r_c, 0.0)
+    np.testing.assert_allclose(orc.inference(X, B, n, plan2), -2.0 * Y, rtol=1e-10, atol=1e-10)
+
+
+def test_r0_rotation_and_sign_invariance():
+    """Only the row space of R0 matters: a rotation of R0 (any invertible mix) leaves Y unchanged."""
+    c1, c2, r_w, r_c, n = 16, 12, 3, 3, 9
+    W = synth.random_weight(c1, c2, 63).astype(np.float64)
+    X = gaussian((n, c1), 64)
+    plan = orc.offline_preparation(W, r_w, r_c, 0.0)
+    Q = np.linalg.qr(gaussian((r_c, r_c), 65))[0]
+    plan_rot = orc.offline_preparation(W, r_w, r_c, 0.0, R0=Q @ plan.R0)
+    np.testing.assert_allclose(orc.inference(X, 1, n, plan_rot), orc.inference(X, 1, n, plan), atol=1e-11)
+
+
+# ------------------------------------------------------------------ P10 known spectrum
+
+def test_generated_weight_has_prescribed_spectrum():
+    w = synth.WORKLOADS["linear384_fp32"]
+    spec = w.layers[0]
+    W32, s = synth.make_weight(w, spec)
+    sv = np.linalg.svd(W32.astype(np.float64), compute_uv=False)
+    np.testing.assert_allclose(sv, s, rtol=2e-5, atol=1e-6 * s[0])
+    np.testing.assert_allclose(s, np.arange(1, 385) ** -0.7)
+
+
+def test_static_factor_matches_known_construction():
+    c1, c2, r_w = 40, 30, 7
+    s = 1.0 / np.arange(1, 31)
+    W, q1, q2 = known_svd_weight(c1, c2, s, 70)
+    plan = orc.offline_preparation(W, r_w, 2, 0.0)
+    np.testing.assert_allclose(plan.W_hat, (q1[:, :r_w] * s[:r_w]) @ q2[:, :r_w].T, atol=1e-12)
+    # R0 spans the next two right singular vectors of W
+    P = plan.R0.T @ plan.R0
+    np.testing.assert_allclose(P, q2[:, r_w:r_w + 2] @ q2[:, r_w:r_w + 2].T, atol=1e-10)
+
+
+# ------------------------------------------------------------------ P11 brute force, tiny shapes
+
+def _tiny_cases():
+    out = []
+    for (c1, c2) in [(4, 6), (6, 4), (5, 5), (8, 3)]:
+        m = min(c1, c2)
+        for r_w in range(0, m):
+            for r_c in range(1, m - r_w + 1):
+                for n in (r_c, 6):
+                    out.append((c1, c2, r_w, r_c, n))
+    return out
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.7])
+def test_brute_force_tiny(lam):
+    """Form X W_res explicitly and solve both ridge least-squares half-steps by QR of
+    the stacked systems [R0^T; sqrt(lam) I] and [L1; sqrt(lam) I]."""
+    count = 0
+    for (c1, c2, r_w, r_c, n) in _tiny_cases():
+        seed = c1 * 1000 + c2 * 100 + r_w * 10 + r_c + n
+        W = gaussian((c1, c2), seed)
+        X = gaussian((n, c1), seed + 1)
+        plan = orc.offline_preparation(W, r_w, r_c, lam)
+        P = X @ plan.W_res
+        # L step: min ||P - L R0||^2 + lam ||L||^2  ->  stacked LS for L^T
+        A = np.vstack([plan.R0.T, np.sqrt(lam) * np.eye(r_c)])
+        L = qr_lstsq(A, np.vstack([P.T, np.zeros((r_c, n))])).T
+        np.testing.assert_allclose(L, X @ plan.P_L, atol=1e-10)
+        # R step: min ||P - L R||^2 + lam ||R||^2
+        if lam == 0.0 and np.linalg.matrix_rank(L) < r_c:
+            LR = L @ np.linalg.pinv(L) @ P
+        else:
+            A = np.vstack([L, np.sqrt(lam) * np.eye(r_c)])
+            LR = L @ qr_lstsq(A, np.vstack([P, np.zeros((r_c, c2))]))
+        Y = orc.inference_instance(X, plan)
+        np.testing.assert_allclose(Y, X @ plan.W_hat + LR, atol=1e-9 * max(1.0, np.abs(Y).max()))
+        # no random perturbation of R1 lowers the ridge objective
+        L1, R1 = orc.factors_instance(X, plan)
+        obj = np.linalg.norm(P - L1 @ R1) ** 2 + lam * np.linalg.norm(R1) ** 2
+        rng = np.random.default_rng(seed)
+        for _ in range(5):
+            D = 1e-3 * rng.standard_normal(R1.shape)
+            obj2 = np.linalg.norm(P - L1 @ (R1 + D)) ** 2 + lam * np.linalg.norm(R1 + D) ** 2
+            assert obj2 >= obj - 1e-12 * max(1.0, obj)
+        count += 1
+    assert count > 40
+
+
+def test_rank_arguments_validated():
+    W = gaussian((5, 4), 90)
+    with pytest.raises(ValueError):
+        orc.offline_preparation(W, 3, 2)
+    with pytest.raises(ValueError):
+        orc.inference(gaussian((5, 5), 91), 2, 3, orc.offline_preparation(W, 1, 1))
