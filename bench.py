@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the DyRA layer forward on one MI355X.
+
+One step = dyra_forward over every layer of the workload (default: the
+DINOv3-ViT-L-like block, qkv 1024->3072, fc1 1024->4096, fc2 4096->1024 on
+128 images x 201 tokens, r = 256, k = 64, bf16) with inputs resident in HBM.
+Prints one JSON line with tokens/s, the speedup over a dense bf16 GEMM of the
+same shapes (hipBLASLt through torch), the relative Frobenius error against
+the float64 oracle on sampled instances, the roofline of the dominant kernel
+and the oracle's own throughput on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s
+PEAK_FP32 = 157.3e12    # MI355X fp32 matrix, FLOP/s
+PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
+
+
+def stage_flops(spec, B, n):
+    """Algorithmic FLOPs of each kernel of the primal path for one layer call."""
+    N = B * n
+    c1, c2, r, k = spec.c1, spec.c2, spec.r, spec.k
+    return {
+        "left": 2.0 * N * c1 * k,
+        "gram_q": 2.0 * N * k * k + 2.0 * N * k * k,
+        "mprime": 2.0 * N * k * c1,
+        "right": 2.0 * B * k * c1 * c2,
+        "output": 2.0 * N * c1 * r + 2.0 * N * (r + k) * c2,
+    }
+
+
+def dyra_flops(spec, B, n):
+    return sum(stage_flops(spec, B, n).values())
+
+
+def time_loop(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / steps
+
+
+def cpu_baseline(workload, plans_orc, X_host, budget_s):
+    """Oracle inference on the first instances of every layer until ~budget_s of CPU time."""
+    import oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    n = workload.n
+    done, t_total = 0, 0.0
+    while done < workload.B:
+        t0 = time.perf_counter()
+        for li, spec in enumerate(workload.layers):
+            Xb = X_host[li][done * n:(done + 1) * n]
+            orc.inference(Xb, 1, n, plans_orc[li])
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    tokens = done * n
+    return {"value": tokens / t_total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {workload.B} instances ({tokens} tokens) through all {len(workload.layers)} "
+                      f"layers, float64 numpy, {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="vitl_block")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time on the host")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--verbose", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the DyRA layer path here is a "
+              f"single-GPU kernel path and has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import torch.nn.functional as F
+
+    import oracle as orc
+    from structured_rank_matmul_amd import dyra, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    B, n, N = w.B, w.n, w.B * w.n
+    log = (lambda *a: print(*a, file=sys.stderr, flush=True)) if args.verbose else (lambda *a: None)
+
+    layers = []
+    for spec in w.layers:
+        W, _ = synth.make_weight(w, spec)
+        X = synth.make_activations(w, spec)
+        t0 = time.perf_counter()
+        plan = dyra.dyra_prepare(W, spec.r, spec.k, 0.0, w.dtype, 0)
+        log(f"prepared {spec.name} in {time.perf_counter() - t0:.1f} s")
+        if w.dtype == "bf16":
+            xd = torch.from_numpy(np.ascontiguousarray(X.data).view(np.int16)).view(torch.bfloat16).to(dev)
+        else:
+            xd = torch.from_numpy(X.data).to(dev)
+        Wd = torch.from_numpy(W).to(dev).to(tdt)           # [c1, c2]
+        Wt = Wd.t().contiguous()                             # [c2, c1], nn.Linear layout
+        layers.append(dict(spec=spec, W=W, X=X, plan=plan, xd=xd, Wd=Wd.contiguous(), Wt=Wt,
+                           y=torch.empty((N, spec.c2), dtype=tdt, device=dev),
+                           yd=torch.empty((N, spec.c2), dtype=tdt, device=dev),
+                           ws=dyra.alloc_workspace(plan, B, n)))
+    stream = torch.cuda.current_stream()
+
+    def dyra_step():
+        for L in layers:
+            dyra.dyra_forward(L["xd"], B, n, L["plan"], L["y"], L["ws"], stream)
+
+    def dense_linear():
+        for L in layers:
+            torch.matmul(L["xd"], L["Wd"], out=L["yd"])
+
+    def dense_nt():
+        for L in layers:
+            F.linear(L["xd"], L["Wt"])
+
+    def dense_ref():
+        for L in layers:
+            dyra.dyra_dense_ref(L["xd"], L["Wt"], L["yd"], stream)
+
+    t_dyra = time_loop(dyra_step, args.steps, args.warmup, stream)
+    t_dense_nn = time_loop(dense_linear, args.steps, args.warmup, stream)
+    t_dense_nt = time_loop(dense_nt, args.steps, args.warmup, stream)
+    t_dense = min(t_dense_nn, t_dense_nt)
+    t_dense_ref = time_loop(dense_ref, max(5, args.steps // 5), 2, stream)
+    log(f"t_dyra {t_dyra * 1e6:.1f} us  dense nn {t_dense_nn * 1e6:.1f} us  nt {t_dense_nt * 1e6:.1f} us  "
+        f"dense_ref {t_dense_ref * 1e6:.1f} us")
+
+    # ---- per-kernel durations with events on the launch stream
+    reps = max(5, args.steps // 5)
+    stage_time, stage_fl = {}, {}
+    for L in layers:
+        names = dyra.stage_names(L["plan"], n)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        acc = np.zeros(len(names))
+        for it in range(reps + 1):
+            dyra.dyra_forward_timed(L["xd"], B, n, L["plan"], L["y"], L["ws"], evs, stream)
+            torch.cuda.synchronize()
+            if it == 0:
+                continue
+            acc += [evs[i].elapsed_time(evs[i + 1]) / 1e3 for i in range(len(names))]
+        fl = stage_flops(L["spec"], B, n)
+        per = {}
+        for i, nm in enumerate(names):
+            d = acc[i] / reps
+            per[nm] = d
+            stage_time[nm] = stage_time.get(nm, 0.0) + d
+            stage_fl[nm] = stage_fl.get(nm, 0.0) + fl.get(nm, 0.0)
+        L["stages"] = per
+        log(f"{L['spec'].name}: " + "  ".join(f"{k} {v * 1e6:.1f}us" for k, v in per.items()))
+    dom = max(stage_time, key=stage_time.get)
+    peak = PEAK_BF16 if w.dtype == "bf16" else PEAK_FP32
+    launches = len(layers)
+    achieved = stage_fl[dom] / stage_time[dom] / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak / 1e12, "unit": "TFLOP/s",
+                "frac": round(achieved * 1e12 / peak, 4), "traffic": None,
+                "kernel": f"{dom}_kernel", "launches_per_step": launches,
+                "avg_launch_us": round(stage_time[dom] / launches * 1e6, 2)}
+
+    # ---- parity on sampled instances
+    parity = {}
+    if not args.no_parity:
+        sample = [0, B // 2, B - 1]
+        worst, worst_gap = 0.0, 0.0
+        for L in layers:
+            spec = L["spec"]
+            op = orc.offline_preparation(L["W"].astype(np.float64), spec.r, spec.k, 0.0)
+            L["orc"] = op
+            rows = np.concatenate([np.arange(b * n, (b + 1) * n) for b in sample])
+            Xs = L["X"].exact[rows]
+            ref = orc.inference(Xs, len(sample), n, op)
+            y = L["y"].float().cpu().numpy().astype(np.float64)[rows]
+            exact = Xs @ L["W"].astype(np.float64)
+            err = orc.rel_fro(y, ref)
+            e_gpu, e_orc = orc.rel_fro(y, exact), orc.rel_fro(ref, exact)
+            gap = abs(e_gpu - e_orc) / e_orc
+            parity[spec.name] = {"rel_fro_vs_oracle": float(f"{err:.3e}"), "e_dyra": round(e_gpu, 5),
+                                 "e_dyra_oracle": round(e_orc, 5),
+                                 "e_weight_only": round(orc.rel_fro(orc.weight_only(Xs, op), exact), 5)}
+            worst, worst_gap = max(worst, err), max(worst_gap, gap)
+        parity["worst_rel_fro"] = float(f"{worst:.3e}")
+        parity["worst_own_error_gap"] = float(f"{worst_gap:.3e}")
+        parity["sample_instances"] = sample
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        plans_orc = [L.get("orc") or orc.offline_preparation(L["W"].astype(np.float64), L["spec"].r,
+                                                             L["spec"].k, 0.0) for L in layers]
+        X_host = [L["X"].exact for L in layers]
+        cpu = cpu_baseline(w, plans_orc, X_host, args.cpu_budget)
+
+    flops = sum(dyra_flops(L["spec"], B, n) for L in layers)
+    dense_flops = sum(2.0 * N * L["spec"].c1 * L["spec"].c2 for L in layers)
+    out = {
+        "metric": "DyRA layer tokens/s, speedup vs dense bf16 GEMM, rel. Frobenius error",
+        "value": round(N / t_dyra, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_dyra * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; shapes and value distributions of the workload, no dataset or trained weights)",
+        "config": {"workload": w.name, "description": w.description, "instances": B, "tokens_per_instance": n,
+                   "layers": {L["spec"].name: [L["spec"].c1, L["spec"].c2, L["spec"].r, L["spec"].k]
+                              for L in layers}},
+        "speedup_vs_dense": round(t_dense / t_dyra, 4),
+        "dense_ms_per_step": round(t_dense * 1e3, 4),
+        "dense_ref_ms_per_step": round(t_dense_ref * 1e3, 4),
+        "dyra_tflops": round(flops / t_dyra / 1e12, 1),
+        "dense_tflops": round(dense_flops / t_dense / 1e12, 1),
+        "stage_us": {L["spec"].name: {k: round(v * 1e6, 2) for k, v in L["stages"].items()} for L in layers},
+        "rel_fro_error": parity,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

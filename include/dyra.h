@@ -1,0 +1,173 @@
+/*
+ * libdyra -- DyRA's one-step dynamic residual approximation of a linear layer
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Method: "DyRA: Dynamic Residual Approximation for Efficient Matrix
+ * Multiplication in DNNs" (Chae, Chung, Lee, Kim).  For a layer Y = X W with
+ * W in R^{c1 x c2}, the library computes
+ *
+ *     Y_hat = (X A_s) V_s^T + L1 R1                       (§2.3 Eq. 6, Prop. 1 Eq. 8)
+ *
+ * where W_hat = A_s V_s^T is the rank-r truncated SVD of W (Appendix B, with
+ * the singular values folded into A_s), W_res = W - W_hat (§2.1 Eq. 1), and per
+ * instance (a block of n consecutive token rows, §2.4) the correction factors
+ * are one ALS step on min ||X W_res - L R||_F (§2.2 Eq. 3-5, Algorithm 1):
+ *
+ *     L1 = X P_L,  P_L = W_res R0^T (R0 R0^T + lambda I)^-1   (Eq. 7)
+ *     R1 = (L1^T L1 + lambda I)^-1 (L1^T X) W_res              (Eq. 5)
+ *
+ * with R0 the top-k right singular vectors of W_res (Appendix D).  "r" is the
+ * static (weight) rank and "k" the correction rank throughout this header.
+ *
+ * All entry points are C99, take plain pointers and sizes, and return a
+ * dyra_status.  None throws, aborts or prints.  Argument checks run on the host
+ * before anything is enqueued, so they can be exercised without a GPU.
+ */
+#ifndef DYRA_H
+#define DYRA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DYRA_OK = 0,
+    DYRA_ERR_ARG = 1,        /* null pointer, bad rank, negative or non-finite lambda */
+    DYRA_ERR_SHAPE = 2,      /* a dimension the kernels do not support (see each call) */
+    DYRA_ERR_DTYPE = 3,      /* unknown dtype */
+    DYRA_ERR_ALIGN = 4,      /* a device pointer not 16-byte aligned */
+    DYRA_ERR_NUMERIC = 5,    /* non-finite weight, or a factorisation that did not converge */
+    DYRA_ERR_HIP = 6,        /* a HIP runtime call or kernel launch failed */
+    DYRA_ERR_NOMEM = 7,      /* host or device allocation failed */
+    DYRA_ERR_WORKSPACE = 8,  /* workspace missing or smaller than dyra_workspace_bytes() */
+    DYRA_ERR_NODEVICE = 9    /* no HIP device, or the plan lives on another device */
+} dyra_status;
+
+typedef enum {
+    DYRA_F32 = 0,   /* float32 operands, float32 accumulation */
+    DYRA_BF16 = 1   /* bfloat16 operands and stored intermediates, float32 accumulation */
+} dyra_dtype;
+
+/* Opaque prepared layer.  Owns its device buffers; immutable after dyra_prepare,
+   so several streams may run dyra_forward on one plan at once, each with its own
+   workspace. */
+typedef struct dyra_plan dyra_plan;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *dyra_status_str(dyra_status s);
+
+/*
+ * Offline factorisation, host only (Algorithm 1, Offline Preparation, lines 2-5;
+ * Appendix B truncated SVD; Appendix D choice of R0; Eq. 7).
+ *
+ * W       host, float32, row-major [c1][c2] in the X W orientation (an nn.Linear
+ *         weight is [c2][c1]: pass its transpose).  Not modified, not retained.
+ * r, k    static rank >= 0 and correction rank >= 0, r + k <= min(c1, c2).
+ * lambda  ridge term >= 0 used in both Gram matrices (§2.2 footnote 2).
+ * Outputs (host, float64, caller-owned; any may be NULL to skip it):
+ *   A_s   [c1][r]   U_r diag(sigma_r), row-major
+ *   V_s   [c2][r]   V_r, row-major
+ *   R0    [k][c2]   V_{r+1..r+k}^T, row-major (orthonormal rows)
+ *   P_L   [c1][k]   W_res R0^T (R0 R0^T + lambda I)^-1, row-major
+ *   sigma [r + k]   leading singular values of W, descending
+ * The SVD is formed from the float64 Gram matrix on the smaller side and a
+ * symmetric eigensolver (Householder tridiagonalisation, bisection, inverse
+ * iteration).  Returns DYRA_ERR_NUMERIC for a non-finite W.  No HIP call is made.
+ */
+dyra_status dyra_factorize_host(const float *W, int64_t c1, int64_t c2, int32_t r, int32_t k,
+                                double lambda, double *A_s, double *V_s, double *R0,
+                                double *P_L, double *sigma);
+
+/*
+ * Algorithm 1, Offline Preparation: factorise W on the host (as
+ * dyra_factorize_host), round the factors to `dtype` (round to nearest even),
+ * pack them in the kernels' layouts and copy them to `device`.  Synchronous;
+ * not on the timed path.
+ *
+ * W, c1, c2, r, k, lambda as for dyra_factorize_host.  c1 and c2 must be
+ * multiples of 32 (DYRA_ERR_SHAPE otherwise).  r and k may be any values with
+ * r + k <= min(c1, c2); k = 0 gives the weight-only product X A_s V_s^T, and
+ * r = min(c1, c2), k = 0 the exact product up to rounding.
+ * On success *plan_out owns device memory until dyra_plan_destroy.
+ */
+dyra_status dyra_prepare(const float *W, int64_t c1, int64_t c2, int32_t r, int32_t k,
+                         float lambda, dyra_dtype dtype, int device, dyra_plan **plan_out);
+
+/* Releases a plan and its device memory.  NULL is ignored. */
+void dyra_plan_destroy(dyra_plan *plan);
+
+/* Dimensions of a plan (any output pointer may be NULL). */
+dyra_status dyra_plan_info(const dyra_plan *plan, int64_t *c1, int64_t *c2, int32_t *r,
+                           int32_t *k, float *lambda, dyra_dtype *dtype, int *device);
+
+/*
+ * Device workspace that dyra_forward needs for B instances of n tokens.
+ * Returns 0 for a NULL plan.  The workspace holds the per-instance factors
+ * L1, (L1^T L1 + lambda I)^-1, the solved left product and R1, plus a small
+ * status header.
+ */
+size_t dyra_workspace_bytes(const dyra_plan *plan, int64_t B, int64_t n);
+
+/*
+ * Algorithm 1, Inference (lines 10-13), for B independent instances of n tokens.
+ *
+ * X          device, plan dtype, row-major [B*n][c1]; instance b is rows [b*n, b*n+n).
+ * Y          device, plan dtype, row-major [B*n][c2]; fully overwritten.
+ * workspace  device, >= dyra_workspace_bytes(plan, B, n) bytes, caller-owned,
+ *            contents on entry ignored.  Calls that overlap in time need
+ *            separate workspaces.
+ * stream     a hipStream_t (NULL = the default stream) on the plan's device.
+ * All pointers 16-byte aligned.  B >= 0, n >= 1 (B = 0 is a no-op).
+ *
+ * Asynchronous: enqueues kernels on `stream` and returns; no allocation, no
+ * host synchronisation.  For n >= k the per-instance right factor is solved
+ * with a Cholesky factorisation of L1^T L1 + lambda I (§2.4); for n < k the
+ * same product L1 R1 is formed in its n x n dual (push-through) form
+ * L1 L1^T (L1 L1^T + lambda I_n)^-1 X W_res, which is also defined at
+ * lambda = 0.  A Cholesky pivot <= 0 (lambda = 0 with rank-deficient L1)
+ * increments a counter that dyra_forward_status() reads back; that instance's
+ * rows are then undefined.
+ */
+dyra_status dyra_forward(const void *X, int64_t B, int64_t n, const dyra_plan *plan, void *Y,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Number of instances whose SPD solve broke down (pivot <= 0) in the last
+ * dyra_forward(X, B, n, plan, ...) that used this workspace.  Copies B flags
+ * from the workspace after synchronising `stream`; *failures receives the count.
+ */
+dyra_status dyra_forward_status(const dyra_plan *plan, int64_t B, int64_t n, const void *workspace,
+                                void *stream, int32_t *failures);
+
+/*
+ * The exact product Y = X W (§2.1 Eq. 2) for parity checks and as the dense
+ * timing point.  X device [N][c1], Wt device [c2][c1] (W transposed, i.e. the
+ * nn.Linear weight layout), Y device [N][c2], all in `dtype`, row-major,
+ * 16-byte aligned; float32 accumulation.  c1 and c2 multiples of 32.
+ * Asynchronous on `stream`.
+ */
+dyra_status dyra_dense_ref(const void *X, const void *Wt, int64_t N, int64_t c1, int64_t c2,
+                           dyra_dtype dtype, void *Y, void *stream);
+
+/*
+ * Stage timing for measurement tools: as dyra_forward, but records
+ * events[0..n_events) (hipEvent_t, created by the caller) on `stream` before
+ * the first kernel and after each kernel of the path.  *n_recorded receives the
+ * number of events used (stages + 1, at most n_events).  Stage names are
+ * returned by dyra_stage_name().
+ */
+dyra_status dyra_forward_timed(const void *X, int64_t B, int64_t n, const dyra_plan *plan,
+                               void *Y, void *workspace, size_t workspace_bytes, void *stream,
+                               void *const *events, int32_t n_events, int32_t *n_recorded);
+
+/* Name of stage i of the path dyra_forward takes for (plan, n); NULL past the end. */
+const char *dyra_stage_name(const dyra_plan *plan, int64_t n, int32_t i);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DYRA_H */

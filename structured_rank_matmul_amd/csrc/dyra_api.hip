@@ -1,0 +1,378 @@
+// libdyra C ABI: plan preparation, workspace layout and the forward path.
+//
+// "DyRA: Dynamic Residual Approximation for Efficient Matrix Multiplication in
+// DNNs", Algorithm 1 (Offline Preparation and Inference).  The host part of
+// the preparation lives in host_factorize.cpp; this file rounds and packs the
+// factors for the kernels, and sequences the kernels of one forward call.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "dyra_internal.h"
+#include "dyra_kernels.h"
+#include "dyra_decode.h"
+
+struct dyra_plan {
+    int device;
+    dyra_dtype dtype;
+    int64_t c1, c2;
+    int32_t r, k;     // static and correction ranks as requested
+    int32_t kw, kc;   // padded: kw = r rounded up to 32, kc = k rounded up to 16
+    float lambda;
+    void *Aext;       // [kw + kc][c1]: rows 0..r-1 = A_s columns, rows kw..kw+k-1 = P_L columns
+    void *Vs;         // [c2][kw]: V_s
+    void *Wres_t;     // [c2][c1]: W_res transposed
+};
+
+namespace {
+
+using dyra::bf16;
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxCorrection = 64;
+constexpr int kMaxDualTokens = 16;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+size_t elem_size(dyra_dtype t) { return t == DYRA_BF16 ? 2 : 4; }
+
+// float64 -> bfloat16 bits, round to nearest even on the float64 value.
+uint16_t bf16_bits(double x) {
+    float f = (float)x;  // RNE to 24 bits
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)(u >> 16);  // inf / nan
+    const uint32_t low = u & 0xffffu;
+    if (low == 0x8000u && (double)f != x) {
+        // f sits exactly halfway between two bf16 values but x does not: the
+        // float rounding decided the side, so follow x's position relative to f.
+        const bool up = std::fabs(x) > std::fabs((double)f);
+        return (uint16_t)((u >> 16) + (up ? 1u : 0u));
+    }
+    const uint32_t bias = 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)((u + bias) >> 16);
+}
+
+enum class Path { Primal, Dual, Static };
+
+// Instances with at most kMaxDualTokens tokens (and any with fewer tokens than
+// the correction rank) take the n x n dual form: its eigen-decomposition stays
+// accurate where the k x k normal equations of the primal form would be
+// ill-conditioned (n close to k).
+Path path_for(const dyra_plan *p, int64_t n) {
+    if (p->kc == 0) return Path::Static;
+    return (n < p->k || n <= kMaxDualTokens) ? Path::Dual : Path::Primal;
+}
+
+struct Layout {
+    size_t flags, L1, Qt, Mp, R1t, dual, total;
+    int64_t npad;
+};
+
+Layout workspace_layout(const dyra_plan *p, int64_t B, int64_t n) {
+    Layout L{};
+    const size_t es = elem_size(p->dtype);
+    const int64_t N = B * n;
+    size_t off = 0;
+    L.flags = off;
+    off += align_up(sizeof(int32_t) * (size_t)std::max<int64_t>(B, 1));
+    if (path_for(p, n) == Path::Primal) {
+        L.L1 = off;
+        off += align_up(es * N * p->kc);
+        L.npad = round_up(n, 32);
+        L.Qt = off;
+        off += align_up(es * B * p->kc * L.npad);
+        L.Mp = off;
+        off += align_up(es * B * p->kc * p->c1);
+        L.R1t = off;
+        off += align_up(es * B * p->c2 * p->kc);
+    } else if (path_for(p, n) == Path::Dual) {
+        L.dual = off;
+        off += align_up(dyra::decode_workspace_bytes(B, n, p->c1, p->kw, p->kc));
+    }
+    L.total = off;
+    return L;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+dyra_status hip_status(hipError_t e) { return e == hipSuccess ? DYRA_OK : DYRA_ERR_HIP; }
+
+dyra_status check_device(int device) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return DYRA_ERR_NODEVICE;
+    return cur == device ? DYRA_OK : DYRA_ERR_NODEVICE;
+}
+
+const char *const kPrimalStages[] = {"left", "gram_q", "mprime", "right", "output"};
+const char *const kDualStages[] = {"decode_project", "decode_coef", "decode_output"};
+const char *const kStaticStages[] = {"output"};
+
+template <typename E>
+dyra_status run_forward(const E *X, int64_t B, int64_t n, const dyra_plan *p, E *Y, char *ws, const Layout &L,
+                        hipStream_t st, void *const *events, int32_t n_events, int32_t *n_recorded) {
+    int32_t ev = 0;
+    auto mark = [&]() -> dyra_status {
+        if (events && ev < n_events) {
+            if (hipEventRecord((hipEvent_t)events[ev], st) != hipSuccess) return DYRA_ERR_HIP;
+            ++ev;
+        }
+        return DYRA_OK;
+    };
+    const int64_t N = B * n;
+    const E *Aext = (const E *)p->Aext;
+    const E *Vs = (const E *)p->Vs;
+    const E *Wres_t = (const E *)p->Wres_t;
+    int *flags = (int *)(ws + L.flags);
+    dyra_status s;
+    if ((s = mark()) != DYRA_OK) return s;
+    const Path path = path_for(p, n);
+    if (path == Path::Primal) {
+        E *L1 = (E *)(ws + L.L1);
+        E *Qt = (E *)(ws + L.Qt);
+        E *Mp = (E *)(ws + L.Mp);
+        E *R1t = (E *)(ws + L.R1t);
+        if ((s = hip_status(dyra::launch_gemm_store<E>(X, p->c1, Aext + (int64_t)p->kw * p->c1, p->c1, N, p->kc,
+                                                       p->c1, L1, p->kc, st))) != DYRA_OK) return s;
+        if ((s = mark()) != DYRA_OK) return s;
+        if ((s = hip_status(dyra::launch_gram_q<E>(L1, B, n, L.npad, p->k, p->kc, p->lambda, Qt, flags, st))) !=
+            DYRA_OK)
+            return s;
+        if ((s = mark()) != DYRA_OK) return s;
+        if ((s = hip_status(dyra::launch_mprime<E>(X, Qt, B, n, L.npad, p->c1, p->kc, Mp, st))) != DYRA_OK) return s;
+        if ((s = mark()) != DYRA_OK) return s;
+        if ((s = hip_status(dyra::launch_right<E>(Mp, Wres_t, B * p->kc, p->c1, p->c2, p->kc, R1t, st))) != DYRA_OK)
+            return s;
+        if ((s = mark()) != DYRA_OK) return s;
+        if ((s = hip_status(dyra::launch_output<E>(X, N, n, p->c1, p->c2, Aext, p->kw, p->kc, Vs, L1, R1t, Y,
+                                                   st))) != DYRA_OK) return s;
+        if ((s = mark()) != DYRA_OK) return s;
+    } else if (path == Path::Static) {
+        if ((s = hip_status(dyra::launch_output<E>(X, N, n, p->c1, p->c2, Aext, p->kw, 0, Vs, nullptr, nullptr, Y,
+                                                   st))) != DYRA_OK) return s;
+        if ((s = mark()) != DYRA_OK) return s;
+    } else {
+        dyra::DecodeArgs<E> a{X, B, n, p->c1, p->c2, p->kw, p->kc, p->k, p->lambda, Aext, Vs, Wres_t, Y,
+                              ws + L.dual, flags};
+        if ((s = hip_status(dyra::launch_decode_project<E>(a, st))) != DYRA_OK) return s;
+        if ((s = mark()) != DYRA_OK) return s;
+        if ((s = hip_status(dyra::launch_decode_coef<E>(a, st))) != DYRA_OK) return s;
+        if ((s = mark()) != DYRA_OK) return s;
+        if ((s = hip_status(dyra::launch_decode_output<E>(a, st))) != DYRA_OK) return s;
+        if ((s = mark()) != DYRA_OK) return s;
+    }
+    if (n_recorded) *n_recorded = ev;
+    return DYRA_OK;
+}
+
+// Flags start at zero for every call: the per-instance failure flags are
+// written (0 or 1) by the SPD-solve kernel for every instance, never accumulated.
+dyra_status forward_impl(const void *X, int64_t B, int64_t n, const dyra_plan *p, void *Y, void *workspace,
+                         size_t workspace_bytes, void *stream, void *const *events, int32_t n_events,
+                         int32_t *n_recorded) {
+    if (n_recorded) *n_recorded = 0;
+    if (!p) return DYRA_ERR_ARG;
+    if (B < 0 || n < 1) return DYRA_ERR_SHAPE;
+    if (B == 0) return DYRA_OK;
+    if (!X || !Y) return DYRA_ERR_ARG;
+    if (!aligned16(X) || !aligned16(Y)) return DYRA_ERR_ALIGN;
+    if (B > INT32_MAX / std::max<int64_t>(n, 1)) return DYRA_ERR_SHAPE;
+    const Path path = path_for(p, n);
+    if (path == Path::Dual && n > kMaxDualTokens) return DYRA_ERR_SHAPE;  // n < k with k > 16 tokens
+    const Layout L = workspace_layout(p, B, n);
+    if (!workspace || workspace_bytes < L.total) return DYRA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return DYRA_ERR_ALIGN;
+    dyra_status s = check_device(p->device);
+    if (s != DYRA_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    if (p->dtype == DYRA_BF16)
+        return run_forward<bf16>((const bf16 *)X, B, n, p, (bf16 *)Y, ws, L, st, events, n_events, n_recorded);
+    return run_forward<float>((const float *)X, B, n, p, (float *)Y, ws, L, st, events, n_events, n_recorded);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dyra_status_str(dyra_status s) {
+    switch (s) {
+    case DYRA_OK: return "ok";
+    case DYRA_ERR_ARG: return "invalid argument";
+    case DYRA_ERR_SHAPE: return "unsupported shape";
+    case DYRA_ERR_DTYPE: return "unknown dtype";
+    case DYRA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case DYRA_ERR_NUMERIC: return "numerical failure";
+    case DYRA_ERR_HIP: return "HIP runtime error";
+    case DYRA_ERR_NOMEM: return "out of memory";
+    case DYRA_ERR_WORKSPACE: return "workspace missing or too small";
+    case DYRA_ERR_NODEVICE: return "no device or wrong device";
+    }
+    return "unknown status";
+}
+
+dyra_status dyra_prepare(const float *W, int64_t c1, int64_t c2, int32_t r, int32_t k, float lambda,
+                         dyra_dtype dtype, int device, dyra_plan **plan_out) {
+    if (!plan_out) return DYRA_ERR_ARG;
+    *plan_out = nullptr;
+    if (dtype != DYRA_BF16 && dtype != DYRA_F32) return DYRA_ERR_DTYPE;
+    if (!W || c1 <= 0 || c2 <= 0 || r < 0 || k < 0) return DYRA_ERR_ARG;
+    if ((int64_t)r + k > std::min(c1, c2)) return DYRA_ERR_ARG;
+    if (!(lambda >= 0.f) || !std::isfinite(lambda)) return DYRA_ERR_ARG;
+    if (c1 % 32 != 0 || c2 % 32 != 0) return DYRA_ERR_SHAPE;
+    if (k > kMaxCorrection) return DYRA_ERR_SHAPE;
+    const int32_t kw = r > 0 ? (int32_t)round_up(r, 32) : 0;
+    const int32_t kc = k > 0 ? (int32_t)round_up(k, 16) : 0;
+    if (!dyra::output_fits(elem_size(dtype), kw, kc)) return DYRA_ERR_SHAPE;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) return DYRA_ERR_NODEVICE;
+
+    dyra::Factors f;
+    dyra_status s = dyra::factorize(W, c1, c2, r, k, (double)lambda, &f);
+    if (s != DYRA_OK) return s;
+
+    const size_t es = elem_size(dtype);
+    const size_t nA = (size_t)(kw + kc) * c1, nV = (size_t)c2 * kw, nR = (size_t)c2 * c1;
+    std::vector<double> A(nA, 0.0), V(nV, 0.0), Rt(nR, 0.0);
+    for (int64_t a = 0; a < c1; ++a) {
+        for (int32_t i = 0; i < r; ++i) A[(size_t)i * c1 + a] = f.A_s[a * r + i];
+        for (int32_t i = 0; i < k; ++i) A[(size_t)(kw + i) * c1 + a] = f.P_L[a * k + i];
+    }
+    for (int64_t b = 0; b < c2; ++b)
+        for (int32_t i = 0; i < r; ++i) V[(size_t)b * kw + i] = f.V_s[b * r + i];
+    for (int64_t a = 0; a < c1; ++a)
+        for (int64_t b = 0; b < c2; ++b) Rt[(size_t)b * c1 + a] = f.W_res[a * c2 + b];
+
+    dyra_plan *p = new (std::nothrow) dyra_plan{};
+    if (!p) return DYRA_ERR_NOMEM;
+    p->device = device;
+    p->dtype = dtype;
+    p->c1 = c1;
+    p->c2 = c2;
+    p->r = r;
+    p->k = k;
+    p->kw = kw;
+    p->kc = kc;
+    p->lambda = lambda;
+    int prev = -1;
+    (void)hipGetDevice(&prev);
+    if (hipSetDevice(device) != hipSuccess) {
+        delete p;
+        return DYRA_ERR_NODEVICE;
+    }
+    auto upload = [&](const std::vector<double> &src, void **dst) -> dyra_status {
+        const size_t bytes = std::max<size_t>(src.size() * es, 16);
+        if (hipMalloc(dst, bytes) != hipSuccess) return DYRA_ERR_NOMEM;
+        std::vector<unsigned char> host(bytes, 0);
+        if (dtype == DYRA_BF16) {
+            uint16_t *h = (uint16_t *)host.data();
+            for (size_t i = 0; i < src.size(); ++i) h[i] = bf16_bits(src[i]);
+        } else {
+            float *h = (float *)host.data();
+            for (size_t i = 0; i < src.size(); ++i) h[i] = (float)src[i];
+        }
+        return hipMemcpy(*dst, host.data(), bytes, hipMemcpyHostToDevice) == hipSuccess ? DYRA_OK : DYRA_ERR_HIP;
+    };
+    if ((s = upload(A, &p->Aext)) == DYRA_OK && (s = upload(V, &p->Vs)) == DYRA_OK)
+        s = upload(Rt, &p->Wres_t);
+    if (prev >= 0) (void)hipSetDevice(prev);
+    if (s != DYRA_OK) {
+        dyra_plan_destroy(p);
+        return s;
+    }
+    *plan_out = p;
+    return DYRA_OK;
+}
+
+void dyra_plan_destroy(dyra_plan *plan) {
+    if (!plan) return;
+    int prev = -1;
+    (void)hipGetDevice(&prev);
+    (void)hipSetDevice(plan->device);
+    if (plan->Aext) (void)hipFree(plan->Aext);
+    if (plan->Vs) (void)hipFree(plan->Vs);
+    if (plan->Wres_t) (void)hipFree(plan->Wres_t);
+    if (prev >= 0) (void)hipSetDevice(prev);
+    delete plan;
+}
+
+dyra_status dyra_plan_info(const dyra_plan *p, int64_t *c1, int64_t *c2, int32_t *r, int32_t *k, float *lambda,
+                           dyra_dtype *dtype, int *device) {
+    if (!p) return DYRA_ERR_ARG;
+    if (c1) *c1 = p->c1;
+    if (c2) *c2 = p->c2;
+    if (r) *r = p->r;
+    if (k) *k = p->k;
+    if (lambda) *lambda = p->lambda;
+    if (dtype) *dtype = p->dtype;
+    if (device) *device = p->device;
+    return DYRA_OK;
+}
+
+size_t dyra_workspace_bytes(const dyra_plan *plan, int64_t B, int64_t n) {
+    if (!plan || B < 0 || n < 1) return 0;
+    return workspace_layout(plan, B, n).total;
+}
+
+dyra_status dyra_forward(const void *X, int64_t B, int64_t n, const dyra_plan *plan, void *Y, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    return forward_impl(X, B, n, plan, Y, workspace, workspace_bytes, stream, nullptr, 0, nullptr);
+}
+
+dyra_status dyra_forward_timed(const void *X, int64_t B, int64_t n, const dyra_plan *plan, void *Y,
+                               void *workspace, size_t workspace_bytes, void *stream, void *const *events,
+                               int32_t n_events, int32_t *n_recorded) {
+    if (!events || n_events < 1) return DYRA_ERR_ARG;
+    return forward_impl(X, B, n, plan, Y, workspace, workspace_bytes, stream, events, n_events, n_recorded);
+}
+
+const char *dyra_stage_name(const dyra_plan *plan, int64_t n, int32_t i) {
+    if (!plan || n < 1 || i < 0) return nullptr;
+    switch (path_for(plan, n)) {
+    case Path::Primal: return i < 5 ? kPrimalStages[i] : nullptr;
+    case Path::Dual: return i < 3 ? kDualStages[i] : nullptr;
+    case Path::Static: return i < 1 ? kStaticStages[i] : nullptr;
+    }
+    return nullptr;
+}
+
+dyra_status dyra_forward_status(const dyra_plan *plan, int64_t B, int64_t n, const void *workspace, void *stream,
+                                int32_t *failures) {
+    if (!plan || !workspace || !failures || B < 0 || n < 1) return DYRA_ERR_ARG;
+    *failures = 0;
+    if (B == 0) return DYRA_OK;
+    const Layout L = workspace_layout(plan, B, n);
+    std::vector<int32_t> flags((size_t)B);
+    hipStream_t st = (hipStream_t)stream;
+    if (hipMemcpyAsync(flags.data(), (const char *)workspace + L.flags, sizeof(int32_t) * (size_t)B,
+                       hipMemcpyDeviceToHost, st) != hipSuccess)
+        return DYRA_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return DYRA_ERR_HIP;
+    int32_t c = 0;
+    for (int32_t f : flags) c += f != 0;
+    *failures = c;
+    return DYRA_OK;
+}
+
+dyra_status dyra_dense_ref(const void *X, const void *Wt, int64_t N, int64_t c1, int64_t c2, dyra_dtype dtype,
+                           void *Y, void *stream) {
+    if (dtype != DYRA_BF16 && dtype != DYRA_F32) return DYRA_ERR_DTYPE;
+    if (N < 0 || c1 <= 0 || c2 <= 0) return DYRA_ERR_SHAPE;
+    if (c1 % 32 != 0 || c2 % 32 != 0) return DYRA_ERR_SHAPE;
+    if (N == 0) return DYRA_OK;
+    if (!X || !Wt || !Y) return DYRA_ERR_ARG;
+    if (!aligned16(X) || !aligned16(Wt) || !aligned16(Y)) return DYRA_ERR_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    if (dtype == DYRA_BF16)
+        return hip_status(dyra::launch_gemm_store<bf16>((const bf16 *)X, c1, (const bf16 *)Wt, c1, N, c2, c1,
+                                                        (bf16 *)Y, c2, st));
+    return hip_status(
+        dyra::launch_gemm_store<float>((const float *)X, c1, (const float *)Wt, c1, N, c2, c1, (float *)Y, c2, st));
+}
+
+}  // extern "C"

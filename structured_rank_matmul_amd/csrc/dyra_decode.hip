@@ -1,0 +1,295 @@
+// Dual-form (n < k) kernels of the DyRA forward path; see dyra_decode.h.
+//
+// "DyRA: Dynamic Residual Approximation for Efficient Matrix Multiplication in
+// DNNs", Algorithm 1 Inference lines 10-13 and Eq. 5-7, evaluated through the
+// push-through identity so that it stays defined when an instance has fewer
+// tokens than the correction rank (token-by-token decode).  These shapes are
+// bound by HBM: W_res and V_s are streamed once per call, 32 output columns
+// per workgroup, and the small operands (X, T) are re-read from L2.
+#include "dyra_decode.h"
+
+#include "mfma_tile.h"
+
+namespace dyra {
+
+namespace {
+
+constexpr int NT = 256;
+constexpr int kRowBlock = 64;  // rows (tokens) per workgroup, two 32-row MFMA blocks
+
+int decode_splits(int64_t c1) {
+    int s = 1;
+    while (s < 16 && c1 % (32 * 2 * s) == 0 && c1 / (2 * s) >= 256) s *= 2;
+    return s;
+}
+
+int64_t rows_per_block(int64_t n) { return (kRowBlock / n) * n; }
+
+struct DualLayout {
+    size_t partial, T, coef, total;
+    int splits;
+};
+
+DualLayout dual_layout(int64_t B, int64_t n, int64_t c1, int kw, int kc) {
+    DualLayout L{};
+    const int64_t N = B * n;
+    const int64_t K1 = kw + kc;
+    L.splits = decode_splits(c1);
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    size_t off = 0;
+    L.partial = off;
+    off += al(sizeof(float) * (size_t)L.splits * N * K1);
+    L.T = off;
+    off += al(sizeof(float) * (size_t)N * K1);
+    L.coef = off;
+    off += al(sizeof(float) * (size_t)B * n * n);
+    L.total = off;
+    return L;
+}
+
+// Fragment of 8 consecutive elements from a float32 row, converted to E.
+__device__ __forceinline__ bf16x8 frag_from_f32(const float *p, bf16) {
+    const f32x4 lo = *reinterpret_cast<const f32x4 *>(p);
+    const f32x4 hi = *reinterpret_cast<const f32x4 *>(p + 4);
+    bf16x8 r;
+    r[0] = (bf16)lo[0]; r[1] = (bf16)lo[1]; r[2] = (bf16)lo[2]; r[3] = (bf16)lo[3];
+    r[4] = (bf16)hi[0]; r[5] = (bf16)hi[1]; r[6] = (bf16)hi[2]; r[7] = (bf16)hi[3];
+    return r;
+}
+__device__ __forceinline__ f32x8 frag_from_f32(const float *p, float) { return ld_frag(p); }
+
+// partial[s][row][col] = sum over the s-th split of c1 of X[row][k] Aext[col][k].
+// Grid (K1/32 column blocks, splits, row blocks of 64).  The 16-deep steps of a
+// split are dealt round-robin to the four wavefronts, then reduced in LDS.
+template <typename E>
+__global__ __launch_bounds__(NT) void decode_project_kernel(const E *__restrict__ X, const E *__restrict__ Aext,
+                                                            int64_t N, int64_t c1, int K1, int splits,
+                                                            float *__restrict__ partial) {
+    __shared__ float red[kRowBlock][33];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 31, lk = (lane >> 5) * 8;
+    const int col0 = blockIdx.x * 32;
+    const int s = blockIdx.y;
+    const int64_t row0 = (int64_t)blockIdx.z * kRowBlock;
+    const int64_t ks = c1 / splits;
+    const int64_t kbeg = s * ks;
+    for (int e = tid; e < kRowBlock * 33; e += NT) (&red[0][0])[e] = 0.f;
+    __syncthreads();
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+    const int col = col0 + lr;
+    const bool col_ok = col < K1;
+    const int64_t ra = row0 + lr, rb = row0 + 32 + lr;
+    typedef typename Frag<E>::type F;
+    for (int64_t k = kbeg + 16 * wave; k < kbeg + ks; k += 64) {
+        F fb = col_ok ? ld_frag(Aext + (int64_t)col * c1 + k + lk) : F{};
+        F fa0 = ra < N ? ld_frag(X + ra * c1 + k + lk) : F{};
+        F fa1 = rb < N ? ld_frag(X + rb * c1 + k + lk) : F{};
+        acc[0] = mma16(acc[0], fa0, fb);
+        acc[1] = mma16(acc[1], fa1, fb);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) atomicAdd(&red[h * 32 + acc_row(lane, t)][lr], acc[h][t]);
+    __syncthreads();
+    for (int e = tid; e < kRowBlock * 32; e += NT) {
+        const int r = e >> 5, c = e & 31;
+        if (row0 + r < N && col0 + c < K1) partial[((int64_t)s * N + row0 + r) * K1 + col0 + c] = red[r][c];
+    }
+}
+
+// One workgroup per instance: T rows = sum of the split partials; then
+// C_b = K (K + lambda I)^-1 with K = L1_b L1_b^T (n x n) from the eigenpairs of
+// K (cyclic Jacobi, float64, one thread).  K is formed in float64 from the
+// float32 L1 values, so an exact rank deficiency shows as eigenvalues at the
+// float64 rounding level; at lambda = 0 eigenvalues below n * 1e-12 * max
+// count as zero, giving the projector onto range(L1_b).
+template <typename E>
+__global__ __launch_bounds__(NT) void decode_coef_kernel(const float *__restrict__ partial, int64_t N, int64_t n,
+                                                         int K1, int kw, int k_real, int splits, float lambda,
+                                                         float *__restrict__ T, float *__restrict__ coef,
+                                                         int *__restrict__ flags) {
+    __shared__ double K[16][16];
+    __shared__ double V[16][16];
+    const int tid = threadIdx.x;
+    const int64_t b = blockIdx.x;
+    const int64_t r0 = b * n;
+    for (int64_t e = tid; e < n * K1; e += NT) {
+        const int64_t i = e / K1, c = e - (e / K1) * K1;
+        float s = 0.f;
+        for (int q = 0; q < splits; ++q) s += partial[((int64_t)q * N + r0 + i) * K1 + c];
+        T[(r0 + i) * K1 + c] = s;
+    }
+    __syncthreads();
+    const int nn = (int)n;
+    for (int e = tid; e < nn * nn; e += NT) {
+        const int i = e / nn, j = e - (e / nn) * nn;
+        double s = 0.0;
+        for (int c = 0; c < k_real; ++c)
+            s += (double)T[(r0 + i) * K1 + kw + c] * (double)T[(r0 + j) * K1 + kw + c];
+        K[i][j] = s;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        for (int i = 0; i < nn; ++i)
+            for (int j = 0; j < nn; ++j) V[i][j] = (i == j) ? 1.0 : 0.0;
+        for (int sweep = 0; sweep < 50; ++sweep) {
+            double off = 0.0, tot = 0.0;
+            for (int i = 0; i < nn; ++i)
+                for (int j = 0; j < nn; ++j) {
+                    tot += K[i][j] * K[i][j];
+                    if (i != j) off += K[i][j] * K[i][j];
+                }
+            if (off <= 1e-30 * tot || off == 0.0) break;
+            for (int p = 0; p < nn - 1; ++p)
+                for (int q = p + 1; q < nn; ++q) {
+                    const double apq = K[p][q];
+                    if (apq == 0.0) continue;
+                    const double theta = (K[q][q] - K[p][p]) / (2.0 * apq);
+                    const double t = (theta >= 0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
+                    const double c = 1.0 / sqrt(t * t + 1.0), s = t * c;
+                    for (int m = 0; m < nn; ++m) {  // K <- K J (columns p, q)
+                        const double kp = K[m][p], kq = K[m][q];
+                        K[m][p] = c * kp - s * kq;
+                        K[m][q] = s * kp + c * kq;
+                    }
+                    for (int m = 0; m < nn; ++m) {  // K <- J^T K (rows p, q)
+                        const double kp = K[p][m], kq = K[q][m];
+                        K[p][m] = c * kp - s * kq;
+                        K[q][m] = s * kp + c * kq;
+                    }
+                    for (int m = 0; m < nn; ++m) {  // V <- V J
+                        const double vp = V[m][p], vq = V[m][q];
+                        V[m][p] = c * vp - s * vq;
+                        V[m][q] = s * vp + c * vq;
+                    }
+                }
+        }
+        double mu_max = 0.0;
+        for (int i = 0; i < nn; ++i) mu_max = fmax(mu_max, K[i][i]);
+        const double tol = (double)nn * 1e-12 * mu_max;
+        double f[16];
+        for (int i = 0; i < nn; ++i) {
+            const double mu = fmax(K[i][i], 0.0);
+            if (lambda > 0.f) f[i] = mu / (mu + (double)lambda);
+            else f[i] = (mu > tol && mu > 0.0) ? 1.0 : 0.0;
+        }
+        float *Cb = coef + b * n * n;
+        for (int i = 0; i < nn; ++i)
+            for (int j = 0; j < nn; ++j) {
+                double s = 0.0;
+                for (int m = 0; m < nn; ++m) s += V[i][m] * f[m] * V[j][m];
+                Cb[i * nn + j] = (float)s;
+            }
+        flags[b] = 0;
+    }
+}
+
+// Y[rows][col0..col0+32) = T_s V_s^T + blockdiag(C_b) (X W_res).  Grid (c2/32,
+// row blocks of whole instances).  The 16-deep steps of both contractions are
+// dealt round-robin to the four wavefronts and reduced in LDS.
+template <typename E>
+__global__ __launch_bounds__(NT) void decode_output_kernel(const E *__restrict__ X, const float *__restrict__ T,
+                                                           const float *__restrict__ coef,
+                                                           const E *__restrict__ Vs, const E *__restrict__ Wres_t,
+                                                           int64_t N, int64_t n, int64_t c1, int64_t c2, int K1,
+                                                           int kw, int64_t rows_blk, E *__restrict__ Y) {
+    __shared__ float Zs[kRowBlock][33];
+    __shared__ float Ss[kRowBlock][33];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 31, lk = (lane >> 5) * 8;
+    const int64_t col0 = (int64_t)blockIdx.x * 32;
+    const int64_t row0 = (int64_t)blockIdx.y * rows_blk;
+    const int64_t row_end = (row0 + rows_blk < N) ? row0 + rows_blk : N;
+    for (int e = tid; e < kRowBlock * 33; e += NT) {
+        (&Zs[0][0])[e] = 0.f;
+        (&Ss[0][0])[e] = 0.f;
+    }
+    __syncthreads();
+    typedef typename Frag<E>::type F;
+    const int64_t col = col0 + lr;
+    const bool col_ok = col < c2;
+    const int64_t ra = row0 + lr, rb = row0 + 32 + lr;
+    const bool a_ok = ra < row_end, b_ok = rb < row_end;
+    f32x16 z0 = f32x16{}, z1 = f32x16{}, s0 = f32x16{}, s1 = f32x16{};
+    for (int64_t k = 16 * wave; k < c1; k += 64) {
+        F fb = col_ok ? ld_frag(Wres_t + col * c1 + k + lk) : F{};
+        F fa0 = a_ok ? ld_frag(X + ra * c1 + k + lk) : F{};
+        F fa1 = b_ok ? ld_frag(X + rb * c1 + k + lk) : F{};
+        z0 = mma16(z0, fa0, fb);
+        z1 = mma16(z1, fa1, fb);
+    }
+    for (int k = 16 * wave; k < kw; k += 64) {
+        F fb = col_ok ? ld_frag(Vs + col * kw + k + lk) : F{};
+        F fa0 = a_ok ? frag_from_f32(T + ra * K1 + k + lk, E{}) : F{};
+        F fa1 = b_ok ? frag_from_f32(T + rb * K1 + k + lk, E{}) : F{};
+        s0 = mma16(s0, fa0, fb);
+        s1 = mma16(s1, fa1, fb);
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        const int r = acc_row(lane, t);
+        atomicAdd(&Zs[r][lr], z0[t]);
+        atomicAdd(&Zs[32 + r][lr], z1[t]);
+        atomicAdd(&Ss[r][lr], s0[t]);
+        atomicAdd(&Ss[32 + r][lr], s1[t]);
+    }
+    __syncthreads();
+    for (int e = tid; e < kRowBlock * 32; e += NT) {
+        const int r = e >> 5, c = e & 31;
+        const int64_t row = row0 + r;
+        if (row >= row_end || col0 + c >= c2) continue;
+        const int64_t b = row / n;
+        const int i = (int)(row - b * n);
+        const int rb0 = (int)(b * n - row0);
+        const float *Cb = coef + b * n * n;
+        float v = Ss[r][c];
+        for (int j = 0; j < (int)n; ++j) v += Cb[i * n + j] * Zs[rb0 + j][c];
+        Y[row * c2 + col0 + c] = to_elem<E>(v);
+    }
+}
+
+}  // namespace
+
+size_t decode_workspace_bytes(int64_t B, int64_t n, int64_t c1, int kw, int kc) {
+    return dual_layout(B, n, c1, kw, kc).total;
+}
+
+template <typename E> hipError_t launch_decode_project(const DecodeArgs<E> &a, hipStream_t st) {
+    const DualLayout L = dual_layout(a.B, a.n, a.c1, a.kw, a.kc);
+    const int64_t N = a.B * a.n;
+    const int K1 = a.kw + a.kc;
+    dim3 grid((unsigned)((K1 + 31) / 32), (unsigned)L.splits, (unsigned)((N + kRowBlock - 1) / kRowBlock));
+    hipLaunchKernelGGL((decode_project_kernel<E>), grid, dim3(NT), 0, st, a.X, a.Aext, N, a.c1, K1, L.splits,
+                       (float *)(a.ws + L.partial));
+    return hipGetLastError();
+}
+
+template <typename E> hipError_t launch_decode_coef(const DecodeArgs<E> &a, hipStream_t st) {
+    const DualLayout L = dual_layout(a.B, a.n, a.c1, a.kw, a.kc);
+    const int64_t N = a.B * a.n;
+    hipLaunchKernelGGL((decode_coef_kernel<E>), dim3((unsigned)a.B), dim3(NT), 0, st,
+                       (const float *)(a.ws + L.partial), N, a.n, a.kw + a.kc, a.kw, a.k_real, L.splits, a.lambda,
+                       (float *)(a.ws + L.T), (float *)(a.ws + L.coef), a.flags);
+    return hipGetLastError();
+}
+
+template <typename E> hipError_t launch_decode_output(const DecodeArgs<E> &a, hipStream_t st) {
+    const DualLayout L = dual_layout(a.B, a.n, a.c1, a.kw, a.kc);
+    const int64_t N = a.B * a.n;
+    const int64_t rb = rows_per_block(a.n);
+    dim3 grid((unsigned)((a.c2 + 31) / 32), (unsigned)((N + rb - 1) / rb));
+    hipLaunchKernelGGL((decode_output_kernel<E>), grid, dim3(NT), 0, st, a.X, (const float *)(a.ws + L.T),
+                       (const float *)(a.ws + L.coef), a.Vs, a.Wres_t, N, a.n, a.c1, a.c2, a.kw + a.kc, a.kw, rb,
+                       a.Y);
+    return hipGetLastError();
+}
+
+template hipError_t launch_decode_project<bf16>(const DecodeArgs<bf16> &, hipStream_t);
+template hipError_t launch_decode_coef<bf16>(const DecodeArgs<bf16> &, hipStream_t);
+template hipError_t launch_decode_output<bf16>(const DecodeArgs<bf16> &, hipStream_t);
+template hipError_t launch_decode_project<float>(const DecodeArgs<float> &, hipStream_t);
+template hipError_t launch_decode_coef<float>(const DecodeArgs<float> &, hipStream_t);
+template hipError_t launch_decode_output<float>(const DecodeArgs<float> &, hipStream_t);
+
+}  // namespace dyra

@@ -1,0 +1,27 @@
+// Internal declarations shared by the host factorisation and the HIP library.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#include "../../include/dyra.h"
+
+namespace dyra {
+
+// Float64 factors of one layer (Algorithm 1, Offline Preparation).
+struct Factors {
+    int64_t c1 = 0, c2 = 0;
+    int32_t r = 0, k = 0;
+    double lambda = 0.0;
+    std::vector<double> A_s;    // [c1][r]   U_r Sigma_r
+    std::vector<double> V_s;    // [c2][r]   V_r
+    std::vector<double> R0;     // [k][c2]   fixed initial right factor
+    std::vector<double> P_L;    // [c1][k]   W_res R0^T (R0 R0^T + lambda I)^-1
+    std::vector<double> sigma;  // [r + k]   leading singular values
+    std::vector<double> W_res;  // [c1][c2]  W - A_s V_s^T
+};
+
+dyra_status factorize(const float *W, int64_t c1, int64_t c2, int32_t r, int32_t k, double lambda,
+                      Factors *out);
+
+}  // namespace dyra
