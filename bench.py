@@ -33,11 +33,13 @@ def stage_flops(spec, B, n):
     N = B * n
     c1, c2, r, k = spec.c1, spec.c2, spec.r, spec.k
     return {
-        "left": 2.0 * N * c1 * k,
-        "gram_q": 2.0 * N * k * k + 2.0 * N * k * k,
+        # one pass over X gives X A_s and L1 = X P_L
+        "left": 2.0 * N * c1 * (r + k),
+        # G = L1^T L1 and Q = L1 C^-T per instance
+        "gram_q": 2.0 * N * k * k + 1.0 * N * k * k,
         "mprime": 2.0 * N * k * c1,
         "right": 2.0 * B * k * c1 * c2,
-        "output": 2.0 * N * c1 * r + 2.0 * N * (r + k) * c2,
+        "output": 2.0 * N * (r + k) * c2,
     }
 
 

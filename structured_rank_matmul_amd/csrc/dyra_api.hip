@@ -69,8 +69,15 @@ Path path_for(const dyra_plan *p, int64_t n) {
     return (n < p->k || n <= kMaxDualTokens) ? Path::Dual : Path::Primal;
 }
 
+// Workspace of one forward call (offsets in bytes, each 256-byte aligned):
+//   flags  int32 [B]             per-instance solve failure flags
+//   T      [N][kw + kc]          X A_s next to L1 (then Q) for every token
+//   Qt     [B][kc][npad]         Q_b^T, token-contiguous, npad = n rounded up to 32
+//   Mp     [B * kc][c1]          M'_b = Q_b^T X_b stacked over instances
+//   R1t    [B][c2][kc]           R1_b transposed
+//   dual   decode workspace      (n <= 16 or n < k only)
 struct Layout {
-    size_t flags, L1, Qt, Mp, R1t, dual, total;
+    size_t flags, T, Qt, Mp, R1t, dual, total;
     int64_t npad;
 };
 
@@ -81,9 +88,11 @@ Layout workspace_layout(const dyra_plan *p, int64_t B, int64_t n) {
     size_t off = 0;
     L.flags = off;
     off += align_up(sizeof(int32_t) * (size_t)std::max<int64_t>(B, 1));
+    if (path_for(p, n) != Path::Dual) {
+        L.T = off;
+        off += align_up(es * N * (p->kw + p->kc));
+    }
     if (path_for(p, n) == Path::Primal) {
-        L.L1 = off;
-        off += align_up(es * N * p->kc);
         L.npad = round_up(n, 32);
         L.Qt = off;
         off += align_up(es * B * p->kc * L.npad);
@@ -111,7 +120,7 @@ dyra_status check_device(int device) {
 
 const char *const kPrimalStages[] = {"left", "gram_q", "mprime", "right", "output"};
 const char *const kDualStages[] = {"decode_project", "decode_coef", "decode_output"};
-const char *const kStaticStages[] = {"output"};
+const char *const kStaticStages[] = {"left", "output"};
 
 template <typename E>
 dyra_status run_forward(const E *X, int64_t B, int64_t n, const dyra_plan *p, E *Y, char *ws, const Layout &L,
@@ -132,29 +141,34 @@ dyra_status run_forward(const E *X, int64_t B, int64_t n, const dyra_plan *p, E 
     dyra_status s;
     if ((s = mark()) != DYRA_OK) return s;
     const Path path = path_for(p, n);
-    if (path == Path::Primal) {
-        E *L1 = (E *)(ws + L.L1);
-        E *Qt = (E *)(ws + L.Qt);
-        E *Mp = (E *)(ws + L.Mp);
-        E *R1t = (E *)(ws + L.R1t);
-        if ((s = hip_status(dyra::launch_gemm_store<E>(X, p->c1, Aext + (int64_t)p->kw * p->c1, p->c1, N, p->kc,
-                                                       p->c1, L1, p->kc, st))) != DYRA_OK) return s;
-        if ((s = mark()) != DYRA_OK) return s;
-        if ((s = hip_status(dyra::launch_gram_q<E>(L1, B, n, L.npad, p->k, p->kc, p->lambda, Qt, flags, st))) !=
+    if (path != Path::Dual) {
+        // T = X [A_s | P_L]^T: the static projection and L1 in one pass over X
+        E *T = (E *)(ws + L.T);
+        const int64_t ldt = p->kw + p->kc;
+        if ((s = hip_status(dyra::launch_gemm_store<E>(X, p->c1, Aext, p->c1, N, ldt, p->c1, T, ldt, st))) !=
             DYRA_OK)
             return s;
         if ((s = mark()) != DYRA_OK) return s;
-        if ((s = hip_status(dyra::launch_mprime<E>(X, Qt, B, n, L.npad, p->c1, p->kc, Mp, st))) != DYRA_OK) return s;
-        if ((s = mark()) != DYRA_OK) return s;
-        if ((s = hip_status(dyra::launch_right<E>(Mp, Wres_t, B * p->kc, p->c1, p->c2, p->kc, R1t, st))) != DYRA_OK)
+        E *R1t = nullptr;
+        if (path == Path::Primal) {
+            E *Qt = (E *)(ws + L.Qt);
+            E *Mp = (E *)(ws + L.Mp);
+            R1t = (E *)(ws + L.R1t);
+            if ((s = hip_status(dyra::launch_gram_q<E>(T, ldt, p->kw, B, n, L.npad, p->k, p->kc, p->lambda, Qt, flags,
+                                                       st))) != DYRA_OK)
+                return s;
+            if ((s = mark()) != DYRA_OK) return s;
+            if ((s = hip_status(dyra::launch_mprime<E>(X, Qt, B, n, L.npad, p->c1, p->kc, Mp, st))) != DYRA_OK)
+                return s;
+            if ((s = mark()) != DYRA_OK) return s;
+            if ((s = hip_status(dyra::launch_right<E>(Mp, Wres_t, B * p->kc, p->c1, p->c2, p->kc, R1t, st))) !=
+                DYRA_OK)
+                return s;
+            if ((s = mark()) != DYRA_OK) return s;
+        }
+        const int kc = path == Path::Primal ? p->kc : 0;
+        if ((s = hip_status(dyra::launch_output<E>(T, ldt, p->kw, kc, Vs, R1t, N, n, p->c2, Y, st))) != DYRA_OK)
             return s;
-        if ((s = mark()) != DYRA_OK) return s;
-        if ((s = hip_status(dyra::launch_output<E>(X, N, n, p->c1, p->c2, Aext, p->kw, p->kc, Vs, L1, R1t, Y,
-                                                   st))) != DYRA_OK) return s;
-        if ((s = mark()) != DYRA_OK) return s;
-    } else if (path == Path::Static) {
-        if ((s = hip_status(dyra::launch_output<E>(X, N, n, p->c1, p->c2, Aext, p->kw, 0, Vs, nullptr, nullptr, Y,
-                                                   st))) != DYRA_OK) return s;
         if ((s = mark()) != DYRA_OK) return s;
     } else {
         dyra::DecodeArgs<E> a{X, B, n, p->c1, p->c2, p->kw, p->kc, p->k, p->lambda, Aext, Vs, Wres_t, Y,
@@ -228,7 +242,6 @@ dyra_status dyra_prepare(const float *W, int64_t c1, int64_t c2, int32_t r, int3
     if (k > kMaxCorrection) return DYRA_ERR_SHAPE;
     const int32_t kw = r > 0 ? (int32_t)round_up(r, 32) : 0;
     const int32_t kc = k > 0 ? (int32_t)round_up(k, 16) : 0;
-    if (!dyra::output_fits(elem_size(dtype), kw, kc)) return DYRA_ERR_SHAPE;
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) return DYRA_ERR_NODEVICE;
 
@@ -336,7 +349,7 @@ const char *dyra_stage_name(const dyra_plan *plan, int64_t n, int32_t i) {
     switch (path_for(plan, n)) {
     case Path::Primal: return i < 5 ? kPrimalStages[i] : nullptr;
     case Path::Dual: return i < 3 ? kDualStages[i] : nullptr;
-    case Path::Static: return i < 1 ? kStaticStages[i] : nullptr;
+    case Path::Static: return i < 2 ? kStaticStages[i] : nullptr;
     }
     return nullptr;
 }

@@ -1,4 +1,4 @@
-// Launchers of the HIP kernels (dyra_kernels.hip).  All enqueue on `st` and
+// Launchers of the HIP kernels of the primal path (gemm.hip, solve.hip).  All enqueue on `st` and
 // return the launch status; none allocates or synchronises.
 #pragma once
 
@@ -8,8 +8,6 @@
 namespace dyra {
 
 typedef __bf16 bf16;
-
-constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 
 // D[M][N] (leading dim ldd) = A[M][K] B[N][K]^T, K a multiple of 32.
 template <typename E>
@@ -22,23 +20,24 @@ hipError_t launch_right(const E *Mp, const E *Wres_t, int64_t rows, int64_t c1, 
                         hipStream_t st);
 
 // With C C^T = L1_b^T L1_b + lambda I: Q_b = L1_b C^-T replaces L1_b in place
-// ([n][kc] rows of L1) and Qt[b] = Q_b^T ([kc][npad], token-contiguous, zero for
-// tokens n..npad-1).  flags[b] = 1 if a pivot broke down (then Q_b = 0).  kc <= 64.
+// (columns [off, off + kc) of T's rows b*n .. b*n + n - 1, leading dimension
+// ldt) and Qt[b] = Q_b^T ([kc][npad], token-contiguous, zero for tokens
+// n..npad-1).  flags[b] = 1 if a pivot broke down (then Q_b = 0).
+// kc in {16, 32, 48, 64}.
 template <typename E>
-hipError_t launch_gram_q(E *L1, int64_t B, int64_t n, int64_t npad, int kc_real, int kc, float lambda, E *Qt,
-                         int *flags, hipStream_t st);
+hipError_t launch_gram_q(E *T, int64_t ldt, int64_t off, int64_t B, int64_t n, int64_t npad, int kc_real, int kc,
+                         float lambda, E *Qt, int *flags, hipStream_t st);
 
 // Mp[b*kc + i][:] = (Qt_b X_b)[i][:].
 template <typename E>
 hipError_t launch_mprime(const E *X, const E *Qt, int64_t B, int64_t n, int64_t npad, int64_t c1, int kc, E *Mp,
                          hipStream_t st);
 
-// Y = (X A_s) V_s^T + L1 R1_b with X A_s kept in LDS.
+// Y[Ntok][c2] = T[:, 0:kw] V_s^T + T[:, kw:kw+kc] R1_b for each token's
+// instance b (n tokens per instance; R1t[b] is [c2][kc]); T has leading
+// dimension ldt.  kc = 0 gives the static product alone.
 template <typename E>
-hipError_t launch_output(const E *X, int64_t N, int64_t n, int64_t c1, int64_t c2, const E *Aext, int kw, int kc,
-                         const E *Vs, const E *L1, const E *R1t, E *Y, hipStream_t st);
-
-// Whether the fused output kernel's LDS tile fits for these padded ranks.
-bool output_fits(size_t elem_bytes, int kw, int kc);
+hipError_t launch_output(const E *T, int64_t ldt, int kw, int kc, const E *Vs, const E *R1t, int64_t Ntok,
+                         int64_t n, int64_t c2, E *Y, hipStream_t st);
 
 }  // namespace dyra

@@ -1,18 +1,33 @@
 // Tiled MFMA GEMM for gfx950: D = A B^T with both operands K-contiguous.
 //
 // Used for the exact product X W (the dense reference, §2.1 Eq. 2), the left
-// factor L1 = X P_L (DyRA paper Eq. 7) and the stacked right factor
-// R1 = M' W_res of all instances at once (Eq. 5; the O(c1 c2 r) term of §2.3).
+// pass T = X [A_s | P_L] that yields both the static projection X A_s and the
+// left factor L1 = X P_L (DyRA paper Eq. 7), the stacked right factor
+// R1 = M' W_res of all instances at once (Eq. 5; the O(c1 c2 r) term of §2.3)
+// and the output Y = (X A_s) V_s^T + L1 R1_b (Eq. 6 with Proposition 1's
+// factored static part).
 //
-// A workgroup owns a BM x BN output tile and four wavefronts each own a
+// A workgroup owns a BM x BN output tile and its WM x WN wavefronts each own a
 // (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks.  K advances in slices of 64
-// (bf16) or 32 (fp32) elements staged through two LDS buffers: the next slice
-// is fetched into registers while the current one feeds the MFMAs.  Tiles are
-// handed out XCD by XCD: workgroup ids are dealt round-robin over the 8 XCDs,
-// so id i works on tile (i % 8) * ceil(T/8) + i / 8 and each XCD's L2 sees a
-// contiguous band of tiles that share operand panels.
+// bytes per operand row (32 bf16 / 16 fp32 elements).  Slices move from global
+// memory straight into LDS (global_load_lds_dwordx4, no register staging), NS
+// of them in flight, so a slice's loads have NS - 1 slices of MFMA work to
+// land; one barrier per slice.  In LDS a slice row is four 16-byte chunks and
+// chunk c of row r sits at position c ^ ((r >> 2) & 3): the 16 rows that a
+// quarter wavefront reads with ds_read_b128 then fall on distinct banks.  Tiles
+// are handed out XCD by XCD: workgroup ids are dealt round-robin over the 8
+// XCDs, so id i works on tile (i % 8) * ceil(T/8) + i / 8 and each XCD's L2
+// sees a contiguous band of tiles that share operand panels.
+//
+// The output product appends correction slices to the K loop: for every
+// instance b whose tokens fall in the tile, A's correction columns (the rows of
+// Q_b; rows of other instances are zeroed in registers) meet R1_b, so each
+// token row picks up exactly its own instance's L1 R1_b in the same
+// accumulators before Y is stored once (the fused merge of §2.4).  32-row
+// blocks with no token of b skip those MFMAs.
 #include "dyra_kernels.h"
 
+#include <algorithm>
 #include <cmath>
 
 #include "mfma_tile.h"
@@ -21,164 +36,358 @@ namespace dyra {
 
 namespace {
 
-template <typename E> constexpr int gemm_bk() { return sizeof(E) == 2 ? 64 : 32; }
+// One K slice is 64 bytes of every operand row.
+template <typename E> constexpr int gemm_bk() { return 64 / (int)sizeof(E); }
 
-// Four consecutive values of one row of a row-major D (columns j..j+3).
+// s_waitcnt on the vector-memory counter alone (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that the compiler may not move memory accesses across and
+// that adds no wait of its own (the waits are explicit).
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+// MFMA operand fragment of 16-deep step h from a swizzled LDS slice row
+// (row_base = the row's first byte, sw = (row >> 2) & 3, hf = lane / 32).
+__device__ __forceinline__ bf16x8 slice_frag(const char *row_base, int h, int hf, int sw, const bf16 *) {
+    return *reinterpret_cast<const bf16x8 *>(row_base + (((2 * h + hf) ^ sw) << 4));
+}
+__device__ __forceinline__ f32x8 slice_frag(const char *row_base, int, int hf, int sw, const float *) {
+    const f32x4 lo = *reinterpret_cast<const f32x4 *>(row_base + (((2 * hf) ^ sw) << 4));
+    const f32x4 hi = *reinterpret_cast<const f32x4 *>(row_base + (((2 * hf + 1) ^ sw) << 4));
+    f32x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+}
+
+__device__ __forceinline__ void lds_dma16(const void *g, char *lds) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+// Four consecutive elements packed for one 8-byte (bf16) / 16-byte (fp32) store.
+template <typename E> struct Pack4;
+template <> struct Pack4<bf16> { typedef uint2 type; };
+template <> struct Pack4<float> { typedef uint4 type; };
+
+template <typename E> __device__ __forceinline__ typename Pack4<E>::type pack4(const float (&v)[4]) {
+    if constexpr (sizeof(E) == 2) {
+        union { uint2 u; bf16 e[4]; } w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w.e[q] = to_elem<E>(v[q]);
+        return w.u;
+    } else {
+        return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+    }
+}
+
+// Row-major D: store4(i, j, p) writes columns j..j+3 of row i.
 template <typename E> struct RowStore {
     E *D;
     int64_t ldd;
-    __device__ __forceinline__ void operator()(int64_t i, int64_t j, const float (&v)[4]) const {
-        E *p = D + i * ldd + j;
-        if constexpr (sizeof(E) == 2) {
-            union { uint2 u; bf16 e[4]; } w;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) w.e[q] = to_elem<E>(v[q]);
-            *reinterpret_cast<uint2 *>(p) = w.u;
-        } else {
-            *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
-        }
+    __device__ __forceinline__ void store4(int64_t i, int64_t j, const typename Pack4<E>::type &p) const {
+        *reinterpret_cast<typename Pack4<E>::type *>(D + i * ldd + j) = p;
     }
 };
 
-// Four consecutive rows r..r+3 (= correction indices kk..kk+3 of instance b) of
-// one column c of the stacked right factor, stored as R1t[b][c][kk..kk+3].
+// Stacked right factor: rows r..r+3 (= correction indices kk..kk+3 of
+// instance b = r / kc) of column c, stored as R1t[b][c][kk..kk+3].
 template <typename E> struct R1tStore {
     E *R1t;
     int64_t kc, c2;
-    __device__ __forceinline__ void operator()(int64_t r, int64_t c, const float (&v)[4]) const {
+    __device__ __forceinline__ void store4(int64_t r, int64_t c, const typename Pack4<E>::type &p) const {
         // rows are below 2^31 (instances x correction rank): 32-bit division
         const uint32_t ru = (uint32_t)r, kcu = (uint32_t)kc;
         const int64_t b = ru / kcu, kk = ru - (uint32_t)b * kcu;
-        E *p = R1t + (b * c2 + c) * kc + kk;
-        if constexpr (sizeof(E) == 2) {
-            union { uint2 u; bf16 e[4]; } w;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) w.e[q] = to_elem<E>(v[q]);
-            *reinterpret_cast<uint2 *>(p) = w.u;
-        } else {
-            *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
-        }
+        *reinterpret_cast<typename Pack4<E>::type *>(R1t + (b * c2 + c) * kc + kk) = p;
     }
+};
+
+constexpr size_t kLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
+
+template <int BM, int BN, int NS> constexpr size_t stage_bytes() { return (size_t)NS * (BM + BN) * 64; }
+// LDS of the staged epilogue: the whole tile as [BM][BN + 4] (ROWS) or
+// [BN][BM + 4] elements; tiles that do not fit store straight from registers.
+template <typename E, int BM, int BN, bool ROWS> constexpr size_t epi_bytes() {
+    return ROWS ? sizeof(E) * (size_t)BM * (BN + 4) : sizeof(E) * (size_t)BN * (BM + 4);
+}
+template <typename E, int BM, int BN, bool ROWS> constexpr bool epi_staged() {
+    return epi_bytes<E, BM, BN, ROWS>() <= kLdsBytes;
+}
+
+// Correction slices of the output product (unused when CORR is false):
+// instance b's Q_b sits in columns [kcol, kcol + kc) of A's rows b*n ..
+// b*n + n - 1, and its R1_b is the [N][kc] matrix R1t + b * N * kc.
+template <typename E> struct Corr {
+    const E *R1t;
+    int64_t n;
+    int kcol, kc;
 };
 
 // ROWS = true: the epilogue receives four consecutive columns of one row (the
 // MFMA is issued with the operands swapped, so a lane holds a row of the
-// block); ROWS = false: four consecutive rows of one column.
-template <typename E, int BM, int BN, int WM, int WN, bool ROWS, class Epi>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict__ A, int64_t lda, const E *__restrict__ B,
-                                                  int64_t ldb, int64_t M, int64_t N, int64_t K, int tiles_n,
-                                                  int ntiles, int per_xcd, Epi epi) {
+// block); ROWS = false: four consecutive rows of one column.  K must be a
+// multiple of the slice (32 bf16 / 16 fp32).
+template <typename E, int BM, int BN, int WM, int WN, int NS, bool ROWS, bool CORR, class Epi>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict__ A, int64_t lda,
+                                                            const E *__restrict__ B, int64_t ldb, int64_t M,
+                                                            int64_t N, int64_t K, int tiles_n, int ntiles,
+                                                            int per_xcd, Corr<E> corr, Epi epi) {
+    constexpr int NW = WM * WN;
+    constexpr int NT = 64 * NW;
     constexpr int BK = gemm_bk<E>();
-    constexpr int NT = 64 * WM * WN;
+    constexpr int VEC = 16 / (int)sizeof(E);
     constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
-    using CA = SliceCopy<E, BM, BK, NT>;
-    using CB = SliceCopy<E, BN, BK, NT>;
+    constexpr int IA = BM / 16, ITOT = (BM + BN) / 16;  // 1 KB load blocks (16 rows) per slice
+    constexpr int IPW = (ITOT + NW - 1) / NW, IMIN = ITOT / NW;
+    constexpr int STAGE = (BM + BN) * 64;  // bytes per slice
+    constexpr int KSTEPS = BK / 16;        // 16-deep MFMA steps per slice
+    static_assert(TM >= 1 && TN >= 1 && IMIN >= 1 && NS >= 2 && NS <= 4, "tile shape");
     extern __shared__ __align__(16) char smem[];
-    // stage st holds A at lds + st * STAGE and B right after it (offsets, not a
-    // pointer table, so every access stays an LDS access)
-    constexpr int STAGE = BM * CA::STRIDE + BN * CB::STRIDE;
-    E *const lds = reinterpret_cast<E *>(smem);
-    const int tile = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-    if (tile >= ntiles) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int lr = lane & 31, hf = lane >> 5;
+    const int sw = (lr >> 2) & 3;  // swizzle of the rows this lane reads
+    // a load block is 16 rows x 64 bytes; lane l fills 16-byte position l of it,
+    // i.e. row l / 4, and so fetches chunk (l % 4) ^ ((l / 16) % 4) of that row
+    const int frow = lane >> 2;
+    const int fcol = ((lane & 3) ^ ((lane >> 4) & 3)) * VEC;
+    // persistent: workgroup i runs on XCD i % 8 and walks that XCD's band of
+    // tiles; the stores of one tile drain while the next tile computes
+    const int xcd = (int)(blockIdx.x % 8), slot = (int)(blockIdx.x / 8), nslots = (int)(gridDim.x / 8);
+    for (int tl = slot; tl < per_xcd; tl += nslots) {
+    const int tile = xcd * per_xcd + tl;
+    if (tile >= ntiles) break;
     const int64_t row0 = (int64_t)(tile / tiles_n) * BM;
     const int64_t col0 = (int64_t)(tile % tiles_n) * BN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
-    const int lr = lane & 31, lk = (lane >> 5) * 8;
+
     f32x16 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
-    CA ca;
-    CB cb;
-    // the last slice may be partial: K is a multiple of 32 (bf16) / 16 (fp32)
-    const int64_t S = (K + BK - 1) / BK;
-    if (S > 0) {
-        ca.load(A, lda, row0, M, 0, tid, K);
-        cb.load(B, ldb, col0, N, 0, tid, K);
-        ca.store(lds, tid);
-        cb.store(lds + BM * CA::STRIDE, tid);
+
+    // static slices, then SC correction slices per instance of the tile
+    const int64_t S0 = K / BK;
+    int64_t S = S0, b_first = 0;
+    int SC = 1;
+    if constexpr (CORR) {
+        const int64_t rend = row0 + BM < M ? row0 + BM : M;
+        b_first = row0 / corr.n;
+        SC = (corr.kc + BK - 1) / BK;
+        S = S0 + ((rend - 1) / corr.n - b_first + 1) * SC;
     }
-    __syncthreads();
-    for (int64_t s = 0; s < S; ++s) {
-        const int buf = (int)(s & 1);
-        if (s + 1 < S) {
-            ca.load(A, lda, row0, M, (s + 1) * BK, tid, K);
-            cb.load(B, ldb, col0, N, (s + 1) * BK, tid, K);
+    // instance b, its token rows [rlo, rhi) and slice index sc of slice s >= S0
+    auto inst_of = [&](int64_t s, int64_t &b, int64_t &rlo, int64_t &rhi, int &sc) {
+        const int64_t j = s - S0;
+        const int64_t bi = j / SC;
+        sc = (int)(j - bi * SC);
+        b = b_first + bi;
+        rlo = b * corr.n;
+        rhi = rlo + corr.n < M ? rlo + corr.n : M;
+    };
+    // static-slice source of this wave's q-th load block (rows clamped into
+    // range: rows past M or N are computed and never stored)
+    const E *base[IPW];
+#pragma unroll
+    for (int q = 0; q < IPW; ++q) {
+        const int j = wave + q * NW;
+        if (j < IA) {
+            const int64_t r = row0 + 16 * j + frow;
+            base[q] = A + (r < M ? r : M - 1) * lda + fcol;
+        } else {
+            const int64_t r = col0 + 16 * (j - IA) + frow;
+            base[q] = B + (r < N ? r : N - 1) * ldb + fcol;
         }
-        const E *a = lds + buf * STAGE + (wm * TM * 32 + lr) * CA::STRIDE + lk;
-        const E *b = lds + buf * STAGE + BM * CA::STRIDE + (wn * TN * 32 + lr) * CB::STRIDE + lk;
+    }
+    auto issue = [&](int64_t s) {
+        char *dst = smem + (int)(s % NS) * STAGE;
+        if (!CORR || s < S0) {
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 16) {
-            typename Frag<E>::type fa[TM], fb[TN];
+            for (int q = 0; q < IPW; ++q) {
+                const int j = wave + q * NW;
+                if (q < IMIN || j < ITOT) lds_dma16(base[q] + s * BK, dst + j * 1024);
+            }
+        } else {
+            int64_t b, rlo, rhi;
+            int sc;
+            inst_of(s, b, rlo, rhi, sc);
+            int kl = sc * BK + fcol;
+            kl = kl < corr.kc ? kl : 0;  // columns past kc are fetched from column 0 and never used
 #pragma unroll
-            for (int i = 0; i < TM; ++i) fa[i] = ld_frag(a + i * 32 * CA::STRIDE + kk);
+            for (int q = 0; q < IPW; ++q) {
+                const int j = wave + q * NW;
+                if (!(q < IMIN || j < ITOT)) continue;
+                const E *g;
+                if (j < IA) {
+                    const int64_t r = row0 + 16 * j + frow;
+                    g = A + (r < M ? r : M - 1) * lda + corr.kcol + kl;
+                } else {
+                    const int64_t r = col0 + 16 * (j - IA) + frow;
+                    g = corr.R1t + (b * N + (r < N ? r : N - 1)) * corr.kc + kl;
+                }
+                lds_dma16(g, dst + j * 1024);
+            }
+        }
+    };
+
+    for (int64_t p = 0; p < NS - 1 && p < S; ++p) issue(p);
+    for (int64_t s = 0; s < S; ++s) {
+        // this wave's loads of slice s have landed once at most `later` slices'
+        // worth (issued after it) are outstanding; the barrier then makes every
+        // wave's part visible and frees the buffer of slice s - 1
+        const int64_t later = (S - 1 - s) < (NS - 2) ? (S - 1 - s) : (NS - 2);
+        if (later >= 2) wait_vmcnt<2 * IMIN>();
+        else if (later == 1) wait_vmcnt<IMIN>();
+        else wait_vmcnt<0>();
+        barrier_only();
+        if (s + NS - 1 < S) issue(s + NS - 1);
+
+        int ksteps = KSTEPS;
+        uint32_t live = ~0u;
+        int64_t rlo = 0, rhi = 0;
+        if (CORR && s >= S0) {
+            int64_t b;
+            int sc;
+            inst_of(s, b, rlo, rhi, sc);
+            const int kleft = (corr.kc - sc * BK) / 16;
+            ksteps = kleft < KSTEPS ? kleft : KSTEPS;
+            live = 0;
 #pragma unroll
-            for (int j = 0; j < TN; ++j) fb[j] = ld_frag(b + j * 32 * CB::STRIDE + kk);
+            for (int i = 0; i < TM; ++i) {
+                const int64_t rb = row0 + (wm * TM + i) * 32;
+                live |= (rb < rhi && rb + 32 > rlo) ? (1u << i) : 0u;
+            }
+        }
+        const char *sa = smem + (int)(s % NS) * STAGE + ((wm * TM) * 32 + lr) * 64;
+        const char *sb = smem + (int)(s % NS) * STAGE + BM * 64 + ((wn * TN) * 32 + lr) * 64;
+        // all fragments of the slice are requested before the first MFMA, so
+        // only the first step waits on LDS latency
+        typename Frag<E>::type fa[KSTEPS][TM], fb[KSTEPS][TN];
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+        for (int h = 0; h < KSTEPS; ++h) {
+            if (h >= ksteps) break;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) fb[h][j] = slice_frag(sb + j * 32 * 64, h, hf, sw, (const E *)nullptr);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) fa[h][i] = slice_frag(sa + i * 32 * 64, h, hf, sw, (const E *)nullptr);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int h = 0; h < KSTEPS; ++h) {
+            if (h >= ksteps) break;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                typename Frag<E>::type a = fa[h][i];
+                if (CORR && s >= S0) {
+                    if (!((live >> i) & 1u)) continue;
+                    const int64_t r = row0 + (wm * TM + i) * 32 + lr;
+                    if (!(r >= rlo && r < rhi)) a = zero_frag(a);
+                }
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[i][j] = ROWS ? mma16(acc[i][j], fb[j], fa[i]) : mma16(acc[i][j], fa[i], fb[j]);
-        }
-        if (s + 1 < S) {
-            ca.store(lds + (buf ^ 1) * STAGE, tid);
-            cb.store(lds + (buf ^ 1) * STAGE + BM * CA::STRIDE, tid);
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                const int64_t rb = row0 + wm * TM * 32 + i * 32, cb0 = col0 + wn * TN * 32 + j * 32;
-                if (ROWS) {
-                    const int64_t r = rb + lr, c = cb0 + acc_row(lane, 4 * g);
-                    if (r < M && c < N) epi(r, c, v);
-                } else {
-                    const int64_t r = rb + acc_row(lane, 4 * g), c = cb0 + lr;
-                    if (r < M && c < N) epi(r, c, v);
-                }
+                    acc[i][j] = ROWS ? mma16(acc[i][j], fb[h][j], a) : mma16(acc[i][j], a, fb[h][j]);
             }
+        }
+    }
+    __syncthreads();
+    // ---- epilogue.  A lane holds four consecutive elements of the store's
+    // contiguous direction (columns for ROWS, rows otherwise).  When the tile
+    // fits in LDS it is staged there and written out with consecutive lanes on
+    // consecutive addresses; otherwise each lane stores its own runs.
+    constexpr int OR = ROWS ? BM : BN, OC = ROWS ? BN : BM;  // LDS tile [OR][OC + 4]
+    constexpr int OS = OC + 4;
+    E *const lds = reinterpret_cast<E *>(smem);
+    if constexpr (epi_staged<E, BM, BN, ROWS>()) {
+        typedef typename Pack4<E>::type P;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                        acc[i][j][4 * g + 3]};
+                    const int ti = (wm * TM + i) * 32, tj = (wn * TN + j) * 32;
+                    const int lrow = ROWS ? ti + lr : tj + lr;              // LDS row
+                    const int lcol = (ROWS ? tj : ti) + acc_row(lane, 4 * g);  // 4 consecutive
+                    *reinterpret_cast<P *>(lds + lrow * OS + lcol) = pack4<E>(v);
+                }
+        __syncthreads();
+        constexpr int CPR = OC / 4, CH = OR * CPR;
+#pragma unroll 4
+        for (int c = tid; c < CH; c += NT) {
+            const int orow = c / CPR, ocol = (c % CPR) * 4;
+            const P v = *reinterpret_cast<const P *>(lds + orow * OS + ocol);
+            const int64_t r = row0 + (ROWS ? orow : ocol), cc = col0 + (ROWS ? ocol : orow);
+            if (r < M && cc < N) epi.store4(r, cc, v);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                        acc[i][j][4 * g + 3]};
+                    const int64_t rb = row0 + wm * TM * 32 + i * 32, cb0 = col0 + wn * TN * 32 + j * 32;
+                    const int64_t r = ROWS ? rb + lr : rb + acc_row(lane, 4 * g);
+                    const int64_t c = ROWS ? cb0 + acc_row(lane, 4 * g) : cb0 + lr;
+                    if (r < M && c < N) epi.store4(r, c, pack4<E>(v));
+                }
+    }
+    // the epilogue's LDS reads finish before the next tile's loads land there
+    __syncthreads();
+    }
 }
 
-template <typename E, int BM, int BN> size_t gemm_smem() {
-    constexpr int BK = gemm_bk<E>();
-    return sizeof(E) * (size_t)2 * (BM + BN) * (BK + Lay<E>::PAD);
+template <typename E, int BM, int BN, int NS, bool ROWS> constexpr size_t gemm_smem() {
+    return (epi_staged<E, BM, BN, ROWS>() && epi_bytes<E, BM, BN, ROWS>() > stage_bytes<BM, BN, NS>())
+               ? epi_bytes<E, BM, BN, ROWS>()
+               : stage_bytes<BM, BN, NS>();
 }
 
-template <typename E, int BM, int BN, int WM, int WN, bool ROWS, class Epi>
-hipError_t gemm_launch(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N, int64_t K, Epi epi,
-                       hipStream_t st) {
-    auto kfn = gemm_kernel<E, BM, BN, WM, WN, ROWS, Epi>;
-    const size_t smem = gemm_smem<E, BM, BN>();
-    static bool attr = false;
-    if (!attr) {
+template <typename E, int BM, int BN, int WM, int WN, int NS, bool ROWS, bool CORR, class Epi>
+hipError_t gemm_launch(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N, int64_t K,
+                       const Corr<E> &corr, Epi epi, hipStream_t st) {
+    static_assert(gemm_smem<E, BM, BN, NS, ROWS>() <= kLdsBytes, "LDS");
+    if (K % gemm_bk<E>() != 0) return hipErrorInvalidValue;
+    auto kfn = gemm_kernel<E, BM, BN, WM, WN, NS, ROWS, CORR, Epi>;
+    constexpr size_t smem = gemm_smem<E, BM, BN, NS, ROWS>();
+    static int per_cu = 0;  // resident workgroups per CU
+    if (per_cu == 0) {
         hipError_t e = hipFuncSetAttribute((const void *)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;
-        attr = true;
+        int occ = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kfn, 64 * WM * WN, smem);
+        if (e != hipSuccess) return e;
+        per_cu = occ > 0 ? occ : 1;
     }
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
     const int ntiles = tiles_m * tiles_n;
     const int per_xcd = (ntiles + 7) / 8;
-    hipLaunchKernelGGL(kfn, dim3((unsigned)(8 * per_xcd)), dim3(64 * WM * WN), smem, st, A, lda, B, ldb, M, N, K, tiles_n,
-                       ntiles, per_xcd, epi);
+    // one resident workgroup per slot: 32 CUs per XCD on gfx950 (256 in all)
+    const int nslots = std::min(per_xcd, 32 * per_cu);
+    hipLaunchKernelGGL(kfn, dim3((unsigned)(8 * nslots)), dim3(64 * WM * WN), smem, st, A, lda, B, ldb, M, N, K,
+                       tiles_n, ntiles, per_xcd, corr, epi);
     return hipGetLastError();
 }
 
 // Tile shape with the smallest estimated time: rounds of 256 concurrent tiles
-// times tile area, with smaller wavefront tiles charged for their higher LDS
-// traffic per MFMA.
-enum class Shape { T256x256, T256x128, T128x128, T64x64 };
+// times tile area, with smaller tiles charged for their higher LDS and L2
+// traffic per MFMA (weights from timings of the shapes on gfx950).
+enum class Shape { T256x256, T256x160, T256x128, T128x128, T64x64 };
 
 Shape pick_shape(int64_t M, int64_t N) {
     if (N <= 64) return Shape::T64x64;
     struct C { Shape s; int bm, bn; double w; } cands[] = {
-        {Shape::T256x256, 256, 256, 1.0}, {Shape::T256x128, 256, 128, 1.1}, {Shape::T128x128, 128, 128, 1.3}};
+        {Shape::T256x256, 256, 256, 1.0}, {Shape::T256x160, 256, 160, 1.2}, {Shape::T256x128, 256, 128, 1.16},
+        {Shape::T128x128, 128, 128, 1.3}};
     Shape best = Shape::T128x128;
     double best_cost = 1e300;
     for (const C &c : cands) {
@@ -193,14 +402,15 @@ Shape pick_shape(int64_t M, int64_t N) {
     return best;
 }
 
-template <typename E, bool ROWS, class Epi>
-hipError_t gemm_dispatch(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N, int64_t K, Epi epi,
-                         hipStream_t st) {
+template <typename E, bool ROWS, bool CORR, class Epi>
+hipError_t gemm_dispatch(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N, int64_t K,
+                         const Corr<E> &corr, Epi epi, hipStream_t st) {
     switch (pick_shape(M, N)) {
-    case Shape::T256x256: return gemm_launch<E, 256, 256, 2, 2, ROWS>(A, lda, B, ldb, M, N, K, epi, st);
-    case Shape::T256x128: return gemm_launch<E, 256, 128, 2, 2, ROWS>(A, lda, B, ldb, M, N, K, epi, st);
-    case Shape::T128x128: return gemm_launch<E, 128, 128, 2, 2, ROWS>(A, lda, B, ldb, M, N, K, epi, st);
-    case Shape::T64x64: return gemm_launch<E, 64, 64, 2, 2, ROWS>(A, lda, B, ldb, M, N, K, epi, st);
+    case Shape::T256x256: return gemm_launch<E, 256, 256, 4, 2, 4, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
+    case Shape::T256x160: return gemm_launch<E, 256, 160, 4, 1, 4, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
+    case Shape::T256x128: return gemm_launch<E, 256, 128, 4, 2, 4, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
+    case Shape::T128x128: return gemm_launch<E, 128, 128, 2, 2, 4, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
+    case Shape::T64x64: return gemm_launch<E, 64, 64, 2, 2, 4, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
     }
     return hipErrorInvalidValue;
 }
@@ -211,14 +421,25 @@ template <typename E>
 hipError_t launch_gemm_store(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N, int64_t K,
                              E *D, int64_t ldd, hipStream_t st) {
     if (M <= 0 || N <= 0) return hipSuccess;
-    return gemm_dispatch<E, true>(A, lda, B, ldb, M, N, K, RowStore<E>{D, ldd}, st);
+    return gemm_dispatch<E, true, false>(A, lda, B, ldb, M, N, K, Corr<E>{}, RowStore<E>{D, ldd}, st);
 }
 
 template <typename E>
 hipError_t launch_right(const E *Mp, const E *Wres_t, int64_t rows, int64_t c1, int64_t c2, int kc, E *R1t,
                         hipStream_t st) {
     if (rows <= 0) return hipSuccess;
-    return gemm_dispatch<E, false>(Mp, c1, Wres_t, c1, rows, c2, c1, R1tStore<E>{R1t, kc, c2}, st);
+    return gemm_dispatch<E, false, false>(Mp, c1, Wres_t, c1, rows, c2, c1, Corr<E>{}, R1tStore<E>{R1t, kc, c2},
+                                          st);
+}
+
+template <typename E>
+hipError_t launch_output(const E *T, int64_t ldt, int kw, int kc, const E *Vs, const E *R1t, int64_t Ntok,
+                         int64_t n, int64_t c2, E *Y, hipStream_t st) {
+    if (Ntok <= 0) return hipSuccess;
+    if (kc > 0 && (n < 1 || kc > 64 || kc % 16 != 0)) return hipErrorInvalidValue;
+    if (kc == 0) return gemm_dispatch<E, true, false>(T, ldt, Vs, kw, Ntok, c2, kw, Corr<E>{}, RowStore<E>{Y, c2}, st);
+    return gemm_dispatch<E, true, true>(T, ldt, Vs, kw, Ntok, c2, kw, Corr<E>{R1t, n, kw, kc}, RowStore<E>{Y, c2},
+                                        st);
 }
 
 template hipError_t launch_gemm_store<bf16>(const bf16 *, int64_t, const bf16 *, int64_t, int64_t, int64_t, int64_t,
@@ -229,5 +450,9 @@ template hipError_t launch_right<bf16>(const bf16 *, const bf16 *, int64_t, int6
                                        hipStream_t);
 template hipError_t launch_right<float>(const float *, const float *, int64_t, int64_t, int64_t, int, float *,
                                         hipStream_t);
+template hipError_t launch_output<bf16>(const bf16 *, int64_t, int, int, const bf16 *, const bf16 *, int64_t,
+                                        int64_t, int64_t, bf16 *, hipStream_t);
+template hipError_t launch_output<float>(const float *, int64_t, int, int, const float *, const float *, int64_t,
+                                         int64_t, int64_t, float *, hipStream_t);
 
 }  // namespace dyra

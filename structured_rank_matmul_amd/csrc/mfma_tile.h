@@ -69,9 +69,9 @@ __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ int acc_row(int lane, int t) { return 8 * (t >> 2) + 4 * (lane >> 5) + (t & 3); }
 
 // Global -> register -> LDS copy of a [ROWS][BK] slice of a row-major matrix
-// (leading dimension ld elements) starting at (row0, k0).  Rows at or beyond
-// `nrows` and columns at or beyond `kmax` are zero-filled (kmax a multiple of
-// the 16-byte vector).  LDS layout [ROWS][BK + PAD].
+// (leading dimension ld elements) starting at (row0, k0).  Rows outside
+// [rlo, rhi) and columns at or beyond `kmax` are zero-filled (kmax a multiple
+// of the 16-byte vector).  LDS layout [ROWS][BK + PAD].
 template <typename E, int ROWS, int BK, int NT> struct SliceCopy {
     static constexpr int VEC = Lay<E>::VEC;
     static constexpr int CPR = BK / VEC;
@@ -80,16 +80,17 @@ template <typename E, int ROWS, int BK, int NT> struct SliceCopy {
     static constexpr int STRIDE = BK + Lay<E>::PAD;
     uint4 reg[PER];
 
-    __device__ __forceinline__ void load(const E *g, int64_t ld, int64_t row0, int64_t nrows, int64_t k0,
-                                         int tid, int64_t kmax = INT64_MAX) {
+    __device__ __forceinline__ void load(const E *g, int64_t ld, int64_t row0, int64_t rlo, int64_t rhi, int64_t k0,
+                                         int tid, int64_t kmax) {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int c = tid + p * NT;
             const int row = c / CPR;
             const int col = (c % CPR) * VEC;
             // branch-free: an out-of-range chunk loads element 0 and is zeroed
-            const bool ok = (CHUNKS % NT == 0 || c < CHUNKS) && row0 + row < nrows && k0 + col < kmax;
-            const int64_t off = ok ? (row0 + row) * ld + k0 + col : 0;
+            const int64_t r = row0 + row;
+            const bool ok = (CHUNKS % NT == 0 || c < CHUNKS) && r >= rlo && r < rhi && k0 + col < kmax;
+            const int64_t off = ok ? r * ld + k0 + col : 0;
             const uint4 v = *reinterpret_cast<const uint4 *>(g + off);
             reg[p] = ok ? v : make_uint4(0, 0, 0, 0);
         }

@@ -12,11 +12,19 @@
 // lambda = 0), so rounding it and Q_b^T X_b to bf16 is not amplified by the
 // conditioning of L1_b as the normal-equation form would be.
 //
-//   gram_q   one workgroup per instance: G (MFMA over tokens), Cholesky and the
-//            triangular inverse C^-1 with the 64 x 64 matrix held in registers
-//            (16 entries per thread, one barrier per column), then
-//            Q_b^T = C^-1 L1_b^T by float32 MFMA, written token-contiguous (Qt)
-//            and row-major over L1_b.
+// L1_b lives in columns [off, off + kc) of the rows b*n .. b*n + n - 1 of the
+// row-major pass output T (leading dimension ldt) and Q_b overwrites it there.
+//
+//   cholq (bf16)  workgroup (token block of 256, instance b): G by MFMA over
+//            all n tokens of b, then every wavefront factors G with one matrix
+//            row per lane and, in the same elimination steps, turns its 64
+//            token rows of L1_b into rows of Q_b: factoring [G; L1_b] leaves
+//            L1_b C^-T in the lower block.  The pivot row's entries reach all
+//            lanes through v_readlane, so the factorisation has no barrier and
+//            no LDS traffic.
+//   gram_q (float32)  one workgroup per instance, all in float64: G, a
+//            right-looking Cholesky and the inverse C^-1 with 16 matrix entries
+//            per thread, then q_t = C^-1 l_t per token.
 //   mprime   workgroup (instance b, 256 input features): M'_b = Q_b^T X_b.
 #include "dyra_kernels.h"
 
@@ -27,21 +35,12 @@ namespace dyra {
 namespace {
 
 constexpr int NT = 256;
-constexpr int TK = 32;  // tokens per slice of the token contraction
+constexpr int TK = 32;  // tokens per slice of the token contraction (mprime)
 
 // Optional per-phase timestamps for profiling builds (empty in the library).
 #ifndef DYRA_PHASE_MARK
 #define DYRA_PHASE_MARK(i)
 #endif
-
-__device__ __forceinline__ f32x8 frag_f32(const bf16 *p) {
-    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(p);
-    f32x8 r;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) r[q] = (float)v[q];
-    return r;
-}
-__device__ __forceinline__ f32x8 frag_f32(const float *p) { return ld_frag(p); }
 
 // Transposes a [TK tokens][kc] slice of a row-major [tokens][kc] matrix into
 // LDS dst[feature][token] (row stride ST); tokens at or beyond `tokens` read 0.
@@ -64,77 +63,184 @@ __device__ __forceinline__ void load_transposed(const E *src, int64_t ld, int64_
     }
 }
 
-// The k x k solve runs in float32 for bf16 data and in float64 for float32
-// data (the float32 path is held to a 1e-5 relative error, which a float32
-// Gram matrix cannot give when L1_b is ill-conditioned).
-template <typename E> struct SolveT { typedef float type; };
-template <> struct SolveT<float> { typedef double type; };
+__device__ __forceinline__ float bcast(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
 
-template <typename E>
-__global__ __launch_bounds__(NT) void gram_q_kernel(E *__restrict__ L1, int64_t n, int64_t npad, int kc_real, int kc,
-                                                    float lambda, E *__restrict__ Qt, int *__restrict__ flags) {
-    typedef typename SolveT<E>::type AT;
-    constexpr bool kMfma = sizeof(E) == 2;  // bf16: Gram and Q on MFMA; float32: float64 FMA
-    constexpr int ST = TK + Lay<E>::PAD;
-    constexpr int GS = 68;  // row stride of the LDS matrix (16-byte aligned rows)
-    __shared__ __align__(16) E Lt[64 * ST];
+// ---------------------------------------------------------------- bf16 path
+template <int KC>
+__global__ __launch_bounds__(NT) void cholq_kernel(bf16 *__restrict__ T, int64_t ldt, int64_t off, int64_t n,
+                                                   int64_t npad, int kc_real, float lambda, bf16 *__restrict__ Qt,
+                                                   int *__restrict__ flags) {
+    constexpr int GS = 68;        // row stride (floats) of G in LDS
+    constexpr int TT = 64;        // tokens per Gram chunk
+    constexpr int ST = TT + 8;    // row stride (bf16) of the transposed chunk
+    constexpr int NBLK = (KC + 31) / 32;
+    __shared__ __align__(16) bf16 Lt[64 * ST];
+    __shared__ __align__(16) float Gs[64 * GS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 31, lk = (lane >> 5) * 8;
+    const int64_t b = blockIdx.y;
+    bf16 *const Tb = T + b * n * ldt + off;  // token t of instance b: Tb + t * ldt
+    DYRA_PHASE_MARK(0);
+
+    // ---- G = L1_b^T L1_b over all n tokens, 32x32 blocks on MFMA
+    const int wm = wave >> 1, wn = wave & 1;
+    const bool gact = wm < NBLK && wn < NBLK;
+    f32x16 acc = f32x16{};
+    uint4 reg[2];
+    // chunk of TT tokens x 64 features: thread c = tid + 256 p loads token
+    // c % 64, features 8 (c / 64) .. +7 (features >= KC and tokens >= n read 0)
+    auto gload = [&](int64_t t0) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int c = tid + p * NT;
+            const int tok = c & 63, j0 = (c >> 6) * 8;
+            const bool ok = t0 + tok < n && j0 < KC;
+            const uint4 v = *reinterpret_cast<const uint4 *>(Tb + (ok ? (t0 + tok) * ldt + j0 : 0));
+            reg[p] = ok ? v : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto gstore = [&]() {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int c = tid + p * NT;
+            const int tok = c & 63, j0 = (c >> 6) * 8;
+            union { uint4 u; bf16 e[8]; } v;
+            v.u = reg[p];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) Lt[(j0 + q) * ST + tok] = v.e[q];
+        }
+    };
+    const int64_t nch = (n + TT - 1) / TT;
+    gload(0);
+    for (int64_t ch = 0; ch < nch; ++ch) {
+        __syncthreads();
+        gstore();
+        __syncthreads();
+        if (ch + 1 < nch) gload((ch + 1) * TT);
+        if (gact) {
+#pragma unroll
+            for (int kk = 0; kk < TT; kk += 16)
+                acc = mma16(acc, ld_frag(Lt + (wm * 32 + lr) * ST + kk + lk), ld_frag(Lt + (wn * 32 + lr) * ST + kk + lk));
+        }
+    }
+    if (gact) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) Gs[(wm * 32 + acc_row(lane, t)) * GS + wn * 32 + lr] = acc[t];
+    }
+    __syncthreads();
+    DYRA_PHASE_MARK(1);
+
+    // ---- lane i holds row i of G + lambda I (identity rows past kc_real)
+    const int i = lane;
+    float g[KC];
+#pragma unroll
+    for (int m = 0; m < KC; m += 4) {
+        const float4 v = *reinterpret_cast<const float4 *>(&Gs[(i < KC ? i : 0) * GS + m]);
+        g[m] = v.x; g[m + 1] = v.y; g[m + 2] = v.z; g[m + 3] = v.w;
+    }
+    const float diag = i < kc_real ? Gs[i * GS + i] : 0.f;
+#pragma unroll
+    for (int m = 0; m < KC; ++m) {
+        const float e = (i < kc_real && m < kc_real) ? g[m] : 0.f;
+        g[m] = (m == i) ? (i < kc_real ? e + lambda : 1.f) : e;
+    }
+    // a pivot at or below the working precision times the largest diagonal
+    // marks a numerically singular G (possible only for lambda = 0)
+    float dmax = diag;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) dmax = fmaxf(dmax, __shfl_xor(dmax, o));
+    const float th = lambda > 0.f ? 0.f : (float)KC * 1.2e-7f * dmax;
+    bool fail = !(dmax > 0.f);
+
+    // ---- this wavefront's 64 token rows of L1_b
+    const int64_t t = (int64_t)blockIdx.x * NT + wave * 64 + lane;
+    const bool tin = t < n;
+    float l[KC];
+#pragma unroll
+    for (int m = 0; m < KC; m += 8) {
+        union { uint4 u; bf16 e[8]; } v;
+        v.u = *reinterpret_cast<const uint4 *>(Tb + (tin ? t * ldt : 0) + m);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) l[m + q] = tin ? (float)v.e[q] : 0.f;
+    }
+    DYRA_PHASE_MARK(2);
+
+    // ---- elimination: step k takes pivot row k (lane k) to all lanes
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+        float pk = bcast(g[k], k);
+        const bool bad = k < kc_real && !(pk > th);  // padding pivots are 1
+        fail = fail || bad;
+        pk = bad ? 1.f : pk;
+        const float rp = 1.f / pk;
+        const float a = g[k] * rp;      // G rows: C[i][k] / C[k][k]
+        const float bt = l[k] * rp;     // token rows: Q[t][k] / C[k][k]
+        l[k] = l[k] * (1.f / sqrtf(pk));
+#pragma unroll
+        for (int m = k + 1; m < KC; ++m) {
+            const float s = bcast(g[m], k);   // trailing row k = C[m][k] C[k][k]
+            g[m] = fmaf(-a, s, g[m]);
+            l[m] = fmaf(-bt, s, l[m]);
+        }
+    }
+    DYRA_PHASE_MARK(3);
+
+    // ---- Q_b rows in place of L1_b, and Qt[b] = Q_b^T (token-contiguous, zero past n)
+    if (tin) {
+#pragma unroll
+        for (int m = 0; m < KC; m += 8) {
+            union { uint4 u; bf16 e[8]; } v;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v.e[q] = fail ? bf16(0.f) : (bf16)l[m + q];
+            *reinterpret_cast<uint4 *>(Tb + t * ldt + m) = v.u;
+        }
+    }
+    if (t < npad) {
+        bf16 *qb = Qt + b * KC * npad + t;
+#pragma unroll
+        for (int m = 0; m < KC; ++m) qb[(int64_t)m * npad] = fail ? bf16(0.f) : (bf16)l[m];
+    }
+    if (blockIdx.x == 0 && tid == 0) flags[b] = fail ? 1 : 0;
+    DYRA_PHASE_MARK(4);
+}
+
+// ------------------------------------------------------------- float32 path
+__global__ __launch_bounds__(NT) void gram_q_f32_kernel(float *__restrict__ T, int64_t ldt, int64_t off, int64_t n,
+                                                        int64_t npad, int kc_real, int kc, float lambda,
+                                                        float *__restrict__ Qt, int *__restrict__ flags) {
+    typedef double AT;
+    constexpr int GS = 68;
+    __shared__ __align__(16) float Lt[TK * 64];
     __shared__ __align__(16) AT G[64 * GS];
     __shared__ AT vec[2][64];
     __shared__ AT rowv[2][64];
     __shared__ int fail;
     __shared__ AT thresh;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lr = lane & 31, lk = (lane >> 5) * 8;
+    const int tid = threadIdx.x;
     const int j = tid & 63, i0 = tid >> 6;  // this thread owns entries (i0 + 4q, j), q = 0..15
     const int64_t b = blockIdx.x;
-    E *Lb = L1 + b * n * kc;
-    DYRA_PHASE_MARK(0);
+    float *Lb = T + b * n * ldt + off;
 
-    for (int e = tid; e < 64 * GS; e += NT) G[e] = AT(0);
     if (tid == 0) fail = 0;
     AT g[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) g[q] = AT(0);
-    // ---- Gram matrix G = L1_b^T L1_b over the instance's tokens
-    if constexpr (kMfma) {
-        const int wm = wave >> 1, wn = wave & 1;
-        const bool active = wm * 32 < kc && wn * 32 < kc;
-        for (int e = tid; e < 64 * ST; e += NT) Lt[e] = to_elem<E>(0.f);
+    // ---- G = L1_b^T L1_b, token slices staged row-major in Lt ([token][feature])
+    for (int64_t t0 = 0; t0 < n; t0 += TK) {
         __syncthreads();
-        f32x16 acc = f32x16{};
-        for (int64_t t0 = 0; t0 < n; t0 += TK) {
-            load_transposed<E, ST>(Lb, kc, t0, n, 0, kc, kc, Lt, tid);
-            __syncthreads();
-            if (active) {
-#pragma unroll
-                for (int kk = 0; kk < TK; kk += 16)
-                    acc = mma16(acc, ld_frag(Lt + (wm * 32 + lr) * ST + kk + lk),
-                                ld_frag(Lt + (wn * 32 + lr) * ST + kk + lk));
-            }
-            __syncthreads();
-        }
-        if (active) {
-#pragma unroll
-            for (int t = 0; t < 16; ++t) G[(wm * 32 + acc_row(lane, t)) * GS + wn * 32 + lr] = acc[t];
+        for (int e = tid; e < TK * 64; e += NT) {
+            const int tt = e >> 6, c = e & 63;
+            Lt[tt * 64 + c] = (t0 + tt < n && c < kc) ? Lb[(t0 + tt) * ldt + c] : 0.f;
         }
         __syncthreads();
+        const int tc = (int)((n - t0) < TK ? (n - t0) : TK);
+        for (int tt = 0; tt < tc; ++tt) {
+            const AT lj = (AT)Lt[tt * 64 + j];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) g[q] = G[(i0 + 4 * q) * GS + j];
-    } else {
-        // token slices staged row-major in Lt ([token][feature], row stride 64)
-        for (int64_t t0 = 0; t0 < n; t0 += TK) {
-            __syncthreads();
-            for (int e = tid; e < TK * 64; e += NT) {
-                const int t = e >> 6, c = e & 63;
-                Lt[t * 64 + c] = (t0 + t < n && c < kc) ? Lb[(t0 + t) * kc + c] : to_elem<E>(0.f);
-            }
-            __syncthreads();
-            const int tc = (int)((n - t0) < TK ? (n - t0) : TK);
-            for (int t = 0; t < tc; ++t) {
-                const AT lj = (AT)to_f32(Lt[t * 64 + j]);
-#pragma unroll
-                for (int q = 0; q < 16; ++q) g[q] += (AT)to_f32(Lt[t * 64 + i0 + 4 * q]) * lj;
-            }
+            for (int q = 0; q < 16; ++q) g[q] += (AT)Lt[tt * 64 + i0 + 4 * q] * lj;
         }
     }
     // ---- G + lambda I on the real indices, identity on the padding
@@ -144,23 +250,19 @@ __global__ __launch_bounds__(NT) void gram_q_kernel(E *__restrict__ L1, int64_t 
         if (i < kc_real && j < kc_real) g[q] += (i == j) ? (AT)lambda : AT(0);
         else g[q] = (i == j) ? AT(1) : AT(0);
     }
-    // a pivot below the working precision times the largest diagonal means a
-    // numerically singular Gram matrix (possible only for lambda = 0)
 #pragma unroll
     for (int q = 0; q < 16; ++q)
         if (i0 + 4 * q == j) vec[0][j] = g[q];  // the diagonal, one owner per entry
     __syncthreads();
-    DYRA_PHASE_MARK(1);
     if (tid == 0) {
         AT dmax = AT(0);
         for (int i = 0; i < kc; ++i) dmax = dmax > vec[0][i] ? dmax : vec[0][i];
-        const AT eps = sizeof(AT) == 4 ? AT(1.2e-7) : AT(2.3e-16);
-        thresh = lambda > 0.f ? AT(0) : (AT)kc * eps * dmax;
+        thresh = lambda > 0.f ? AT(0) : (AT)kc * AT(2.3e-16) * dmax;
         if (!(dmax > AT(0))) fail = 1;
     }
     __syncthreads();
     const AT th = thresh;
-    // ---- Cholesky G = C C^T (lower), right-looking, one barrier per column, no branches
+    // ---- Cholesky G = C C^T (lower), right-looking, one barrier per column
     for (int k = 0; k < kc; ++k) {
         AT *colk = vec[k & 1];
         if (j == k) {
@@ -169,7 +271,7 @@ __global__ __launch_bounds__(NT) void gram_q_kernel(E *__restrict__ L1, int64_t 
         }
         __syncthreads();
         AT pk = colk[k];
-        if (!(pk > th)) {
+        if (k < kc_real && !(pk > th)) {
             if (tid == 0) fail = 1;
             pk = AT(1);
         }
@@ -186,12 +288,10 @@ __global__ __launch_bounds__(NT) void gram_q_kernel(E *__restrict__ L1, int64_t 
             g[q] = (jact && i >= k && i < kc) ? v : g[q];
         }
     }
-    // upper part to zero: g now holds C
 #pragma unroll
     for (int q = 0; q < 16; ++q) g[q] = (j > i0 + 4 * q) ? AT(0) : g[q];
     __syncthreads();
-    DYRA_PHASE_MARK(2);
-    // ---- C^-1 by in-place Gauss-Jordan (stays lower-triangular), no branches
+    // ---- C^-1 by in-place Gauss-Jordan (stays lower-triangular)
     for (int k = 0; k < kc; ++k) {
         AT *colk = vec[k & 1];
         AT *rowk = rowv[k & 1];
@@ -200,7 +300,6 @@ __global__ __launch_bounds__(NT) void gram_q_kernel(E *__restrict__ L1, int64_t 
             for (int q = 0; q < 16; ++q) colk[i0 + 4 * q] = g[q];
         }
         if ((k & 3) == i0) {
-            // g[k >> 2] without a runtime register index (which would go to scratch)
             AT v = AT(0);
 #pragma unroll
             for (int q = 0; q < 16; ++q) v = (q == (k >> 2)) ? g[q] : v;
@@ -220,56 +319,24 @@ __global__ __launch_bounds__(NT) void gram_q_kernel(E *__restrict__ L1, int64_t 
         }
     }
     __syncthreads();
-    DYRA_PHASE_MARK(3);
     const bool failed = fail != 0;
 #pragma unroll
     for (int q = 0; q < 16; ++q) G[(i0 + 4 * q) * GS + j] = failed ? AT(0) : g[q];
     __syncthreads();
-    // ---- Q^T = C^-1 L1_b^T -> Qt[b] (token-contiguous) and Q in place of L1_b
-    E *Qb = Qt + b * kc * npad;
-    if constexpr (kMfma) {
-        const int nrb = (kc + 31) / 32;
-        for (int64_t tb = wave; tb * 32 < npad; tb += 4) {
-            const int64_t t = tb * 32 + lr;
-            f32x16 z[2] = {f32x16{}, f32x16{}};
-            for (int kk = 0; kk < kc; kk += 16) {
-                const f32x8 fb = t < n ? frag_f32(Lb + t * kc + kk + lk) : f32x8{};
-                for (int ib = 0; ib < nrb; ++ib)
-                    z[ib] = mma16(z[ib], ld_frag((const float *)&G[(ib * 32 + lr) * GS + kk + lk]), fb);
-            }
-            for (int ib = 0; ib < nrb; ++ib) {
+    // ---- one token per thread: q_t = C^-1 l_t
+    float *Qb = Qt + b * kc * npad;
+    for (int64_t t = tid; t < npad; t += NT) {
+        AT l[64];
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int i = ib * 32 + acc_row(lane, q);
-                    if (i < kc) Qb[(int64_t)i * npad + t] = to_elem<E>(z[ib][q]);
-                }
-                if (t < n) {
+        for (int c = 0; c < 64; ++c) l[c] = (t < n && c < kc) ? (AT)Lb[t * ldt + c] : AT(0);
+        for (int i = 0; i < kc; ++i) {
+            AT sum = AT(0);
 #pragma unroll
-                    for (int gg = 0; gg < 4; ++gg) {
-                        const int i = ib * 32 + acc_row(lane, 4 * gg);
-                        if (i >= kc) continue;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) Lb[t * kc + i + q] = to_elem<E>(z[ib][4 * gg + q]);
-                    }
-                }
-            }
-        }
-    } else {
-        // one token per thread: q_t = C^-1 l_t in float64
-        for (int64_t t = tid; t < npad; t += NT) {
-            AT l[64];
-#pragma unroll
-            for (int c = 0; c < 64; ++c) l[c] = (t < n && c < kc) ? (AT)to_f32(Lb[t * kc + c]) : AT(0);
-            for (int i = 0; i < kc; ++i) {
-                AT sum = AT(0);
-#pragma unroll
-                for (int c = 0; c < 64; ++c) sum += G[i * GS + c] * l[c];
-                Qb[(int64_t)i * npad + t] = to_elem<E>((float)sum);
-                if (t < n) Lb[t * kc + i] = to_elem<E>((float)sum);
-            }
+            for (int c = 0; c < 64; ++c) sum += G[i * GS + c] * l[c];
+            Qb[(int64_t)i * npad + t] = (float)sum;
+            if (t < n) Lb[t * ldt + i] = (float)sum;
         }
     }
-    DYRA_PHASE_MARK(4);
     if (tid == 0) flags[b] = failed ? 1 : 0;
 }
 
@@ -331,12 +398,28 @@ __global__ __launch_bounds__(NT) void mprime_kernel(const E *__restrict__ X, con
 
 }  // namespace
 
-template <typename E>
-hipError_t launch_gram_q(E *L1, int64_t B, int64_t n, int64_t npad, int kc_real, int kc, float lambda, E *Qt,
-                         int *flags, hipStream_t st) {
+template <>
+hipError_t launch_gram_q<bf16>(bf16 *T, int64_t ldt, int64_t off, int64_t B, int64_t n, int64_t npad, int kc_real,
+                               int kc, float lambda, bf16 *Qt, int *flags, hipStream_t st) {
     if (B <= 0) return hipSuccess;
-    hipLaunchKernelGGL((gram_q_kernel<E>), dim3((unsigned)B), dim3(NT), 0, st, L1, n, npad, kc_real, kc, lambda, Qt,
-                       flags);
+    const dim3 grid((unsigned)((npad + NT - 1) / NT), (unsigned)B);
+    switch (kc) {
+    case 16: hipLaunchKernelGGL(cholq_kernel<16>, grid, dim3(NT), 0, st, T, ldt, off, n, npad, kc_real, lambda, Qt, flags); break;
+    case 32: hipLaunchKernelGGL(cholq_kernel<32>, grid, dim3(NT), 0, st, T, ldt, off, n, npad, kc_real, lambda, Qt, flags); break;
+    case 48: hipLaunchKernelGGL(cholq_kernel<48>, grid, dim3(NT), 0, st, T, ldt, off, n, npad, kc_real, lambda, Qt, flags); break;
+    case 64: hipLaunchKernelGGL(cholq_kernel<64>, grid, dim3(NT), 0, st, T, ldt, off, n, npad, kc_real, lambda, Qt, flags); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <>
+hipError_t launch_gram_q<float>(float *T, int64_t ldt, int64_t off, int64_t B, int64_t n, int64_t npad, int kc_real,
+                                int kc, float lambda, float *Qt, int *flags, hipStream_t st) {
+    if (B <= 0) return hipSuccess;
+    if (kc < 1 || kc > 64) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(gram_q_f32_kernel, dim3((unsigned)B), dim3(NT), 0, st, T, ldt, off, n, npad, kc_real, kc,
+                       lambda, Qt, flags);
     return hipGetLastError();
 }
 
@@ -349,10 +432,6 @@ hipError_t launch_mprime(const E *X, const E *Qt, int64_t B, int64_t n, int64_t 
     return hipGetLastError();
 }
 
-template hipError_t launch_gram_q<bf16>(bf16 *, int64_t, int64_t, int64_t, int, int, float, bf16 *, int *,
-                                        hipStream_t);
-template hipError_t launch_gram_q<float>(float *, int64_t, int64_t, int64_t, int, int, float, float *, int *,
-                                         hipStream_t);
 template hipError_t launch_mprime<bf16>(const bf16 *, const bf16 *, int64_t, int64_t, int64_t, int64_t, int, bf16 *,
                                         hipStream_t);
 template hipError_t launch_mprime<float>(const float *, const float *, int64_t, int64_t, int64_t, int64_t, int,
