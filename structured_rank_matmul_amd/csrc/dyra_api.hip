@@ -73,6 +73,7 @@ Path path_for(const dyra_plan *p, int64_t n) {
 //   flags  int32 [B]             per-instance solve failure flags
 //   T      [N][kw + kc]          X A_s next to L1 (then Q) for every token
 //   Qt     [B][kc][npad]         Q_b^T, token-contiguous, npad = n rounded up to 32
+//                                (float32 only; bf16 reads Q_b from T)
 //   Mp     [B * kc][c1]          M'_b = Q_b^T X_b stacked over instances
 //   R1t    [B][c2][kc]           R1_b transposed
 //   dual   decode workspace      (n <= 16 or n < k only)
@@ -95,7 +96,7 @@ Layout workspace_layout(const dyra_plan *p, int64_t B, int64_t n) {
     if (path_for(p, n) == Path::Primal) {
         L.npad = round_up(n, 32);
         L.Qt = off;
-        off += align_up(es * B * p->kc * L.npad);
+        if (p->dtype == DYRA_F32) off += align_up(es * B * p->kc * L.npad);
         L.Mp = off;
         off += align_up(es * B * p->kc * p->c1);
         L.R1t = off;
@@ -158,7 +159,8 @@ dyra_status run_forward(const E *X, int64_t B, int64_t n, const dyra_plan *p, E 
                                                        st))) != DYRA_OK)
                 return s;
             if ((s = mark()) != DYRA_OK) return s;
-            if ((s = hip_status(dyra::launch_mprime<E>(X, Qt, B, n, L.npad, p->c1, p->kc, Mp, st))) != DYRA_OK)
+            if ((s = hip_status(dyra::launch_mprime<E>(X, T, ldt, p->kw, Qt, B, n, L.npad, p->c1, p->kc, Mp, st))) !=
+                DYRA_OK)
                 return s;
             if ((s = mark()) != DYRA_OK) return s;
             if ((s = hip_status(dyra::launch_right<E>(Mp, Wres_t, B * p->kc, p->c1, p->c2, p->kc, R1t, st))) !=

@@ -21,17 +21,18 @@ hipError_t launch_right(const E *Mp, const E *Wres_t, int64_t rows, int64_t c1, 
 
 // With C C^T = L1_b^T L1_b + lambda I: Q_b = L1_b C^-T replaces L1_b in place
 // (columns [off, off + kc) of T's rows b*n .. b*n + n - 1, leading dimension
-// ldt) and Qt[b] = Q_b^T ([kc][npad], token-contiguous, zero for tokens
-// n..npad-1).  flags[b] = 1 if a pivot broke down (then Q_b = 0).
-// kc in {16, 32, 48, 64}.
+// ldt).  float32 also writes Qt[b] = Q_b^T ([kc][npad], token-contiguous, zero
+// for tokens n..npad-1); bf16 leaves Qt untouched.  flags[b] = 1 if a pivot
+// broke down (then Q_b = 0).  kc in {16, 32, 48, 64}.
 template <typename E>
 hipError_t launch_gram_q(E *T, int64_t ldt, int64_t off, int64_t B, int64_t n, int64_t npad, int kc_real, int kc,
                          float lambda, E *Qt, int *flags, hipStream_t st);
 
-// Mp[b*kc + i][:] = (Qt_b X_b)[i][:].
+// Mp[b*kc + i][:] = (Q_b^T X_b)[i][:]: bf16 reads Q_b from T (as left by
+// launch_gram_q), float32 from Qt.
 template <typename E>
-hipError_t launch_mprime(const E *X, const E *Qt, int64_t B, int64_t n, int64_t npad, int64_t c1, int kc, E *Mp,
-                         hipStream_t st);
+hipError_t launch_mprime(const E *X, const E *T, int64_t ldt, int64_t off, const E *Qt, int64_t B, int64_t n,
+                         int64_t npad, int64_t c1, int kc, E *Mp, hipStream_t st);
 
 // Y[Ntok][c2] = T[:, 0:kw] V_s^T + T[:, kw:kw+kc] R1_b for each token's
 // instance b (n tokens per instance; R1t[b] is [c2][kc]); T has leading

@@ -39,17 +39,6 @@ namespace {
 // One K slice is 64 bytes of every operand row.
 template <typename E> constexpr int gemm_bk() { return 64 / (int)sizeof(E); }
 
-// s_waitcnt on the vector-memory counter alone (gfx9 encoding: vmcnt in bits
-// 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
-template <int N> __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier that the compiler may not move memory accesses across and
-// that adds no wait of its own (the waits are explicit).
-__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
-
 // MFMA operand fragment of 16-deep step h from a swizzled LDS slice row
 // (row_base = the row's first byte, sw = (row >> 2) & 3, hf = lane / 32).
 __device__ __forceinline__ bf16x8 slice_frag(const char *row_base, int h, int hf, int sw, const bf16 *) {
@@ -64,9 +53,6 @@ __device__ __forceinline__ f32x8 slice_frag(const char *row_base, int, int hf, i
     return r;
 }
 
-__device__ __forceinline__ void lds_dma16(const void *g, char *lds) {
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
-}
 
 // Four consecutive elements packed for one 8-byte (bf16) / 16-byte (fp32) store.
 template <typename E> struct Pack4;

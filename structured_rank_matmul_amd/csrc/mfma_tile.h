@@ -68,44 +68,22 @@ __device__ __forceinline__ float to_f32(float v) { return v; }
 // Row of the accumulator register t for lane l (see the layout note above).
 __device__ __forceinline__ int acc_row(int lane, int t) { return 8 * (t >> 2) + 4 * (lane >> 5) + (t & 3); }
 
-// Global -> register -> LDS copy of a [ROWS][BK] slice of a row-major matrix
-// (leading dimension ld elements) starting at (row0, k0).  Rows outside
-// [rlo, rhi) and columns at or beyond `kmax` are zero-filled (kmax a multiple
-// of the 16-byte vector).  LDS layout [ROWS][BK + PAD].
-template <typename E, int ROWS, int BK, int NT> struct SliceCopy {
-    static constexpr int VEC = Lay<E>::VEC;
-    static constexpr int CPR = BK / VEC;
-    static constexpr int CHUNKS = ROWS * CPR;
-    static constexpr int PER = (CHUNKS + NT - 1) / NT;
-    static constexpr int STRIDE = BK + Lay<E>::PAD;
-    uint4 reg[PER];
+// Asynchronous 16-byte copy global -> LDS (global_load_lds_dwordx4): lane l
+// writes LDS bytes [lds + 16 l, lds + 16 l + 16); lds must be wave-uniform.
+// Completion is tracked by the vector-memory counter only.
+__device__ __forceinline__ void lds_dma16(const void *g, char *lds) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
 
-    __device__ __forceinline__ void load(const E *g, int64_t ld, int64_t row0, int64_t rlo, int64_t rhi, int64_t k0,
-                                         int tid, int64_t kmax) {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int c = tid + p * NT;
-            const int row = c / CPR;
-            const int col = (c % CPR) * VEC;
-            // branch-free: an out-of-range chunk loads element 0 and is zeroed
-            const int64_t r = row0 + row;
-            const bool ok = (CHUNKS % NT == 0 || c < CHUNKS) && r >= rlo && r < rhi && k0 + col < kmax;
-            const int64_t off = ok ? r * ld + k0 + col : 0;
-            const uint4 v = *reinterpret_cast<const uint4 *>(g + off);
-            reg[p] = ok ? v : make_uint4(0, 0, 0, 0);
-        }
-    }
-    __device__ __forceinline__ void store(E *lds, int tid) const {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int c = tid + p * NT;
-            if (CHUNKS % NT == 0 || c < CHUNKS) {
-                const int row = c / CPR;
-                const int col = (c % CPR) * VEC;
-                *reinterpret_cast<uint4 *>(lds + row * STRIDE + col) = reg[p];
-            }
-        }
-    }
-};
+// s_waitcnt on the vector-memory counter alone (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that the compiler may not move memory accesses across and
+// that adds no wait of its own (the waits are explicit).
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
 }  // namespace dyra

@@ -16,16 +16,20 @@
 // row-major pass output T (leading dimension ldt) and Q_b overwrites it there.
 //
 //   cholq (bf16)  workgroup (token block of 256, instance b): G by MFMA over
-//            all n tokens of b, then every wavefront factors G with one matrix
-//            row per lane and, in the same elimination steps, turns its 64
-//            token rows of L1_b into rows of Q_b: factoring [G; L1_b] leaves
-//            L1_b C^-T in the lower block.  The pivot row's entries reach all
-//            lanes through v_readlane, so the factorisation has no barrier and
-//            no LDS traffic.
+//            all n tokens of b (the block's own tokens are loaded once, into
+//            registers, and serve both G and the elimination), then every
+//            wavefront factors G with one matrix row per lane and, in the same
+//            elimination steps, turns its 64 token rows of L1_b into rows of
+//            Q_b: factoring [G; L1_b] leaves L1_b C^-T in the lower block.  The
+//            pivot row's entries reach all lanes through v_readlane, so the
+//            factorisation has no barrier and no LDS traffic.
 //   gram_q (float32)  one workgroup per instance, all in float64: G, a
 //            right-looking Cholesky and the inverse C^-1 with 16 matrix entries
-//            per thread, then q_t = C^-1 l_t per token.
-//   mprime   workgroup (instance b, 256 input features): M'_b = Q_b^T X_b.
+//            per thread, then q_t = C^-1 l_t per token, written both in place
+//            and transposed (Qt) for the float32 mprime.
+//   mprime (bf16)  workgroup (instance b, 256 input features):
+//            M'_b = Q_b^T X_b with X_b and Q_b read row-major through LDS.
+//   mprime (float32)  the same product from Q_b^T stored token-contiguous.
 #include "dyra_kernels.h"
 
 #include "mfma_tile.h"
@@ -67,15 +71,54 @@ __device__ __forceinline__ float bcast(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// One elimination step of the lane-per-row factorisation (step K, pivot row
+// K held by lane K).  Lane i holds row i of the trailing matrix in g and its
+// token row in l.  The pivot row's entries are broadcast to SGPRs in batches
+// of 8 ahead of the FMAs that use them.
+template <int KC, int K, int M0>
+__device__ __forceinline__ void elim_batch(float (&g)[KC], float (&l)[KC], float a, float bt) {
+    constexpr int CNT = (KC - M0) < 8 ? (KC - M0) : 8;
+    float sv[CNT];
+#pragma unroll
+    for (int u = 0; u < CNT; ++u) sv[u] = bcast(g[M0 + u], K);  // trailing row K = C[m][K] C[K][K]
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < CNT; ++u) {
+        g[M0 + u] = fmaf(-a, sv[u], g[M0 + u]);
+        l[M0 + u] = fmaf(-bt, sv[u], l[M0 + u]);
+    }
+    // the batch's FMAs complete here, so its broadcasts die here (otherwise
+    // the compiler may defer the token-row FMAs and spill the SGPRs)
+#pragma unroll
+    for (int u = 0; u < CNT; ++u) asm volatile("" : "+v"(g[M0 + u]), "+v"(l[M0 + u]));
+    if constexpr (M0 + 8 < KC) elim_batch<KC, K, M0 + 8>(g, l, a, bt);
+}
+
+template <int KC, int K>
+__device__ __forceinline__ void elim_step(float (&g)[KC], float (&l)[KC], int kc_real, float th, bool &fail) {
+    if constexpr (K < KC) {
+        float pk = bcast(g[K], K);
+        const bool bad = K < kc_real && !(pk > th);  // padding pivots are 1
+        fail = fail || bad;
+        pk = bad ? 1.f : pk;
+        const float rp = __builtin_amdgcn_rcpf(pk);
+        const float a = g[K] * rp;   // G rows: C[i][K] / C[K][K]
+        const float bt = l[K] * rp;  // token rows: Q[t][K] / C[K][K]
+        l[K] = l[K] * __builtin_amdgcn_rsqf(pk);
+        if constexpr (K + 1 < KC) elim_batch<KC, K, K + 1>(g, l, a, bt);
+        elim_step<KC, K + 1>(g, l, kc_real, th, fail);
+    }
+}
+
 // ---------------------------------------------------------------- bf16 path
 template <int KC>
 __global__ __launch_bounds__(NT) void cholq_kernel(bf16 *__restrict__ T, int64_t ldt, int64_t off, int64_t n,
-                                                   int64_t npad, int kc_real, float lambda, bf16 *__restrict__ Qt,
-                                                   int *__restrict__ flags) {
+                                                   int kc_real, float lambda, int *__restrict__ flags) {
     constexpr int GS = 68;        // row stride (floats) of G in LDS
-    constexpr int TT = 64;        // tokens per Gram chunk
-    constexpr int ST = TT + 8;    // row stride (bf16) of the transposed chunk
+    constexpr int TT = NT;        // tokens per Gram chunk = tokens per workgroup
+    constexpr int ST = TT + 8;    // row stride (bf16) of the transposed chunk [feature][token]
     constexpr int NBLK = (KC + 31) / 32;
+    constexpr int NV = KC / 8;    // 16-byte vectors per token row
     __shared__ __align__(16) bf16 Lt[64 * ST];
     __shared__ __align__(16) float Gs[64 * GS];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -85,50 +128,60 @@ __global__ __launch_bounds__(NT) void cholq_kernel(bf16 *__restrict__ T, int64_t
     bf16 *const Tb = T + b * n * ldt + off;  // token t of instance b: Tb + t * ldt
     DYRA_PHASE_MARK(0);
 
-    // ---- G = L1_b^T L1_b over all n tokens, 32x32 blocks on MFMA
+    // this thread's token row of L1_b, requested first so that its latency
+    // overlaps the set-up (tokens past n read as zero)
+    const int64_t tbase = (int64_t)blockIdx.x * TT;
+    const int64_t t = tbase + tid;
+    const bool tin = t < n;
+    uint4 lraw[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const uint4 x = *reinterpret_cast<const uint4 *>(Tb + (tin ? t * ldt : 0) + 8 * v);
+        lraw[v] = tin ? x : make_uint4(0, 0, 0, 0);
+    }
+    // features KC .. 32 NBLK - 1 of the transposed chunk are MFMA padding
+    if (KC % 32 != 0) {
+        for (int e = tid; e < (32 * NBLK - KC) * ST; e += NT) Lt[KC * ST + e] = bf16(0.f);
+    }
+
+    // ---- G = L1_b^T L1_b over all n tokens, 32x32 blocks on MFMA; the
+    // workgroup's own chunk comes from lraw, others (n > TT) are loaded
     const int wm = wave >> 1, wn = wave & 1;
     const bool gact = wm < NBLK && wn < NBLK;
     f32x16 acc = f32x16{};
-    uint4 reg[2];
-    // chunk of TT tokens x 64 features: thread c = tid + 256 p loads token
-    // c % 64, features 8 (c / 64) .. +7 (features >= KC and tokens >= n read 0)
-    auto gload = [&](int64_t t0) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int c = tid + p * NT;
-            const int tok = c & 63, j0 = (c >> 6) * 8;
-            const bool ok = t0 + tok < n && j0 < KC;
-            const uint4 v = *reinterpret_cast<const uint4 *>(Tb + (ok ? (t0 + tok) * ldt + j0 : 0));
-            reg[p] = ok ? v : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto gstore = [&]() {
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int c = tid + p * NT;
-            const int tok = c & 63, j0 = (c >> 6) * 8;
-            union { uint4 u; bf16 e[8]; } v;
-            v.u = reg[p];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) Lt[(j0 + q) * ST + tok] = v.e[q];
-        }
-    };
     const int64_t nch = (n + TT - 1) / TT;
-    gload(0);
     for (int64_t ch = 0; ch < nch; ++ch) {
-        __syncthreads();
-        gstore();
-        __syncthreads();
-        if (ch + 1 < nch) gload((ch + 1) * TT);
-        if (gact) {
+        const int64_t c0 = ch * TT;
+        uint4 v[NV];
+        if (c0 == tbase) {
 #pragma unroll
+            for (int q = 0; q < NV; ++q) v[q] = lraw[q];
+        } else {
+            const bool ok = c0 + tid < n;
+#pragma unroll
+            for (int q = 0; q < NV; ++q) {
+                const uint4 x = *reinterpret_cast<const uint4 *>(Tb + (ok ? (c0 + tid) * ldt : 0) + 8 * q);
+                v[q] = ok ? x : make_uint4(0, 0, 0, 0);
+            }
+        }
+        __syncthreads();  // the previous chunk's MFMA reads are done
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            union { uint4 u; bf16 e[8]; } w;
+            w.u = v[q];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Lt[(8 * q + e) * ST + tid] = w.e[e];
+        }
+        __syncthreads();
+        if (gact) {
+#pragma unroll 4
             for (int kk = 0; kk < TT; kk += 16)
                 acc = mma16(acc, ld_frag(Lt + (wm * 32 + lr) * ST + kk + lk), ld_frag(Lt + (wn * 32 + lr) * ST + kk + lk));
         }
     }
     if (gact) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) Gs[(wm * 32 + acc_row(lane, t)) * GS + wn * 32 + lr] = acc[t];
+        for (int q = 0; q < 16; ++q) Gs[(wm * 32 + acc_row(lane, q)) * GS + wn * 32 + lr] = acc[q];
     }
     __syncthreads();
     DYRA_PHASE_MARK(1);
@@ -138,8 +191,8 @@ __global__ __launch_bounds__(NT) void cholq_kernel(bf16 *__restrict__ T, int64_t
     float g[KC];
 #pragma unroll
     for (int m = 0; m < KC; m += 4) {
-        const float4 v = *reinterpret_cast<const float4 *>(&Gs[(i < KC ? i : 0) * GS + m]);
-        g[m] = v.x; g[m + 1] = v.y; g[m + 2] = v.z; g[m + 3] = v.w;
+        const float4 x = *reinterpret_cast<const float4 *>(&Gs[(i < KC ? i : 0) * GS + m]);
+        g[m] = x.x; g[m + 1] = x.y; g[m + 2] = x.z; g[m + 3] = x.w;
     }
     const float diag = i < kc_real ? Gs[i * GS + i] : 0.f;
 #pragma unroll
@@ -154,54 +207,29 @@ __global__ __launch_bounds__(NT) void cholq_kernel(bf16 *__restrict__ T, int64_t
     for (int o = 32; o > 0; o >>= 1) dmax = fmaxf(dmax, __shfl_xor(dmax, o));
     const float th = lambda > 0.f ? 0.f : (float)KC * 1.2e-7f * dmax;
     bool fail = !(dmax > 0.f);
-
-    // ---- this wavefront's 64 token rows of L1_b
-    const int64_t t = (int64_t)blockIdx.x * NT + wave * 64 + lane;
-    const bool tin = t < n;
     float l[KC];
 #pragma unroll
-    for (int m = 0; m < KC; m += 8) {
-        union { uint4 u; bf16 e[8]; } v;
-        v.u = *reinterpret_cast<const uint4 *>(Tb + (tin ? t * ldt : 0) + m);
+    for (int q = 0; q < NV; ++q) {
+        union { uint4 u; bf16 e[8]; } w;
+        w.u = lraw[q];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) l[m + q] = tin ? (float)v.e[q] : 0.f;
+        for (int e = 0; e < 8; ++e) l[8 * q + e] = (float)w.e[e];
     }
     DYRA_PHASE_MARK(2);
 
     // ---- elimination: step k takes pivot row k (lane k) to all lanes
-#pragma unroll
-    for (int k = 0; k < KC; ++k) {
-        float pk = bcast(g[k], k);
-        const bool bad = k < kc_real && !(pk > th);  // padding pivots are 1
-        fail = fail || bad;
-        pk = bad ? 1.f : pk;
-        const float rp = 1.f / pk;
-        const float a = g[k] * rp;      // G rows: C[i][k] / C[k][k]
-        const float bt = l[k] * rp;     // token rows: Q[t][k] / C[k][k]
-        l[k] = l[k] * (1.f / sqrtf(pk));
-#pragma unroll
-        for (int m = k + 1; m < KC; ++m) {
-            const float s = bcast(g[m], k);   // trailing row k = C[m][k] C[k][k]
-            g[m] = fmaf(-a, s, g[m]);
-            l[m] = fmaf(-bt, s, l[m]);
-        }
-    }
+    elim_step<KC, 0>(g, l, kc_real, th, fail);
     DYRA_PHASE_MARK(3);
 
-    // ---- Q_b rows in place of L1_b, and Qt[b] = Q_b^T (token-contiguous, zero past n)
+    // ---- Q_b rows in place of L1_b
     if (tin) {
 #pragma unroll
         for (int m = 0; m < KC; m += 8) {
-            union { uint4 u; bf16 e[8]; } v;
+            union { uint4 u; bf16 e[8]; } w;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v.e[q] = fail ? bf16(0.f) : (bf16)l[m + q];
-            *reinterpret_cast<uint4 *>(Tb + t * ldt + m) = v.u;
+            for (int q = 0; q < 8; ++q) w.e[q] = fail ? bf16(0.f) : (bf16)l[m + q];
+            *reinterpret_cast<uint4 *>(Tb + t * ldt + m) = w.u;
         }
-    }
-    if (t < npad) {
-        bf16 *qb = Qt + b * KC * npad + t;
-#pragma unroll
-        for (int m = 0; m < KC; ++m) qb[(int64_t)m * npad] = fail ? bf16(0.f) : (bf16)l[m];
     }
     if (blockIdx.x == 0 && tid == 0) flags[b] = fail ? 1 : 0;
     DYRA_PHASE_MARK(4);
@@ -396,18 +424,163 @@ __global__ __launch_bounds__(NT) void mprime_kernel(const E *__restrict__ X, con
     }
 }
 
+// ------------------------------------------------- M'_b = Q_b^T X_b, bf16
+// Workgroup (256 input features, instance b); token slices of 32 rows of X_b
+// and of Q_b go straight into LDS (row-major, as stored), NS in flight, and
+// the token-contiguous MFMA fragments come out of LDS through transposing
+// reads (ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives
+// element i % 4 of the 8-byte rows addressed by lanes i / 4 + 4 q, q = 0..3,
+// so 16 lanes addressing a 4-token x 16-feature block receive one feature
+// each, four tokens deep).  LDS chunk swizzles keep those reads on distinct
+// banks: X rows (512 bytes) hold chunk c at c ^ 4 (r % 4), Q rows (128 bytes)
+// at c ^ 4 ((r / 2) % 2).
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint2 lds_tr16(const char *p) {
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)(__attribute__((address_space(3))) char *)p);
+    union { v4i16 s; uint2 u; } w;
+    w.s = v;
+    return w.u;
+}
+
+template <int KC>
+__global__ __launch_bounds__(NT) void mprime_tr_kernel(const bf16 *__restrict__ X, const bf16 *__restrict__ T,
+                                                       int64_t ldt, int64_t off, int64_t n, int64_t c1,
+                                                       bf16 *__restrict__ Mp) {
+    constexpr int CW = 256;                 // features per workgroup
+    constexpr int TS = 32;                  // tokens per slice
+    constexpr int NS = 4;                   // slices in flight
+    constexpr int XBYTES = TS * CW * 2;     // 16 KB
+    constexpr int QROW = 128;               // bytes per Q row in LDS (64 columns)
+    constexpr int QBYTES = TS * QROW;       // 4 KB
+    constexpr int STAGE = XBYTES + QBYTES;
+    constexpr int NKB = (KC + 31) / 32;     // 32-row blocks of M'_b
+    constexpr int IPW = (XBYTES + QBYTES) / 1024 / 4;  // load blocks per wave per slice (5)
+    extern __shared__ __align__(16) char smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t b = blockIdx.y;
+    const int64_t f0 = (int64_t)blockIdx.x * CW;
+    const bf16 *Xb = X + b * n * c1;
+    const bf16 *Qb = T + b * n * ldt + off;
+    const int64_t S = (n + TS - 1) / TS;
+
+    // load pattern: X block j (rows 2j, 2j+1), lane l -> row 2j + l/32,
+    // position l%32; Q block j (rows 8j..8j+7), lane l -> row 8j + l/8, position l%8
+    auto issue = [&](int64_t s) {
+        char *dst = smem + (int)(s % NS) * STAGE;
+        const int64_t t0 = s * TS;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int j = wave + 4 * q;  // X blocks 0..15
+            const int row = 2 * j + (lane >> 5);
+            const int c = (lane & 31) ^ (4 * (row & 3));
+            int64_t t = t0 + row;
+            t = t < n ? t : n - 1;
+            int64_t f = f0 + 8 * c;
+            f = f < c1 ? f : 0;  // past c1: any in-range address, never stored
+            lds_dma16(Xb + t * c1 + f, dst + j * 1024);
+        }
+        {
+            const int j = wave;  // Q blocks 0..3
+            const int row = 8 * j + (lane >> 3);
+            const int c = (lane & 7) ^ (4 * ((row >> 1) & 1));
+            int64_t t = t0 + row;
+            t = t < n ? t : n - 1;
+            lds_dma16(Qb + t * ldt + (8 * c < KC ? 8 * c : 0), dst + XBYTES + j * 1024);
+        }
+    };
+
+    // per-lane transposing-read offsets: 16-lane group g = lane / 16 covers
+    // tokens 8 (g / 2) + 4 u + (lane % 16) / 4 and columns 16 (g % 2) + 4 (lane % 4) + 0..3
+    const int g = lane >> 4, rq = (lane & 15) >> 2, cq = 4 * (lane & 3);
+    const int hcol = 16 * (g & 1) + cq;  // column inside a 32-column block
+    auto xoff = [&](int row, int col) { return row * (CW * 2) + (((col >> 3) ^ (4 * (row & 3))) << 4) + (col & 7) * 2; };
+    auto qoff = [&](int row, int col) { return row * QROW + (((col >> 3) ^ (4 * ((row >> 1) & 1))) << 4) + (col & 7) * 2; };
+
+    f32x16 acc[2][NKB];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int ib = 0; ib < NKB; ++ib) acc[jb][ib] = f32x16{};
+
+    for (int64_t p = 0; p < NS - 1 && p < S; ++p) issue(p);
+    for (int64_t s = 0; s < S; ++s) {
+        const int64_t later = (S - 1 - s) < (NS - 2) ? (S - 1 - s) : (NS - 2);
+        if (later >= 2) wait_vmcnt<2 * IPW>();
+        else if (later == 1) wait_vmcnt<IPW>();
+        else wait_vmcnt<0>();
+        barrier_only();
+        if (s + NS - 1 < S) issue(s + NS - 1);
+        const char *sx = smem + (int)(s % NS) * STAGE;
+        const char *sq = sx + XBYTES;
+        const int64_t t0 = s * TS;
+        const bool tail = t0 + TS > n;
+#pragma unroll
+        for (int h = 0; h < TS / 16; ++h) {
+            bf16x8 fx[2], fq[NKB];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int row = 16 * h + 8 * (g >> 1) + 4 * u + rq;
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb) {
+                    const uint2 v = lds_tr16(sx + xoff(row, 64 * wave + 32 * jb + hcol));
+                    reinterpret_cast<uint2 *>(&fx[jb])[u] = v;
+                }
+#pragma unroll
+                for (int ib = 0; ib < NKB; ++ib) {
+                    const uint2 v = lds_tr16(sq + qoff(row, 32 * ib + hcol));
+                    reinterpret_cast<uint2 *>(&fq[ib])[u] = v;
+                }
+            }
+            // Q columns past KC and tokens past n contribute nothing
+#pragma unroll
+            for (int ib = 0; ib < NKB; ++ib) {
+                if (KC % 32 != 0 && 32 * ib + (lane & 31) >= KC) fq[ib] = bf16x8{};
+                if (tail) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (t0 + 16 * h + 8 * (lane >> 5) + e >= n) fq[ib][e] = bf16(0.f);
+                }
+            }
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+                for (int ib = 0; ib < NKB; ++ib) acc[jb][ib] = mma16(acc[jb][ib], fx[jb], fq[ib]);
+        }
+    }
+    // lane holds row kk = 32 ib + lane % 32 of M'_b and four consecutive features
+#pragma unroll
+    for (int ib = 0; ib < NKB; ++ib) {
+        const int kk = 32 * ib + (lane & 31);
+        if (kk >= KC) continue;
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t f = f0 + 64 * wave + 32 * jb + acc_row(lane, 4 * q);
+                if (f >= c1) continue;
+                union { uint2 u; bf16 e[4]; } w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w.e[e] = (bf16)acc[jb][ib][4 * q + e];
+                *reinterpret_cast<uint2 *>(Mp + (b * KC + kk) * c1 + f) = w.u;
+            }
+    }
+}
+
 }  // namespace
 
 template <>
 hipError_t launch_gram_q<bf16>(bf16 *T, int64_t ldt, int64_t off, int64_t B, int64_t n, int64_t npad, int kc_real,
-                               int kc, float lambda, bf16 *Qt, int *flags, hipStream_t st) {
+                               int kc, float lambda, bf16 *, int *flags, hipStream_t st) {
     if (B <= 0) return hipSuccess;
     const dim3 grid((unsigned)((npad + NT - 1) / NT), (unsigned)B);
     switch (kc) {
-    case 16: hipLaunchKernelGGL(cholq_kernel<16>, grid, dim3(NT), 0, st, T, ldt, off, n, npad, kc_real, lambda, Qt, flags); break;
-    case 32: hipLaunchKernelGGL(cholq_kernel<32>, grid, dim3(NT), 0, st, T, ldt, off, n, npad, kc_real, lambda, Qt, flags); break;
-    case 48: hipLaunchKernelGGL(cholq_kernel<48>, grid, dim3(NT), 0, st, T, ldt, off, n, npad, kc_real, lambda, Qt, flags); break;
-    case 64: hipLaunchKernelGGL(cholq_kernel<64>, grid, dim3(NT), 0, st, T, ldt, off, n, npad, kc_real, lambda, Qt, flags); break;
+    case 16: hipLaunchKernelGGL(cholq_kernel<16>, grid, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda, flags); break;
+    case 32: hipLaunchKernelGGL(cholq_kernel<32>, grid, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda, flags); break;
+    case 48: hipLaunchKernelGGL(cholq_kernel<48>, grid, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda, flags); break;
+    case 64: hipLaunchKernelGGL(cholq_kernel<64>, grid, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda, flags); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -423,18 +596,42 @@ hipError_t launch_gram_q<float>(float *T, int64_t ldt, int64_t off, int64_t B, i
     return hipGetLastError();
 }
 
-template <typename E>
-hipError_t launch_mprime(const E *X, const E *Qt, int64_t B, int64_t n, int64_t npad, int64_t c1, int kc, E *Mp,
-                         hipStream_t st) {
+template <>
+hipError_t launch_mprime<bf16>(const bf16 *X, const bf16 *T, int64_t ldt, int64_t off, const bf16 *, int64_t B,
+                               int64_t n, int64_t, int64_t c1, int kc, bf16 *Mp, hipStream_t st) {
     if (B <= 0) return hipSuccess;
-    hipLaunchKernelGGL((mprime_kernel<E>), dim3((unsigned)((c1 + 255) / 256), (unsigned)B), dim3(NT), 0, st, X, Qt,
-                       n, npad, c1, kc, Mp);
+    constexpr size_t smem = 4 * (32 * 256 * 2 + 32 * 128);
+    const dim3 grid((unsigned)((c1 + 255) / 256), (unsigned)B);
+#define DYRA_MP(KC)                                                                                               \
+    {                                                                                                             \
+        static bool attr = false;                                                                                 \
+        if (!attr) {                                                                                              \
+            hipError_t e = hipFuncSetAttribute((const void *)mprime_tr_kernel<KC>,                                \
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);            \
+            if (e != hipSuccess) return e;                                                                        \
+            attr = true;                                                                                          \
+        }                                                                                                         \
+        hipLaunchKernelGGL(mprime_tr_kernel<KC>, grid, dim3(NT), smem, st, X, T, ldt, off, n, c1, Mp);            \
+        break;                                                                                                    \
+    }
+    switch (kc) {
+    case 16: DYRA_MP(16)
+    case 32: DYRA_MP(32)
+    case 48: DYRA_MP(48)
+    case 64: DYRA_MP(64)
+    default: return hipErrorInvalidValue;
+    }
+#undef DYRA_MP
     return hipGetLastError();
 }
 
-template hipError_t launch_mprime<bf16>(const bf16 *, const bf16 *, int64_t, int64_t, int64_t, int64_t, int, bf16 *,
-                                        hipStream_t);
-template hipError_t launch_mprime<float>(const float *, const float *, int64_t, int64_t, int64_t, int64_t, int,
-                                         float *, hipStream_t);
+template <>
+hipError_t launch_mprime<float>(const float *X, const float *, int64_t, int64_t, const float *Qt, int64_t B,
+                                int64_t n, int64_t npad, int64_t c1, int kc, float *Mp, hipStream_t st) {
+    if (B <= 0) return hipSuccess;
+    hipLaunchKernelGGL((mprime_kernel<float>), dim3((unsigned)((c1 + 255) / 256), (unsigned)B), dim3(NT), 0, st, X,
+                       Qt, n, npad, c1, kc, Mp);
+    return hipGetLastError();
+}
 
 }  // namespace dyra
