@@ -43,23 +43,55 @@ def stage_flops(spec, B, n):
     }
 
 
+def stage_bytes(spec, B, n, es):
+    """Algorithmic HBM bytes of each kernel of the primal path for one layer call
+    (every operand read once, every result written once; es = element size)."""
+    N = B * n
+    c1, c2, r, k = spec.c1, spec.c2, spec.r, spec.k
+    return {
+        "left": es * (N * c1 + (r + k) * c1 + N * (r + k)),
+        "gram_q": es * (2 * N * k),
+        "mprime": es * (N * c1 + N * k + B * k * c1),
+        "right": es * (B * k * c1 + c1 * c2 + B * k * c2),
+        "output": es * (N * (r + k) + c2 * r + B * k * c2 + N * c2),
+    }
+
+
+# kernel behind each stage of the primal path (for the roofline record)
+STAGE_KERNEL = {
+    "left": "gemm_kernel (T = X [A_s | P_L])",
+    "gram_q": "cholq_kernel",
+    "mprime": "mprime_tr_kernel",
+    "right": "gemm_kernel (R1 = M' W_res, R1t store)",
+    "output": "gemm_kernel with correction slices (Y = T_s V_s^T + Q R1_b)",
+}
+TRAFFIC_FILE = {"output": "profiles/output_gemm_{workload}_traffic.txt"}
+
+
 def dyra_flops(spec, B, n):
     return sum(stage_flops(spec, B, n).values())
 
 
-def time_loop(fn, steps, warmup, stream):
+def time_loop(fn, steps, warmup, stream, per_step=False):
+    """Mean seconds per step over `steps` timed steps (events on `stream`);
+    with per_step, also the list of single-step durations."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if per_step else 2)]
+    evs[0].record(stream)
+    for i in range(steps):
         fn()
-    end.record(stream)
+        if per_step:
+            evs[i + 1].record(stream)
+    if not per_step:
+        evs[1].record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / 1e3 / steps
+    total = evs[0].elapsed_time(evs[-1]) / 1e3
+    if not per_step:
+        return total / steps
+    return total / steps, [evs[i].elapsed_time(evs[i + 1]) / 1e3 for i in range(steps)]
 
 
 def cpu_baseline(workload, plans_orc, X_host, budget_s):
@@ -97,6 +129,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run three forward steps and a calibration copy only (for rocprofv3 --pmc runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the DyRA layer path here is a "
@@ -152,7 +186,21 @@ def main():
         for L in layers:
             dyra.dyra_dense_ref(L["xd"], L["Wt"], L["yd"], stream)
 
-    t_dyra = time_loop(dyra_step, args.steps, args.warmup, stream)
+    if args.traffic_probe:
+        # three forwards, then a plain copy of known size that calibrates the
+        # FETCH_SIZE / WRITE_SIZE counters (torch.neg: reads and writes COPY bytes)
+        for _ in range(3):
+            dyra_step()
+        copy_bytes = 1 << 30
+        src = torch.ones(copy_bytes // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe": True, "copy_bytes": copy_bytes, "workload": w.name}))
+        return
+
+    t_dyra, step_times = time_loop(dyra_step, args.steps, args.warmup, stream, per_step=True)
     t_dense_nn = time_loop(dense_linear, args.steps, args.warmup, stream)
     t_dense_nt = time_loop(dense_nt, args.steps, args.warmup, stream)
     t_dense = min(t_dense_nn, t_dense_nt)
@@ -182,14 +230,32 @@ def main():
             stage_fl[nm] = stage_fl.get(nm, 0.0) + fl.get(nm, 0.0)
         L["stages"] = per
         log(f"{L['spec'].name}: " + "  ".join(f"{k} {v * 1e6:.1f}us" for k, v in per.items()))
+    # ---- roofline of the dominant kernel: algorithmic FLOPs and bytes per
+    # launch against MFMA and HBM peaks; the larger ideal time is the bound
     dom = max(stage_time, key=stage_time.get)
-    peak = PEAK_BF16 if w.dtype == "bf16" else PEAK_FP32
+    es = 2 if w.dtype == "bf16" else 4
     launches = len(layers)
-    achieved = stage_fl[dom] / stage_time[dom] / 1e12
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak / 1e12, "unit": "TFLOP/s",
-                "frac": round(achieved * 1e12 / peak, 4), "traffic": None,
-                "kernel": f"{dom}_kernel", "launches_per_step": launches,
-                "avg_launch_us": round(stage_time[dom] / launches * 1e6, 2)}
+    dom_fl = sum(stage_flops(L["spec"], B, n)[dom] for L in layers)
+    dom_by = sum(stage_bytes(L["spec"], B, n, es)[dom] for L in layers)
+    peak = PEAK_BF16 if w.dtype == "bf16" else PEAK_FP32
+    t_dom = stage_time[dom]
+    if dom_by / PEAK_HBM > dom_fl / peak:
+        bound, achieved, pk, unit = "hbm", dom_by / t_dom / 1e9, PEAK_HBM / 1e9, "GB/s"
+    else:
+        bound, achieved, pk, unit = "mfma", dom_fl / t_dom / 1e12, peak / 1e12, "TFLOP/s"
+    traffic = None
+    if dom in TRAFFIC_FILE:
+        from structured_rank_matmul_amd import profiling
+        traffic = profiling.read_traffic(os.path.join(ROOT, TRAFFIC_FILE[dom].format(workload=w.name)))
+    roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": pk, "unit": unit,
+                "frac": round(achieved / pk, 4),
+                "traffic": None if traffic is None else round(traffic, 0),
+                "kernel": STAGE_KERNEL.get(dom, dom), "stage": dom, "launches_per_step": launches,
+                "avg_launch_us": round(t_dom / launches * 1e6, 2),
+                "algorithmic_bytes_per_launch": round(dom_by / launches, 0),
+                "algorithmic_flops_per_launch": round(dom_fl / launches, 0),
+                "mfma_frac": round(dom_fl / t_dom / peak, 4),
+                "hbm_frac": round(dom_by / t_dom / PEAK_HBM, 4)}
 
     # ---- parity on sampled instances
     parity = {}
@@ -233,6 +299,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(t_dyra * 1e3, 4),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(step_times, q)) * 1e3, 4) for q in (10, 50, 90)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -105,9 +105,11 @@ dyra_status dyra_plan_info(const dyra_plan *plan, int64_t *c1, int64_t *c2, int3
 
 /*
  * Device workspace that dyra_forward needs for B instances of n tokens.
- * Returns 0 for a NULL plan.  The workspace holds the per-instance factors
- * L1, (L1^T L1 + lambda I)^-1, the solved left product and R1, plus a small
- * status header.
+ * Returns 0 for a NULL plan, B < 0 or n < 1.  The workspace holds one int32
+ * failure flag per instance, the left pass output [X A_s | L1] (L1 later
+ * replaced by Q = L1 C^-T, C C^T = L1^T L1 + lambda I), M' = Q^T X and R1 per
+ * instance (for float32 also Q^T), or the dual form's buffers when n <= 16 or
+ * n < k.
  */
 size_t dyra_workspace_bytes(const dyra_plan *plan, int64_t B, int64_t n);
 
@@ -123,21 +125,24 @@ size_t dyra_workspace_bytes(const dyra_plan *plan, int64_t B, int64_t n);
  * All pointers 16-byte aligned.  B >= 0, n >= 1 (B = 0 is a no-op).
  *
  * Asynchronous: enqueues kernels on `stream` and returns; no allocation, no
- * host synchronisation.  For n >= k the per-instance right factor is solved
- * with a Cholesky factorisation of L1^T L1 + lambda I (§2.4); for n < k the
- * same product L1 R1 is formed in its n x n dual (push-through) form
- * L1 L1^T (L1 L1^T + lambda I_n)^-1 X W_res, which is also defined at
- * lambda = 0.  A Cholesky pivot <= 0 (lambda = 0 with rank-deficient L1)
- * increments a counter that dyra_forward_status() reads back; that instance's
- * rows are then undefined.
+ * host synchronisation.  For n > 16 and n >= k the per-instance right factor
+ * comes from a Cholesky factorisation of L1^T L1 + lambda I (§2.4); for
+ * n <= 16 or n < k the same product L1 R1 is formed in its n x n dual
+ * (push-through) form L1 L1^T (L1 L1^T + lambda I_n)^-1 X W_res, which is also
+ * defined at lambda = 0 and better conditioned when n is close to k.  A
+ * Cholesky pivot at or below the working precision (lambda = 0 with a
+ * numerically rank-deficient L1) sets that instance's failure flag, read back
+ * by dyra_forward_status(); its rows then hold the static product X A_s V_s^T
+ * alone.  Every call rewrites every flag.
  */
 dyra_status dyra_forward(const void *X, int64_t B, int64_t n, const dyra_plan *plan, void *Y,
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Number of instances whose SPD solve broke down (pivot <= 0) in the last
- * dyra_forward(X, B, n, plan, ...) that used this workspace.  Copies B flags
- * from the workspace after synchronising `stream`; *failures receives the count.
+ * Number of instances whose SPD solve broke down in the last
+ * dyra_forward(X, B, n, plan, ...) that used this workspace.  Copies the B
+ * flags from the workspace on `stream` and synchronises it; *failures
+ * receives the count.
  */
 dyra_status dyra_forward_status(const dyra_plan *plan, int64_t B, int64_t n, const void *workspace,
                                 void *stream, int32_t *failures);
