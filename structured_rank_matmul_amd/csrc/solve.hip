@@ -28,7 +28,7 @@
 //            per thread, then q_t = C^-1 l_t per token, written both in place
 //            and transposed (Qt) for the float32 mprime.
 //   mprime (bf16)  workgroup (instance b, 256 input features):
-//            M'_b = Q_b^T X_b with X_b and Q_b read row-major through LDS.
+//            M'_b = Q_b^T X_b with X_b and Q_b staged row-major through LDS.
 //   mprime (float32)  the same product from Q_b^T stored token-contiguous.
 #include "dyra_kernels.h"
 
@@ -426,15 +426,22 @@ __global__ __launch_bounds__(NT) void mprime_kernel(const E *__restrict__ X, con
 
 // ------------------------------------------------- M'_b = Q_b^T X_b, bf16
 // Workgroup (256 input features, instance b); token slices of 32 rows of X_b
-// and of Q_b go straight into LDS (row-major, as stored), NS in flight, and
-// the token-contiguous MFMA fragments come out of LDS through transposing
-// reads (ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives
-// element i % 4 of the 8-byte rows addressed by lanes i / 4 + 4 q, q = 0..3,
-// so 16 lanes addressing a 4-token x 16-feature block receive one feature
-// each, four tokens deep).  LDS chunk swizzles keep those reads on distinct
-// banks: X rows (512 bytes) hold chunk c at c ^ 4 (r % 4), Q rows (128 bytes)
-// at c ^ 4 ((r / 2) % 2).
+// and of Q_b are loaded into registers one slice ahead, written to a double
+// buffered LDS stage row-major (as stored), and the token-contiguous MFMA
+// fragments come out of LDS through transposing reads (ds_read_b64_tr_b16: in
+// each group of 16 lanes, lane i receives element i % 4 of the 8-byte rows
+// addressed by lanes i / 4 + 4 q, q = 0..3, so 16 lanes addressing a 4-token x
+// 16-feature block receive one feature each, four tokens deep).  LDS chunk
+// swizzles keep those reads on distinct banks: X rows (512 bytes) hold chunk c
+// at c ^ 4 (r % 4), Q rows (128 bytes) at c ^ 4 ((r / 2) % 2).  The finished
+// 64 x 256 block of M'_b goes back through LDS so that it leaves as whole
+// 512-byte row segments.
+//
+// Register staging keeps more bytes in flight per compute unit than the
+// direct-to-LDS loads of the GEMMs: this kernel streams X_b once from HBM
+// and is bound by that read, not by the MFMA work.
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // (a struct type here would stay in scratch)
 
 __device__ __forceinline__ uint2 lds_tr16(const char *p) {
     const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -450,14 +457,16 @@ __global__ __launch_bounds__(NT) void mprime_tr_kernel(const bf16 *__restrict__ 
                                                        bf16 *__restrict__ Mp) {
     constexpr int CW = 256;                 // features per workgroup
     constexpr int TS = 32;                  // tokens per slice
-    constexpr int NS = 4;                   // slices in flight
-    constexpr int XBYTES = TS * CW * 2;     // 16 KB
+    constexpr int RB = CW * 2;              // bytes per X row in LDS
+    constexpr int XBYTES = TS * RB;         // 16 KB
     constexpr int QROW = 128;               // bytes per Q row in LDS (64 columns)
-    constexpr int QBYTES = TS * QROW;       // 4 KB
-    constexpr int STAGE = XBYTES + QBYTES;
+    constexpr int STAGE = XBYTES + TS * QROW;
+    constexpr int LX = XBYTES / 16 / NT;    // 16-byte X loads per thread and slice (4)
+    constexpr int CPX = RB / 16;            // 16-byte chunks per X row
     constexpr int NKB = (KC + 31) / 32;     // 32-row blocks of M'_b
-    constexpr int IPW = (XBYTES + QBYTES) / 1024 / 4;  // load blocks per wave per slice (5)
-    extern __shared__ __align__(16) char smem[];
+    constexpr int MS = CW + 8;              // row stride (elements) of the staged M'_b block
+    static_assert(TS * QROW == 16 * NT && KC * MS * 2 <= 2 * STAGE, "layout");
+    __shared__ __align__(16) char smem[2 * STAGE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t b = blockIdx.y;
@@ -466,37 +475,39 @@ __global__ __launch_bounds__(NT) void mprime_tr_kernel(const bf16 *__restrict__ 
     const bf16 *Qb = T + b * n * ldt + off;
     const int64_t S = (n + TS - 1) / TS;
 
-    // load pattern: X block j (rows 2j, 2j+1), lane l -> row 2j + l/32,
-    // position l%32; Q block j (rows 8j..8j+7), lane l -> row 8j + l/8, position l%8
-    auto issue = [&](int64_t s) {
-        char *dst = smem + (int)(s % NS) * STAGE;
+    // thread tid loads X chunks q * 256 + tid (row-major over the slice) and
+    // Q chunk tid; rows past n repeat row n - 1 (masked in the product),
+    // features past c1 read feature 0 (never stored)
+    u32x4 reg[LX + 1];
+    auto load = [&](int64_t s) __attribute__((always_inline)) {
         const int64_t t0 = s * TS;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int j = wave + 4 * q;  // X blocks 0..15
-            const int row = 2 * j + (lane >> 5);
-            const int c = (lane & 31) ^ (4 * (row & 3));
-            int64_t t = t0 + row;
-            t = t < n ? t : n - 1;
-            int64_t f = f0 + 8 * c;
-            f = f < c1 ? f : 0;  // past c1: any in-range address, never stored
-            lds_dma16(Xb + t * c1 + f, dst + j * 1024);
+        for (int q = 0; q < LX; ++q) {
+            const int e = q * NT + tid, row = e / CPX, c = e % CPX;
+            const int64_t t = t0 + row < n ? t0 + row : n - 1;
+            const int64_t f = f0 + 8 * c < c1 ? f0 + 8 * c : 0;
+            reg[q] = *reinterpret_cast<const u32x4 *>(Xb + t * c1 + f);
         }
-        {
-            const int j = wave;  // Q blocks 0..3
-            const int row = 8 * j + (lane >> 3);
-            const int c = (lane & 7) ^ (4 * ((row >> 1) & 1));
-            int64_t t = t0 + row;
-            t = t < n ? t : n - 1;
-            lds_dma16(Qb + t * ldt + (8 * c < KC ? 8 * c : 0), dst + XBYTES + j * 1024);
+        const int row = tid >> 3, c = tid & 7;
+        const int64_t t = t0 + row < n ? t0 + row : n - 1;
+        reg[LX] = *reinterpret_cast<const u32x4 *>(Qb + t * ldt + (8 * c < KC ? 8 * c : 0));
+    };
+    auto stage = [&](int slot) __attribute__((always_inline)) {
+        char *dst = smem + slot * STAGE;
+#pragma unroll
+        for (int q = 0; q < LX; ++q) {
+            const int e = q * NT + tid, row = e / CPX, c = e % CPX;
+            *reinterpret_cast<u32x4 *>(dst + row * RB + ((c ^ (4 * (row & 3))) << 4)) = reg[q];
         }
+        const int row = tid >> 3, c = tid & 7;
+        *reinterpret_cast<u32x4 *>(dst + XBYTES + row * QROW + ((c ^ (4 * ((row >> 1) & 1))) << 4)) = reg[LX];
     };
 
     // per-lane transposing-read offsets: 16-lane group g = lane / 16 covers
     // tokens 8 (g / 2) + 4 u + (lane % 16) / 4 and columns 16 (g % 2) + 4 (lane % 4) + 0..3
     const int g = lane >> 4, rq = (lane & 15) >> 2, cq = 4 * (lane & 3);
     const int hcol = 16 * (g & 1) + cq;  // column inside a 32-column block
-    auto xoff = [&](int row, int col) { return row * (CW * 2) + (((col >> 3) ^ (4 * (row & 3))) << 4) + (col & 7) * 2; };
+    auto xoff = [&](int row, int col) { return row * RB + (((col >> 3) ^ (4 * (row & 3))) << 4) + (col & 7) * 2; };
     auto qoff = [&](int row, int col) { return row * QROW + (((col >> 3) ^ (4 * ((row >> 1) & 1))) << 4) + (col & 7) * 2; };
 
     f32x16 acc[2][NKB];
@@ -505,15 +516,15 @@ __global__ __launch_bounds__(NT) void mprime_tr_kernel(const bf16 *__restrict__ 
 #pragma unroll
         for (int ib = 0; ib < NKB; ++ib) acc[jb][ib] = f32x16{};
 
-    for (int64_t p = 0; p < NS - 1 && p < S; ++p) issue(p);
+    // slice s: stage it (waits for its loads), barrier, request slice s + 1,
+    // multiply.  The stage written at slice s + 2 was last read at slice s,
+    // before the barrier of slice s + 1.
+    load(0);
     for (int64_t s = 0; s < S; ++s) {
-        const int64_t later = (S - 1 - s) < (NS - 2) ? (S - 1 - s) : (NS - 2);
-        if (later >= 2) wait_vmcnt<2 * IPW>();
-        else if (later == 1) wait_vmcnt<IPW>();
-        else wait_vmcnt<0>();
-        barrier_only();
-        if (s + NS - 1 < S) issue(s + NS - 1);
-        const char *sx = smem + (int)(s % NS) * STAGE;
+        stage((int)(s & 1));
+        __syncthreads();
+        if (s + 1 < S) load(s + 1);
+        const char *sx = smem + (int)(s & 1) * STAGE;
         const char *sq = sx + XBYTES;
         const int64_t t0 = s * TS;
         const bool tail = t0 + TS > n;
@@ -524,15 +535,11 @@ __global__ __launch_bounds__(NT) void mprime_tr_kernel(const bf16 *__restrict__ 
             for (int u = 0; u < 2; ++u) {
                 const int row = 16 * h + 8 * (g >> 1) + 4 * u + rq;
 #pragma unroll
-                for (int jb = 0; jb < 2; ++jb) {
-                    const uint2 v = lds_tr16(sx + xoff(row, 64 * wave + 32 * jb + hcol));
-                    reinterpret_cast<uint2 *>(&fx[jb])[u] = v;
-                }
+                for (int jb = 0; jb < 2; ++jb)
+                    reinterpret_cast<uint2 *>(&fx[jb])[u] = lds_tr16(sx + xoff(row, 64 * wave + 32 * jb + hcol));
 #pragma unroll
-                for (int ib = 0; ib < NKB; ++ib) {
-                    const uint2 v = lds_tr16(sq + qoff(row, 32 * ib + hcol));
-                    reinterpret_cast<uint2 *>(&fq[ib])[u] = v;
-                }
+                for (int ib = 0; ib < NKB; ++ib)
+                    reinterpret_cast<uint2 *>(&fq[ib])[u] = lds_tr16(sq + qoff(row, 32 * ib + hcol));
             }
             // Q columns past KC and tokens past n contribute nothing
 #pragma unroll
@@ -550,7 +557,11 @@ __global__ __launch_bounds__(NT) void mprime_tr_kernel(const bf16 *__restrict__ 
                 for (int ib = 0; ib < NKB; ++ib) acc[jb][ib] = mma16(acc[jb][ib], fx[jb], fq[ib]);
         }
     }
-    // lane holds row kk = 32 ib + lane % 32 of M'_b and four consecutive features
+
+    // lane holds row kk = 32 ib + lane % 32 of M'_b and, per register group q,
+    // four consecutive features; staged as [kk][feature], stored by rows
+    __syncthreads();
+    bf16 *ms = reinterpret_cast<bf16 *>(smem);
 #pragma unroll
     for (int ib = 0; ib < NKB; ++ib) {
         const int kk = 32 * ib + (lane & 31);
@@ -559,13 +570,20 @@ __global__ __launch_bounds__(NT) void mprime_tr_kernel(const bf16 *__restrict__ 
         for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t f = f0 + 64 * wave + 32 * jb + acc_row(lane, 4 * q);
-                if (f >= c1) continue;
                 union { uint2 u; bf16 e[4]; } w;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) w.e[e] = (bf16)acc[jb][ib][4 * q + e];
-                *reinterpret_cast<uint2 *>(Mp + (b * KC + kk) * c1 + f) = w.u;
+                *reinterpret_cast<uint2 *>(ms + kk * MS + 64 * wave + 32 * jb + acc_row(lane, 4 * q)) = w.u;
             }
+    }
+    __syncthreads();
+    constexpr int CPM = CW / 8;  // 16-byte chunks per M'_b row segment
+#pragma unroll
+    for (int q = 0; q < KC * CPM / NT; ++q) {
+        const int e = q * NT + tid, row = e / CPM, c = e % CPM;
+        if (f0 + 8 * c < c1)
+            *reinterpret_cast<u32x4 *>(Mp + (b * KC + row) * c1 + f0 + 8 * c) =
+                *reinterpret_cast<const u32x4 *>(ms + row * MS + 8 * c);
     }
 }
 
@@ -600,28 +618,14 @@ template <>
 hipError_t launch_mprime<bf16>(const bf16 *X, const bf16 *T, int64_t ldt, int64_t off, const bf16 *, int64_t B,
                                int64_t n, int64_t, int64_t c1, int kc, bf16 *Mp, hipStream_t st) {
     if (B <= 0) return hipSuccess;
-    constexpr size_t smem = 4 * (32 * 256 * 2 + 32 * 128);
     const dim3 grid((unsigned)((c1 + 255) / 256), (unsigned)B);
-#define DYRA_MP(KC)                                                                                               \
-    {                                                                                                             \
-        static bool attr = false;                                                                                 \
-        if (!attr) {                                                                                              \
-            hipError_t e = hipFuncSetAttribute((const void *)mprime_tr_kernel<KC>,                                \
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);            \
-            if (e != hipSuccess) return e;                                                                        \
-            attr = true;                                                                                          \
-        }                                                                                                         \
-        hipLaunchKernelGGL(mprime_tr_kernel<KC>, grid, dim3(NT), smem, st, X, T, ldt, off, n, c1, Mp);            \
-        break;                                                                                                    \
-    }
     switch (kc) {
-    case 16: DYRA_MP(16)
-    case 32: DYRA_MP(32)
-    case 48: DYRA_MP(48)
-    case 64: DYRA_MP(64)
+    case 16: hipLaunchKernelGGL(mprime_tr_kernel<16>, grid, dim3(NT), 0, st, X, T, ldt, off, n, c1, Mp); break;
+    case 32: hipLaunchKernelGGL(mprime_tr_kernel<32>, grid, dim3(NT), 0, st, X, T, ldt, off, n, c1, Mp); break;
+    case 48: hipLaunchKernelGGL(mprime_tr_kernel<48>, grid, dim3(NT), 0, st, X, T, ldt, off, n, c1, Mp); break;
+    case 64: hipLaunchKernelGGL(mprime_tr_kernel<64>, grid, dim3(NT), 0, st, X, T, ldt, off, n, c1, Mp); break;
     default: return hipErrorInvalidValue;
     }
-#undef DYRA_MP
     return hipGetLastError();
 }
 

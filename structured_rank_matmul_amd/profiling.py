@@ -11,8 +11,8 @@ rocprofv3 writes, with ``--output-format csv``:
 FETCH_SIZE run and a WRITE_SIZE run into HBM bytes per dispatch of one kernel,
 each counter scaled by what it reads for a plain copy kernel whose bytes are
 known (the copy reads and writes exactly ``--copy-bytes``).  The traffic file
-also records a hash of the kernel sources, so that a figure taken before a
-kernel change is recognised as stale.
+also records a hash of the sources the kernel is built from (``--sources``), so
+that a figure taken before a change to that kernel is recognised as stale.
 
     python -m structured_rank_matmul_amd.profiling stats DIR --command "..." --out profiles/x.txt
     python -m structured_rank_matmul_amd.profiling traffic FETCH_DIR WRITE_DIR --kernel REGEX \
@@ -30,13 +30,14 @@ import statistics
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# sources whose change invalidates a recorded traffic figure
-KERNEL_SOURCES = ("csrc/gemm.hip", "csrc/solve.hip", "csrc/mfma_tile.h", "csrc/dyra_api.hip")
+# sources of the GEMM kernels (the output stage's kernel among them): a change
+# to any of them invalidates a recorded traffic figure
+GEMM_SOURCES = ("csrc/gemm.hip", "csrc/mfma_tile.h")
 
 
-def sources_sha256(root: str = HERE) -> str:
+def sources_sha256(sources=GEMM_SOURCES, root: str = HERE) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(root, rel), "rb") as f:
             h.update(rel.encode())
             h.update(f.read())
@@ -149,13 +150,14 @@ def cmd_traffic(a):
         out.append(f"    WRITE_SIZE {v:12.1f} KiB mean over {cnt} dispatches  {short_name(name, 90)}")
     out += ["", f"fetch_bytes_per_dispatch = {fetch_b:.6e}", f"write_bytes_per_dispatch = {write_b:.6e}",
             f"traffic_bytes_per_dispatch = {fetch_b + write_b:.6e}",
-            f"kernel_sources_sha256 = {sources_sha256()}"]
+            f"kernel_sources = {','.join(a.sources)}",
+            f"kernel_sources_sha256 = {sources_sha256(a.sources)}"]
     _write(a.out, "\n".join(out) + "\n")
 
 
 def read_traffic(path: str):
     """Traffic bytes per dispatch from a summary written by ``traffic``, or None
-    if the file is missing or the kernel sources changed since."""
+    if the file is missing or the kernel's sources changed since."""
     if not os.path.exists(path):
         return None
     vals = {}
@@ -164,7 +166,8 @@ def read_traffic(path: str):
             if "=" in line and not line.startswith(" "):
                 k, v = line.split("=", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_sources_sha256") != sources_sha256():
+    sources = tuple(x for x in vals.get("kernel_sources", "").split(",") if x)
+    if not sources or vals.get("kernel_sources_sha256") != sources_sha256(sources):
         return None
     try:
         return float(vals["traffic_bytes_per_dispatch"])
@@ -199,6 +202,8 @@ def main(argv=None):
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
+    t.add_argument("--sources", type=lambda v: tuple(v.split(",")), default=GEMM_SOURCES,
+                   help="comma-separated kernel sources, relative to the package")
     t.add_argument("--title", default="")
     t.add_argument("--out", default="-")
     t.set_defaults(fn=cmd_traffic)
