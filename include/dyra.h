@@ -139,6 +139,21 @@ dyra_status dyra_forward(const void *X, int64_t B, int64_t n, const dyra_plan *p
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The fused linear layer of §2.4: as dyra_forward, but
+ *     Y = X A_s V_s^T + bias + alpha L1 R1
+ * per instance, with the bias added to every row and alpha weighting only the
+ * dynamic correction (alpha = 1 and no bias is Eq. 6 / dyra_forward).
+ *
+ * bias   device, plan dtype, [c2], caller-owned, or NULL for none; aligned to
+ *        its element size (DYRA_ERR_ALIGN otherwise).
+ * alpha  finite (DYRA_ERR_ARG otherwise); 0 gives the static product plus bias.
+ * Everything else, including the paths taken and the failure flags, as for
+ * dyra_forward.  The bias is added in float32 before the single rounding of Y.
+ */
+dyra_status dyra_forward_ex(const void *X, int64_t B, int64_t n, const dyra_plan *plan, const void *bias,
+                            float alpha, void *Y, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Number of instances whose SPD solve broke down in the last
  * dyra_forward(X, B, n, plan, ...) that used this workspace.  Copies the B
  * flags from the workspace on `stream` and synchronises it; *failures

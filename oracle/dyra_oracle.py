@@ -35,7 +35,9 @@ Readings taken where the paper is silent (all listed with the design notes):
   * Where lambda = 0 and L^(1)'s Gram is singular (fewer tokens than the
     correction rank), L^(1) R^(1) is taken as its lambda -> 0+ limit, the
     minimum-norm least-squares solution, which is unique as a product.
-  * No bias and no output scale (Eq. 6 and Algorithm 1 carry neither).
+  * Eq. 6 and Algorithm 1 carry no bias and no scale.  §2.4's fused linear
+    layer adds a bias b and weights the correction by alpha; both are optional
+    arguments here, and alpha = 1 without a bias is Eq. 6.
 """
 from __future__ import annotations
 
@@ -121,29 +123,35 @@ def right_factor(L1: np.ndarray, X: np.ndarray, W_res: np.ndarray, lam: float) -
     return np.linalg.solve(gram, rhs)
 
 
-def inference_instance(X: np.ndarray, plan: OraclePlan) -> np.ndarray:
+def inference_instance(X: np.ndarray, plan: OraclePlan, bias: Optional[np.ndarray] = None,
+                       alpha: float = 1.0) -> np.ndarray:
     """Algorithm 1, procedure Inference, for one instance X [n, c1].
 
     line 10: Y_base <- X W_hat
     line 11: L1 <- X P_L                             (Eq. 7)
     line 12: R1 <- (L1^T L1 + lambda I)^-1 (L1^T X) W_res   (Eq. 5)
     line 13: Y <- Y_base + L1 R1                     (Eq. 6)
+    With §2.4's fused linear layer, line 13 becomes Y <- Y_base + b + alpha L1 R1
+    (bias b [c2] added to every token row; alpha weights the correction only).
     """
     X = np.asarray(X, dtype=np.float64)
     Y_base = X @ plan.W_hat
+    if bias is not None:
+        Y_base = Y_base + np.asarray(bias, dtype=np.float64)[None, :]
     if plan.r_c == 0:
         return Y_base
     L1 = X @ plan.P_L
     R1 = right_factor(L1, X, plan.W_res, plan.lam)
-    return Y_base + L1 @ R1
+    return Y_base + alpha * (L1 @ R1)
 
 
-def inference(X: np.ndarray, B: int, n: int, plan: OraclePlan) -> np.ndarray:
+def inference(X: np.ndarray, B: int, n: int, plan: OraclePlan, bias: Optional[np.ndarray] = None,
+              alpha: float = 1.0) -> np.ndarray:
     """Algorithm 1 Inference over B independent instances of n tokens.
 
     X is [B*n, c1] with instance b in rows [b*n, (b+1)*n).  The paper solves the
     r x r system "for each batch instance" (§2.4), so every instance gets its
-    own L1, R1.
+    own L1, R1.  bias / alpha: §2.4's fused output (see inference_instance).
     """
     X = np.asarray(X, dtype=np.float64)
     if X.shape[0] != B * n:
@@ -151,7 +159,7 @@ def inference(X: np.ndarray, B: int, n: int, plan: OraclePlan) -> np.ndarray:
     Y = np.empty((B * n, plan.W.shape[1]))
     for b in range(B):
         rows = slice(b * n, (b + 1) * n)
-        Y[rows] = inference_instance(X[rows], plan)
+        Y[rows] = inference_instance(X[rows], plan, bias, alpha)
     return Y
 
 

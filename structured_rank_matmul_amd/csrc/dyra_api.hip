@@ -124,8 +124,9 @@ const char *const kDualStages[] = {"decode_project", "decode_coef", "decode_outp
 const char *const kStaticStages[] = {"left", "output"};
 
 template <typename E>
-dyra_status run_forward(const E *X, int64_t B, int64_t n, const dyra_plan *p, E *Y, char *ws, const Layout &L,
-                        hipStream_t st, void *const *events, int32_t n_events, int32_t *n_recorded) {
+dyra_status run_forward(const E *X, int64_t B, int64_t n, const dyra_plan *p, const E *bias, float alpha, E *Y,
+                        char *ws, const Layout &L, hipStream_t st, void *const *events, int32_t n_events,
+                        int32_t *n_recorded) {
     int32_t ev = 0;
     auto mark = [&]() -> dyra_status {
         if (events && ev < n_events) {
@@ -163,18 +164,19 @@ dyra_status run_forward(const E *X, int64_t B, int64_t n, const dyra_plan *p, E 
                 DYRA_OK)
                 return s;
             if ((s = mark()) != DYRA_OK) return s;
-            if ((s = hip_status(dyra::launch_right<E>(Mp, Wres_t, B * p->kc, p->c1, p->c2, p->kc, R1t, st))) !=
-                DYRA_OK)
+            if ((s = hip_status(dyra::launch_right<E>(Mp, Wres_t, B * p->kc, p->c1, p->c2, p->kc, alpha, R1t,
+                                                      st))) != DYRA_OK)
                 return s;
             if ((s = mark()) != DYRA_OK) return s;
         }
         const int kc = path == Path::Primal ? p->kc : 0;
-        if ((s = hip_status(dyra::launch_output<E>(T, ldt, p->kw, kc, Vs, R1t, N, n, p->c2, Y, st))) != DYRA_OK)
+        if ((s = hip_status(dyra::launch_output<E>(T, ldt, p->kw, kc, Vs, R1t, N, n, p->c2, bias, Y, st))) !=
+            DYRA_OK)
             return s;
         if ((s = mark()) != DYRA_OK) return s;
     } else {
         dyra::DecodeArgs<E> a{X, B, n, p->c1, p->c2, p->kw, p->kc, p->k, p->lambda, Aext, Vs, Wres_t, Y,
-                              ws + L.dual, flags};
+                              ws + L.dual, flags, bias, alpha};
         if ((s = hip_status(dyra::launch_decode_project<E>(a, st))) != DYRA_OK) return s;
         if ((s = mark()) != DYRA_OK) return s;
         if ((s = hip_status(dyra::launch_decode_coef<E>(a, st))) != DYRA_OK) return s;
@@ -188,11 +190,13 @@ dyra_status run_forward(const E *X, int64_t B, int64_t n, const dyra_plan *p, E 
 
 // Flags start at zero for every call: the per-instance failure flags are
 // written (0 or 1) by the SPD-solve kernel for every instance, never accumulated.
-dyra_status forward_impl(const void *X, int64_t B, int64_t n, const dyra_plan *p, void *Y, void *workspace,
-                         size_t workspace_bytes, void *stream, void *const *events, int32_t n_events,
-                         int32_t *n_recorded) {
+dyra_status forward_impl(const void *X, int64_t B, int64_t n, const dyra_plan *p, const void *bias, float alpha,
+                         void *Y, void *workspace, size_t workspace_bytes, void *stream, void *const *events,
+                         int32_t n_events, int32_t *n_recorded) {
     if (n_recorded) *n_recorded = 0;
     if (!p) return DYRA_ERR_ARG;
+    if (!std::isfinite(alpha)) return DYRA_ERR_ARG;
+    if (bias && ((uintptr_t)bias % elem_size(p->dtype)) != 0) return DYRA_ERR_ALIGN;
     if (B < 0 || n < 1) return DYRA_ERR_SHAPE;
     if (B == 0) return DYRA_OK;
     if (!X || !Y) return DYRA_ERR_ARG;
@@ -208,8 +212,10 @@ dyra_status forward_impl(const void *X, int64_t B, int64_t n, const dyra_plan *p
     hipStream_t st = (hipStream_t)stream;
     char *ws = (char *)workspace;
     if (p->dtype == DYRA_BF16)
-        return run_forward<bf16>((const bf16 *)X, B, n, p, (bf16 *)Y, ws, L, st, events, n_events, n_recorded);
-    return run_forward<float>((const float *)X, B, n, p, (float *)Y, ws, L, st, events, n_events, n_recorded);
+        return run_forward<bf16>((const bf16 *)X, B, n, p, (const bf16 *)bias, alpha, (bf16 *)Y, ws, L, st, events,
+                                 n_events, n_recorded);
+    return run_forward<float>((const float *)X, B, n, p, (const float *)bias, alpha, (float *)Y, ws, L, st, events,
+                              n_events, n_recorded);
 }
 
 }  // namespace
@@ -336,14 +342,20 @@ size_t dyra_workspace_bytes(const dyra_plan *plan, int64_t B, int64_t n) {
 
 dyra_status dyra_forward(const void *X, int64_t B, int64_t n, const dyra_plan *plan, void *Y, void *workspace,
                          size_t workspace_bytes, void *stream) {
-    return forward_impl(X, B, n, plan, Y, workspace, workspace_bytes, stream, nullptr, 0, nullptr);
+    return forward_impl(X, B, n, plan, nullptr, 1.f, Y, workspace, workspace_bytes, stream, nullptr, 0, nullptr);
+}
+
+dyra_status dyra_forward_ex(const void *X, int64_t B, int64_t n, const dyra_plan *plan, const void *bias,
+                            float alpha, void *Y, void *workspace, size_t workspace_bytes, void *stream) {
+    return forward_impl(X, B, n, plan, bias, alpha, Y, workspace, workspace_bytes, stream, nullptr, 0, nullptr);
 }
 
 dyra_status dyra_forward_timed(const void *X, int64_t B, int64_t n, const dyra_plan *plan, void *Y,
                                void *workspace, size_t workspace_bytes, void *stream, void *const *events,
                                int32_t n_events, int32_t *n_recorded) {
     if (!events || n_events < 1) return DYRA_ERR_ARG;
-    return forward_impl(X, B, n, plan, Y, workspace, workspace_bytes, stream, events, n_events, n_recorded);
+    return forward_impl(X, B, n, plan, nullptr, 1.f, Y, workspace, workspace_bytes, stream, events, n_events,
+                        n_recorded);
 }
 
 const char *dyra_stage_name(const dyra_plan *plan, int64_t n, int32_t i) {

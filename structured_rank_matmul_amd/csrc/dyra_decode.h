@@ -26,6 +26,8 @@ template <typename E> struct DecodeArgs {
     E *Y;             // [B*n][c2]
     char *ws;         // dual-form workspace (decode_workspace_bytes)
     int *flags;       // [B]
+    const E *bias;    // [c2] or null, added to every row
+    float alpha;      // weight of the correction term (1 in Eq. 6)
 };
 
 size_t decode_workspace_bytes(int64_t B, int64_t n, int64_t c1, int kw, int kc);
@@ -34,7 +36,7 @@ size_t decode_workspace_bytes(int64_t B, int64_t n, int64_t c1, int kw, int kc);
 template <typename E> hipError_t launch_decode_project(const DecodeArgs<E> &a, hipStream_t st);
 // Sums the partials into T and forms C_b per instance.
 template <typename E> hipError_t launch_decode_coef(const DecodeArgs<E> &a, hipStream_t st);
-// Y = T_s V_s^T + blockdiag(C_b) (X W_res), streaming W_res and V_s once.
+// Y = T_s V_s^T + bias + alpha blockdiag(C_b) (X W_res), streaming W_res and V_s once.
 template <typename E> hipError_t launch_decode_output(const DecodeArgs<E> &a, hipStream_t st);
 
 }  // namespace dyra

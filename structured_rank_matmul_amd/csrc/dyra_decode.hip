@@ -185,7 +185,8 @@ __global__ __launch_bounds__(NT) void decode_coef_kernel(const float *__restrict
     }
 }
 
-// Y[rows][col0..col0+32) = T_s V_s^T + blockdiag(C_b) (X W_res).  Grid (c2/32,
+// Y[rows][col0..col0+32) = T_s V_s^T + bias + alpha blockdiag(C_b) (X W_res)
+// (§2.4's fused output with bias and correction weight alpha).  Grid (c2/32,
 // row blocks of whole instances).  The 16-deep steps of both contractions are
 // dealt round-robin to the four wavefronts and reduced in LDS.
 template <typename E>
@@ -193,7 +194,8 @@ __global__ __launch_bounds__(NT) void decode_output_kernel(const E *__restrict__
                                                            const float *__restrict__ coef,
                                                            const E *__restrict__ Vs, const E *__restrict__ Wres_t,
                                                            int64_t N, int64_t n, int64_t c1, int64_t c2, int K1,
-                                                           int kw, int64_t rows_blk, E *__restrict__ Y) {
+                                                           int kw, int64_t rows_blk, const E *__restrict__ bias,
+                                                           float alpha, E *__restrict__ Y) {
     __shared__ float Zs[kRowBlock][33];
     __shared__ float Ss[kRowBlock][33];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -243,8 +245,10 @@ __global__ __launch_bounds__(NT) void decode_output_kernel(const E *__restrict__
         const int i = (int)(row - b * n);
         const int rb0 = (int)(b * n - row0);
         const float *Cb = coef + b * n * n;
-        float v = Ss[r][c];
-        for (int j = 0; j < (int)n; ++j) v += Cb[i * n + j] * Zs[rb0 + j][c];
+        float z = 0.f;
+        for (int j = 0; j < (int)n; ++j) z += Cb[i * n + j] * Zs[rb0 + j][c];
+        float v = Ss[r][c] + alpha * z;
+        if (bias) v += (float)bias[col0 + c];
         Y[row * c2 + col0 + c] = to_elem<E>(v);
     }
 }
@@ -281,7 +285,7 @@ template <typename E> hipError_t launch_decode_output(const DecodeArgs<E> &a, hi
     dim3 grid((unsigned)((a.c2 + 31) / 32), (unsigned)((N + rb - 1) / rb));
     hipLaunchKernelGGL((decode_output_kernel<E>), grid, dim3(NT), 0, st, a.X, (const float *)(a.ws + L.T),
                        (const float *)(a.ws + L.coef), a.Vs, a.Wres_t, N, a.n, a.c1, a.c2, a.kw + a.kc, a.kw, rb,
-                       a.Y);
+                       a.bias, a.alpha, a.Y);
     return hipGetLastError();
 }
 

@@ -14,10 +14,10 @@ template <typename E>
 hipError_t launch_gemm_store(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N, int64_t K,
                              E *D, int64_t ldd, hipStream_t st);
 
-// R1t[b][c][kk] = (Mp W_res)[b*kc + kk][c] for the stacked Mp [rows][c1].
+// R1t[b][c][kk] = alpha (Mp W_res)[b*kc + kk][c] for the stacked Mp [rows][c1].
 template <typename E>
-hipError_t launch_right(const E *Mp, const E *Wres_t, int64_t rows, int64_t c1, int64_t c2, int kc, E *R1t,
-                        hipStream_t st);
+hipError_t launch_right(const E *Mp, const E *Wres_t, int64_t rows, int64_t c1, int64_t c2, int kc, float alpha,
+                        E *R1t, hipStream_t st);
 
 // With C C^T = L1_b^T L1_b + lambda I: Q_b = L1_b C^-T replaces L1_b in place
 // (columns [off, off + kc) of T's rows b*n .. b*n + n - 1, leading dimension
@@ -34,11 +34,12 @@ template <typename E>
 hipError_t launch_mprime(const E *X, const E *T, int64_t ldt, int64_t off, const E *Qt, int64_t B, int64_t n,
                          int64_t npad, int64_t c1, int kc, E *Mp, hipStream_t st);
 
-// Y[Ntok][c2] = T[:, 0:kw] V_s^T + T[:, kw:kw+kc] R1_b for each token's
-// instance b (n tokens per instance; R1t[b] is [c2][kc]); T has leading
-// dimension ldt.  kc = 0 gives the static product alone.
+// Y[Ntok][c2] = T[:, 0:kw] V_s^T + bias + T[:, kw:kw+kc] R1_b for each
+// token's instance b (n tokens per instance; R1t[b] is [c2][kc]); T has
+// leading dimension ldt; bias [c2] or null.  kc = 0 gives the static product
+// (plus bias) alone.
 template <typename E>
 hipError_t launch_output(const E *T, int64_t ldt, int kw, int kc, const E *Vs, const E *R1t, int64_t Ntok,
-                         int64_t n, int64_t c2, E *Y, hipStream_t st);
+                         int64_t n, int64_t c2, const E *bias, E *Y, hipStream_t st);
 
 }  // namespace dyra

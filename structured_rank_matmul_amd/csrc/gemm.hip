@@ -70,20 +70,42 @@ template <typename E> __device__ __forceinline__ typename Pack4<E>::type pack4(c
     }
 }
 
-// Row-major D: store4(i, j, p) writes columns j..j+3 of row i.
+// Epilogue functors.  fix4(v, i, j) adjusts four float32 results before they
+// are rounded to E: (i, j) is the first of four consecutive columns of row i
+// (row-major stores) or of four consecutive rows of column j (R1t stores).
+// store4 then writes the rounded four.
+
+// Row-major D: store4(i, j, p) writes columns j..j+3 of row i.  With a bias
+// (the fused linear layer of §2.4: Y = X_tmp A^T + b + alpha L R) every row
+// gets bias[j] added to column j before rounding.
 template <typename E> struct RowStore {
     E *D;
     int64_t ldd;
+    const E *bias = nullptr;  // [ncols] or null
+    int64_t ncols = 0;
+    __device__ __forceinline__ void fix4(float (&v)[4], int64_t, int64_t j) const {
+        if (bias) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (j + q < ncols) v[q] += (float)bias[j + q];
+        }
+    }
     __device__ __forceinline__ void store4(int64_t i, int64_t j, const typename Pack4<E>::type &p) const {
         *reinterpret_cast<typename Pack4<E>::type *>(D + i * ldd + j) = p;
     }
 };
 
 // Stacked right factor: rows r..r+3 (= correction indices kk..kk+3 of
-// instance b = r / kc) of column c, stored as R1t[b][c][kk..kk+3].
+// instance b = r / kc) of column c, stored as R1t[b][c][kk..kk+3], scaled by
+// alpha (the correction's weight in §2.4's fused output; 1 in Eq. 6).
 template <typename E> struct R1tStore {
     E *R1t;
     int64_t kc, c2;
+    float alpha = 1.f;
+    __device__ __forceinline__ void fix4(float (&v)[4], int64_t, int64_t) const {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] *= alpha;
+    }
     __device__ __forceinline__ void store4(int64_t r, int64_t c, const typename Pack4<E>::type &p) const {
         // rows are below 2^31 (instances x correction rank): 32-bit division
         const uint32_t ru = (uint32_t)r, kcu = (uint32_t)kc;
@@ -296,11 +318,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                        acc[i][j][4 * g + 3]};
+                    float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                  acc[i][j][4 * g + 3]};
                     const int ti = (wm * TM + i) * 32, tj = (wn * TN + j) * 32;
                     const int lrow = ROWS ? ti + lr : tj + lr;              // LDS row
                     const int lcol = (ROWS ? tj : ti) + acc_row(lane, 4 * g);  // 4 consecutive
+                    epi.fix4(v, row0 + (ROWS ? lrow : lcol), col0 + (ROWS ? lcol : lrow));
                     *reinterpret_cast<P *>(lds + lrow * OS + lcol) = pack4<E>(v);
                 }
         __syncthreads();
@@ -319,11 +342,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                        acc[i][j][4 * g + 3]};
+                    float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                  acc[i][j][4 * g + 3]};
                     const int64_t rb = row0 + wm * TM * 32 + i * 32, cb0 = col0 + wn * TN * 32 + j * 32;
                     const int64_t r = ROWS ? rb + lr : rb + acc_row(lane, 4 * g);
                     const int64_t c = ROWS ? cb0 + acc_row(lane, 4 * g) : cb0 + lr;
+                    epi.fix4(v, r, c);
                     if (r < M && c < N) epi.store4(r, c, pack4<E>(v));
                 }
     }
@@ -411,34 +435,34 @@ hipError_t launch_gemm_store(const E *A, int64_t lda, const E *B, int64_t ldb, i
 }
 
 template <typename E>
-hipError_t launch_right(const E *Mp, const E *Wres_t, int64_t rows, int64_t c1, int64_t c2, int kc, E *R1t,
-                        hipStream_t st) {
+hipError_t launch_right(const E *Mp, const E *Wres_t, int64_t rows, int64_t c1, int64_t c2, int kc, float alpha,
+                        E *R1t, hipStream_t st) {
     if (rows <= 0) return hipSuccess;
-    return gemm_dispatch<E, false, false>(Mp, c1, Wres_t, c1, rows, c2, c1, Corr<E>{}, R1tStore<E>{R1t, kc, c2},
-                                          st);
+    return gemm_dispatch<E, false, false>(Mp, c1, Wres_t, c1, rows, c2, c1, Corr<E>{},
+                                          R1tStore<E>{R1t, kc, c2, alpha}, st);
 }
 
 template <typename E>
 hipError_t launch_output(const E *T, int64_t ldt, int kw, int kc, const E *Vs, const E *R1t, int64_t Ntok,
-                         int64_t n, int64_t c2, E *Y, hipStream_t st) {
+                         int64_t n, int64_t c2, const E *bias, E *Y, hipStream_t st) {
     if (Ntok <= 0) return hipSuccess;
     if (kc > 0 && (n < 1 || kc > 64 || kc % 16 != 0)) return hipErrorInvalidValue;
-    if (kc == 0) return gemm_dispatch<E, true, false>(T, ldt, Vs, kw, Ntok, c2, kw, Corr<E>{}, RowStore<E>{Y, c2}, st);
-    return gemm_dispatch<E, true, true>(T, ldt, Vs, kw, Ntok, c2, kw, Corr<E>{R1t, n, kw, kc}, RowStore<E>{Y, c2},
-                                        st);
+    const RowStore<E> epi{Y, c2, bias, c2};
+    if (kc == 0) return gemm_dispatch<E, true, false>(T, ldt, Vs, kw, Ntok, c2, kw, Corr<E>{}, epi, st);
+    return gemm_dispatch<E, true, true>(T, ldt, Vs, kw, Ntok, c2, kw, Corr<E>{R1t, n, kw, kc}, epi, st);
 }
 
 template hipError_t launch_gemm_store<bf16>(const bf16 *, int64_t, const bf16 *, int64_t, int64_t, int64_t, int64_t,
                                             bf16 *, int64_t, hipStream_t);
 template hipError_t launch_gemm_store<float>(const float *, int64_t, const float *, int64_t, int64_t, int64_t,
                                              int64_t, float *, int64_t, hipStream_t);
-template hipError_t launch_right<bf16>(const bf16 *, const bf16 *, int64_t, int64_t, int64_t, int, bf16 *,
+template hipError_t launch_right<bf16>(const bf16 *, const bf16 *, int64_t, int64_t, int64_t, int, float, bf16 *,
                                        hipStream_t);
-template hipError_t launch_right<float>(const float *, const float *, int64_t, int64_t, int64_t, int, float *,
+template hipError_t launch_right<float>(const float *, const float *, int64_t, int64_t, int64_t, int, float, float *,
                                         hipStream_t);
 template hipError_t launch_output<bf16>(const bf16 *, int64_t, int, int, const bf16 *, const bf16 *, int64_t,
-                                        int64_t, int64_t, bf16 *, hipStream_t);
+                                        int64_t, int64_t, const bf16 *, bf16 *, hipStream_t);
 template hipError_t launch_output<float>(const float *, int64_t, int, int, const float *, const float *, int64_t,
-                                         int64_t, int64_t, float *, hipStream_t);
+                                         int64_t, int64_t, const float *, float *, hipStream_t);
 
 }  // namespace dyra

@@ -24,7 +24,7 @@ _DTYPES = {"f32": DYRA_F32, "float32": DYRA_F32, "bf16": DYRA_BF16, "bfloat16": 
 # Every symbol include/dyra.h declares.
 EXPORTED = (
     "dyra_status_str", "dyra_factorize_host", "dyra_prepare", "dyra_plan_destroy", "dyra_plan_info",
-    "dyra_workspace_bytes", "dyra_forward", "dyra_forward_status", "dyra_dense_ref",
+    "dyra_workspace_bytes", "dyra_forward", "dyra_forward_ex", "dyra_forward_status", "dyra_dense_ref",
     "dyra_forward_timed", "dyra_stage_name",
 )
 
@@ -64,6 +64,8 @@ def load() -> ctypes.CDLL:
     L.dyra_workspace_bytes.restype = ctypes.c_size_t
     L.dyra_forward.argtypes = [vp, i64, i64, vp, vp, vp, ctypes.c_size_t, vp]
     L.dyra_forward.restype = ctypes.c_int
+    L.dyra_forward_ex.argtypes = [vp, i64, i64, vp, vp, f32, vp, vp, ctypes.c_size_t, vp]
+    L.dyra_forward_ex.restype = ctypes.c_int
     L.dyra_forward_status.argtypes = [vp, i64, i64, vp, vp, ctypes.POINTER(i32)]
     L.dyra_forward_status.restype = ctypes.c_int
     L.dyra_dense_ref.argtypes = [vp, vp, i64, i64, i64, ctypes.c_int, vp, vp]
@@ -200,6 +202,28 @@ def dyra_forward(X, B: int, n: int, plan: Plan, Y=None, workspace=None, stream=N
                              _dev_ptr(workspace), workspace.numel() * workspace.element_size(),
                              _stream_ptr(stream))
     _check(st, "dyra_forward")
+    return Y
+
+
+def dyra_forward_ex(X, B: int, n: int, plan: Plan, bias=None, alpha: float = 1.0, Y=None, workspace=None,
+                    stream=None):
+    """§2.4's fused linear layer: Y = X A_s V_s^T + bias + alpha L1 R1 (bias [c2] device tensor or None)."""
+    import torch
+    if X.dtype != plan.torch_dtype:
+        raise ValueError(f"X dtype {X.dtype} does not match the plan's {plan.torch_dtype}")
+    if tuple(X.shape) != (B * n, plan.c1):
+        raise ValueError(f"X shape {tuple(X.shape)} != ({B * n}, {plan.c1})")
+    if bias is not None and (bias.dtype != X.dtype or tuple(bias.shape) != (plan.c2,)):
+        raise ValueError(f"bias must be [{plan.c2}] in {X.dtype}")
+    if Y is None:
+        Y = torch.empty((B * n, plan.c2), dtype=X.dtype, device=X.device)
+    if workspace is None:
+        workspace = alloc_workspace(plan, B, n)
+    st = load().dyra_forward_ex(_dev_ptr(X), int(B), int(n), ctypes.c_void_p(plan.handle),
+                                _dev_ptr(bias) if bias is not None else None, float(alpha), _dev_ptr(Y),
+                                _dev_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream_ptr(stream))
+    _check(st, "dyra_forward_ex")
     return Y
 
 

@@ -63,6 +63,7 @@ def test_forward_and_dense_ref_reject_bad_arguments():
     L = dyra.load()
     # null plan
     assert L.dyra_forward(16, 1, 4, None, 16, 16, 1 << 20, None) == 1
+    assert L.dyra_forward_ex(16, 1, 4, None, None, 1.0, 16, 16, 1 << 20, None) == 1
     assert L.dyra_workspace_bytes(None, 1, 4) == 0
     # dense ref: shape, dtype and alignment are checked before any launch
     assert L.dyra_dense_ref(16, 16, 8, 48, 64, 1, 16, None) == 2

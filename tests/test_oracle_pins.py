@@ -364,3 +364,48 @@ def test_rank_arguments_validated():
         orc.offline_preparation(W, 3, 2)
     with pytest.raises(ValueError):
         orc.inference(gaussian((5, 5), 91), 2, 3, orc.offline_preparation(W, 1, 1))
+
+
+# ------------------------------------------------------------------ §2.4 fused output: bias and alpha
+
+@pytest.mark.parametrize("c1,c2", [(7, 5), (6, 9)])
+def test_fused_bias_full_rank_is_exact_affine(c1, c2):
+    """§2.4's fused linear layer at full static rank without correction is the
+    plain affine map X W + b (P1 with a bias)."""
+    W = gaussian((c1, c2), 100)
+    X = gaussian((8, c1), 101)
+    b = gaussian((1, c2), 102)[0]
+    plan = orc.offline_preparation(W, min(c1, c2), 0)
+    Y = orc.inference(X, 2, 4, plan, bias=b)
+    assert orc.rel_fro(Y, X @ W + b[None, :]) < 1e-13
+
+
+def test_fused_alpha_zero_is_weight_only_plus_bias():
+    """alpha = 0 leaves the static product X W_hat plus the bias, with W_hat the
+    rank-r_w truncated SVD formed here from numpy's SVD of W directly."""
+    W = gaussian((12, 10), 103)
+    X = gaussian((15, 12), 104)
+    b = gaussian((1, 10), 105)[0]
+    plan = orc.offline_preparation(W, 3, 4)
+    U, S, Vt = np.linalg.svd(W)
+    W_hat = (U[:, :3] * S[:3]) @ Vt[:3]
+    Y = orc.inference(X, 3, 5, plan, bias=b, alpha=0.0)
+    np.testing.assert_allclose(Y, X @ W_hat + b[None, :], atol=1e-12)
+
+
+@pytest.mark.parametrize("alpha", [0.5, -1.25, 3.0])
+def test_fused_alpha_scales_only_the_correction(alpha):
+    """Y(alpha) - Y(0) = alpha (Y(1) - Y(0)), and the bias shifts every row of
+    every instance by b: the static part is neither scaled nor biased twice."""
+    W = gaussian((16, 11), 106)
+    X = gaussian((18, 16), 107)
+    b = gaussian((1, 11), 108)[0]
+    plan = orc.offline_preparation(W, 4, 3, 0.05)
+    y0 = orc.inference(X, 3, 6, plan, alpha=0.0)
+    y1 = orc.inference(X, 3, 6, plan)
+    ya = orc.inference(X, 3, 6, plan, alpha=alpha)
+    np.testing.assert_allclose(ya - y0, alpha * (y1 - y0), atol=1e-12)
+    yb = orc.inference(X, 3, 6, plan, bias=b, alpha=alpha)
+    np.testing.assert_allclose(yb - ya, np.broadcast_to(b, ya.shape), atol=1e-12)
+    # the correction really is there: alpha changes the output
+    assert orc.rel_fro(y1, y0) > 1e-3
