@@ -128,6 +128,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time on the host")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--no-flops-matched", action="store_true",
+                    help="skip the FLOPs-matched static baseline (a second prepare and timing per layer)")
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run three forward steps and a calibration copy only (for rocprofv3 --pmc runs)")
@@ -141,7 +143,7 @@ def main():
     import torch.nn.functional as F
 
     import oracle as orc
-    from structured_rank_matmul_amd import dyra, synth
+    from structured_rank_matmul_amd import costs, dyra, synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -282,6 +284,37 @@ def main():
         parity["worst_own_error_gap"] = float(f"{worst_gap:.3e}")
         parity["sample_instances"] = sample
 
+    # ---- FLOPs-matched static baseline (§2.3 FLOPs-Matched Comparison,
+    # Appendix E.4): the truncated SVD at the rank whose exact FLOPs equal
+    # DyRA's, run through the same library (the k = 0 path), timed and scored
+    # on the same sampled instances against the exact product X W
+    matched = None
+    if not args.no_flops_matched:
+        matched = {}
+        sample = [0, B // 2, B - 1]
+        rows = np.concatenate([np.arange(b * n, (b + 1) * n) for b in sample])
+        for L in layers:
+            spec = L["spec"]
+            s = costs.flops_matched_rank(n, spec.c1, spec.c2, spec.r, spec.k)
+            plan_s = dyra.dyra_prepare(L["W"], s, 0, 0.0, w.dtype, 0)
+            ws_s = dyra.alloc_workspace(plan_s, B, n)
+            ys = torch.empty_like(L["y"])
+            t_s = time_loop(lambda: dyra.dyra_forward(L["xd"], B, n, plan_s, ys, ws_s, stream), reps, 3, stream)
+            t_d = time_loop(lambda: dyra.dyra_forward(L["xd"], B, n, L["plan"], L["y"], L["ws"], stream), reps, 3,
+                            stream)
+            Xs = L["X"].exact[rows]
+            exact = Xs @ L["W"].astype(np.float64)
+            e_s = orc.rel_fro(ys.float().cpu().numpy().astype(np.float64)[rows], exact)
+            e_d = orc.rel_fro(L["y"].float().cpu().numpy().astype(np.float64)[rows], exact)
+            matched[spec.name] = {"static_rank": s, "e_dyra": round(e_d, 5), "e_static": round(e_s, 5),
+                                  "t_dyra_us": round(t_d * 1e6, 2), "t_static_us": round(t_s * 1e6, 2),
+                                  "flops_dyra": costs.dyra_flops(n, spec.c1, spec.c2, spec.r, spec.k) * B,
+                                  "flops_static": costs.static_flops(n, spec.c1, spec.c2, s) * B}
+            log(f"{spec.name}: FLOPs-matched static rank {s}: e_static {e_s:.4f} vs e_dyra {e_d:.4f}; "
+                f"t_static {t_s * 1e6:.1f} us vs t_dyra {t_d * 1e6:.1f} us")
+            plan_s.close()
+        matched["sample_instances"] = sample
+
     cpu = None
     if not args.no_cpu_baseline:
         plans_orc = [L.get("orc") or orc.offline_preparation(L["W"].astype(np.float64), L["spec"].r,
@@ -315,6 +348,7 @@ def main():
         "dense_tflops": round(dense_flops / t_dense / 1e12, 1),
         "stage_us": {L["spec"].name: {k: round(v * 1e6, 2) for k, v in L["stages"].items()} for L in layers},
         "rel_fro_error": parity,
+        "flops_matched_static": matched,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
