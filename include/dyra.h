@@ -96,6 +96,30 @@ dyra_status dyra_factorize_host(const float *W, int64_t c1, int64_t c2, int32_t 
 dyra_status dyra_prepare(const float *W, int64_t c1, int64_t c2, int32_t r, int32_t k,
                          float lambda, dyra_dtype dtype, int device, dyra_plan **plan_out);
 
+/*
+ * dyra_prepare with the method's two further knobs (§2.2 Fig. 2 / Appendix E.3
+ * Gaussian R^(0); §3.3 ablation over the ALS iteration count t):
+ *
+ * R0              host, float32, row-major [k][c2], caller-owned, not retained;
+ *                 used as R^(0) in P_L = W_res R0^T (R0 R0^T + lambda I)^-1
+ *                 (Eq. 7) in place of the top-k right singular vectors of W_res.
+ *                 NULL keeps the default (Appendix D).  Non-finite entries give
+ *                 DYRA_ERR_NUMERIC, a rank-deficient R0 with lambda = 0 as well.
+ * als_half_steps  number of single ALS updates, alternating L (Eq. 4) and R
+ *                 (Eq. 5) from R^(0): 2 = one iteration, t = 1 (Algorithm 1,
+ *                 dyra_prepare's choice), 3 = t 1.5 (L, R, L), 4 = t 2, up to 8;
+ *                 DYRA_ERR_ARG outside [2, 8].  The output is the product of the
+ *                 last L and the last R.  Ignored when k = 0.
+ *
+ * A plan with als_half_steps > 2 also holds W_res untransposed ([c1][c2]) and
+ * needs a larger workspace; dyra_forward runs the extra steps for instances of
+ * n > 16 tokens with n >= k and returns DYRA_ERR_SHAPE for the dual form
+ * (n <= 16 or n < k), which carries one ALS step only.
+ */
+dyra_status dyra_prepare_ex(const float *W, int64_t c1, int64_t c2, int32_t r, int32_t k, float lambda,
+                            dyra_dtype dtype, int device, const float *R0, int32_t als_half_steps,
+                            dyra_plan **plan_out);
+
 /* Releases a plan and its device memory.  NULL is ignored. */
 void dyra_plan_destroy(dyra_plan *plan);
 

@@ -124,7 +124,7 @@ def right_factor(L1: np.ndarray, X: np.ndarray, W_res: np.ndarray, lam: float) -
 
 
 def inference_instance(X: np.ndarray, plan: OraclePlan, bias: Optional[np.ndarray] = None,
-                       alpha: float = 1.0) -> np.ndarray:
+                       alpha: float = 1.0, half_steps: int = 2) -> np.ndarray:
     """Algorithm 1, procedure Inference, for one instance X [n, c1].
 
     line 10: Y_base <- X W_hat
@@ -133,6 +133,9 @@ def inference_instance(X: np.ndarray, plan: OraclePlan, bias: Optional[np.ndarra
     line 13: Y <- Y_base + L1 R1                     (Eq. 6)
     With §2.4's fused linear layer, line 13 becomes Y <- Y_base + b + alpha L1 R1
     (bias b [c2] added to every token row; alpha weights the correction only).
+    half_steps > 2 continues the alternation of Eq. 4 / Eq. 5 from there (the
+    §3.3 ablation over the iteration count: 3 = t 1.5, 4 = t 2) and uses the
+    product of the last L and the last R.
     """
     X = np.asarray(X, dtype=np.float64)
     Y_base = X @ plan.W_hat
@@ -140,26 +143,32 @@ def inference_instance(X: np.ndarray, plan: OraclePlan, bias: Optional[np.ndarra
         Y_base = Y_base + np.asarray(bias, dtype=np.float64)[None, :]
     if plan.r_c == 0:
         return Y_base
-    L1 = X @ plan.P_L
-    R1 = right_factor(L1, X, plan.W_res, plan.lam)
-    return Y_base + alpha * (L1 @ R1)
+    if half_steps == 2:
+        L1 = X @ plan.P_L
+        R1 = right_factor(L1, X, plan.W_res, plan.lam)
+        return Y_base + alpha * (L1 @ R1)
+    L, R = als(X, plan.W_res, plan.R0, plan.lam, half_steps)
+    return Y_base + alpha * (L @ R)
 
 
 def inference(X: np.ndarray, B: int, n: int, plan: OraclePlan, bias: Optional[np.ndarray] = None,
-              alpha: float = 1.0) -> np.ndarray:
+              alpha: float = 1.0, half_steps: int = 2) -> np.ndarray:
     """Algorithm 1 Inference over B independent instances of n tokens.
 
     X is [B*n, c1] with instance b in rows [b*n, (b+1)*n).  The paper solves the
     r x r system "for each batch instance" (§2.4), so every instance gets its
-    own L1, R1.  bias / alpha: §2.4's fused output (see inference_instance).
+    own L1, R1.  bias / alpha: §2.4's fused output; half_steps: further ALS
+    updates (see inference_instance).
     """
     X = np.asarray(X, dtype=np.float64)
     if X.shape[0] != B * n:
         raise ValueError("X rows must equal B*n")
+    if half_steps < 2:
+        raise ValueError("half_steps must be >= 2")
     Y = np.empty((B * n, plan.W.shape[1]))
     for b in range(B):
         rows = slice(b * n, (b + 1) * n)
-        Y[rows] = inference_instance(X[rows], plan, bias, alpha)
+        Y[rows] = inference_instance(X[rows], plan, bias, alpha, half_steps)
     return Y
 
 

@@ -23,9 +23,11 @@ struct dyra_plan {
     int32_t r, k;     // static and correction ranks as requested
     int32_t kw, kc;   // padded: kw = r rounded up to 32, kc = k rounded up to 16
     float lambda;
+    int32_t half_steps;  // single ALS updates: 2 = Algorithm 1 (t = 1), 3 = t 1.5, 4 = t 2, ...
     void *Aext;       // [kw + kc][c1]: rows 0..r-1 = A_s columns, rows kw..kw+k-1 = P_L columns
     void *Vs;         // [c2][kw]: V_s
     void *Wres_t;     // [c2][c1]: W_res transposed
+    void *Wres;       // [c1][c2]: W_res (only with half_steps > 2, for the L updates)
 };
 
 namespace {
@@ -35,6 +37,7 @@ using dyra::bf16;
 constexpr size_t kAlign = 256;
 constexpr int kMaxCorrection = 64;
 constexpr int kMaxDualTokens = 16;
+constexpr int kMaxHalfSteps = 8;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -76,9 +79,15 @@ Path path_for(const dyra_plan *p, int64_t n) {
 //                                (float32 only; bf16 reads Q_b from T)
 //   Mp     [B * kc][c1]          M'_b = Q_b^T X_b stacked over instances
 //   R1t    [B][c2][kc]           R1_b transposed
+//   with further ALS steps (half_steps > 2, als.hip):
+//   C      float64 [B][kc][kc]   Cholesky factors of the last R update
+//   R1row  [B*kc][c2]            R' by rows
+//   Sp     [B*kc][c1]            S'^T = R' W_res^T
+//   H, Kp  float32 [B][kc][kc]   R' R'^T and the L update's coefficients
+//   P      [B*kc][c1]            coefficient rows of the new L
 //   dual   decode workspace      (n <= 16 or n < k only)
 struct Layout {
-    size_t flags, T, Qt, Mp, R1t, dual, total;
+    size_t flags, T, Qt, Mp, R1t, C, R1row, Sp, H, Kp, P, dual, total;
     int64_t npad;
 };
 
@@ -101,6 +110,21 @@ Layout workspace_layout(const dyra_plan *p, int64_t B, int64_t n) {
         off += align_up(es * B * p->kc * p->c1);
         L.R1t = off;
         off += align_up(es * B * p->c2 * p->kc);
+        if (p->half_steps > 2) {
+            const size_t kk = (size_t)B * p->kc * p->kc;
+            L.C = off;
+            off += align_up(sizeof(double) * kk);
+            L.R1row = off;
+            off += align_up(es * B * p->kc * p->c2);
+            L.Sp = off;
+            off += align_up(es * B * p->kc * p->c1);
+            L.H = off;
+            off += align_up(sizeof(float) * kk);
+            L.Kp = off;
+            off += align_up(sizeof(float) * kk);
+            L.P = off;
+            off += align_up(es * B * p->kc * p->c1);
+        }
     } else if (path_for(p, n) == Path::Dual) {
         L.dual = off;
         off += align_up(dyra::decode_workspace_bytes(B, n, p->c1, p->kw, p->kc));
@@ -119,22 +143,31 @@ dyra_status check_device(int device) {
     return cur == device ? DYRA_OK : DYRA_ERR_NODEVICE;
 }
 
-const char *const kPrimalStages[] = {"left", "gram_q", "mprime", "right", "output"};
-const char *const kDualStages[] = {"decode_project", "decode_coef", "decode_output"};
-const char *const kStaticStages[] = {"left", "output"};
+// Names of the kernels dyra_forward enqueues for (plan, n), in order.
+std::vector<const char *> stage_list(const dyra_plan *p, int64_t n) {
+    switch (path_for(p, n)) {
+    case Path::Dual: return {"decode_project", "decode_coef", "decode_output"};
+    case Path::Static: return {"left", "output"};
+    case Path::Primal: break;
+    }
+    std::vector<const char *> v = {"left", "gram_q", "mprime", "right"};
+    for (int h = 2; h < p->half_steps; h += 2) {
+        for (const char *st : {"als_transpose", "als_s", "als_gram", "als_coef", "als_apply", "als_lupdate"})
+            v.push_back(st);
+        if (h + 1 < p->half_steps)
+            for (const char *st : {"gram_q", "mprime", "right"}) v.push_back(st);
+    }
+    v.push_back("output");
+    return v;
+}
 
 template <typename E>
 dyra_status run_forward(const E *X, int64_t B, int64_t n, const dyra_plan *p, const E *bias, float alpha, E *Y,
                         char *ws, const Layout &L, hipStream_t st, void *const *events, int32_t n_events,
                         int32_t *n_recorded) {
     int32_t ev = 0;
-    auto mark = [&]() -> dyra_status {
-        if (events && ev < n_events) {
-            if (hipEventRecord((hipEvent_t)events[ev], st) != hipSuccess) return DYRA_ERR_HIP;
-            ++ev;
-        }
-        return DYRA_OK;
-    };
+    const dyra::EventMark em{events, n_events, &ev, st};
+    auto mark = [&]() -> dyra_status { return hip_status(em(hipSuccess)); };
     const int64_t N = B * n;
     const E *Aext = (const E *)p->Aext;
     const E *Vs = (const E *)p->Vs;
@@ -156,18 +189,36 @@ dyra_status run_forward(const E *X, int64_t B, int64_t n, const dyra_plan *p, co
             E *Qt = (E *)(ws + L.Qt);
             E *Mp = (E *)(ws + L.Mp);
             R1t = (E *)(ws + L.R1t);
-            if ((s = hip_status(dyra::launch_gram_q<E>(T, ldt, p->kw, B, n, L.npad, p->k, p->kc, p->lambda, Qt, flags,
-                                                       st))) != DYRA_OK)
-                return s;
-            if ((s = mark()) != DYRA_OK) return s;
-            if ((s = hip_status(dyra::launch_mprime<E>(X, T, ldt, p->kw, Qt, B, n, L.npad, p->c1, p->kc, Mp, st))) !=
-                DYRA_OK)
-                return s;
-            if ((s = mark()) != DYRA_OK) return s;
-            if ((s = hip_status(dyra::launch_right<E>(Mp, Wres_t, B * p->kc, p->c1, p->c2, p->kc, alpha, R1t,
-                                                      st))) != DYRA_OK)
-                return s;
-            if ((s = mark()) != DYRA_OK) return s;
+            double *Cf = p->half_steps > 2 ? (double *)(ws + L.C) : nullptr;
+            // R update (Eq. 5, Algorithm 1 line 12): Q = L C^-T in place, M' = Q^T X,
+            // R' = M' W_res (times alpha when it is the last update)
+            auto r_update = [&](float alpha_r) -> dyra_status {
+                dyra_status t;
+                if ((t = hip_status(dyra::launch_gram_q<E>(T, ldt, p->kw, B, n, L.npad, p->k, p->kc, p->lambda, Qt,
+                                                           flags, Cf, st))) != DYRA_OK)
+                    return t;
+                if ((t = mark()) != DYRA_OK) return t;
+                if ((t = hip_status(dyra::launch_mprime<E>(X, T, ldt, p->kw, Qt, B, n, L.npad, p->c1, p->kc, Mp,
+                                                           st))) != DYRA_OK)
+                    return t;
+                if ((t = mark()) != DYRA_OK) return t;
+                if ((t = hip_status(dyra::launch_right<E>(Mp, Wres_t, B * p->kc, p->c1, p->c2, p->kc, alpha_r, R1t,
+                                                          st))) != DYRA_OK)
+                    return t;
+                return mark();
+            };
+            if ((s = r_update(p->half_steps == 2 ? alpha : 1.f)) != DYRA_OK) return s;
+            // further ALS steps (§3.3 ablation): an L update (Eq. 4), then an R update
+            for (int h = 2; h < p->half_steps; h += 2) {
+                const bool last_l = h + 1 == p->half_steps;
+                const dyra::AlsArgs<E> a{X, B, n, p->c1, p->c2, p->kc, p->k, p->lambda, R1t, (E *)(ws + L.R1row),
+                                         (const E *)p->Wres, (E *)(ws + L.Sp), (float *)(ws + L.H), Cf,
+                                         (float *)(ws + L.Kp), (E *)(ws + L.P), flags, T, ldt, p->kw};
+                if ((s = hip_status(dyra::launch_als_lupdate<E>(a, last_l ? 1 : 0, alpha, st, em))) != DYRA_OK)
+                    return s;
+                if (last_l) break;
+                if ((s = r_update(h + 2 == p->half_steps ? alpha : 1.f)) != DYRA_OK) return s;
+            }
         }
         const int kc = path == Path::Primal ? p->kc : 0;
         if ((s = hip_status(dyra::launch_output<E>(T, ldt, p->kw, kc, Vs, R1t, N, n, p->c2, bias, Y, st))) !=
@@ -204,6 +255,7 @@ dyra_status forward_impl(const void *X, int64_t B, int64_t n, const dyra_plan *p
     if (B > INT32_MAX / std::max<int64_t>(n, 1)) return DYRA_ERR_SHAPE;
     const Path path = path_for(p, n);
     if (path == Path::Dual && n > kMaxDualTokens) return DYRA_ERR_SHAPE;  // n < k with k > 16 tokens
+    if (path == Path::Dual && p->half_steps > 2) return DYRA_ERR_SHAPE;   // one ALS step only in the dual form
     const Layout L = workspace_layout(p, B, n);
     if (!workspace || workspace_bytes < L.total) return DYRA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return DYRA_ERR_ALIGN;
@@ -240,10 +292,17 @@ const char *dyra_status_str(dyra_status s) {
 
 dyra_status dyra_prepare(const float *W, int64_t c1, int64_t c2, int32_t r, int32_t k, float lambda,
                          dyra_dtype dtype, int device, dyra_plan **plan_out) {
+    return dyra_prepare_ex(W, c1, c2, r, k, lambda, dtype, device, nullptr, 2, plan_out);
+}
+
+dyra_status dyra_prepare_ex(const float *W, int64_t c1, int64_t c2, int32_t r, int32_t k, float lambda,
+                            dyra_dtype dtype, int device, const float *R0, int32_t als_half_steps,
+                            dyra_plan **plan_out) {
     if (!plan_out) return DYRA_ERR_ARG;
     *plan_out = nullptr;
     if (dtype != DYRA_BF16 && dtype != DYRA_F32) return DYRA_ERR_DTYPE;
     if (!W || c1 <= 0 || c2 <= 0 || r < 0 || k < 0) return DYRA_ERR_ARG;
+    if (als_half_steps < 2 || als_half_steps > kMaxHalfSteps) return DYRA_ERR_ARG;
     if ((int64_t)r + k > std::min(c1, c2)) return DYRA_ERR_ARG;
     if (!(lambda >= 0.f) || !std::isfinite(lambda)) return DYRA_ERR_ARG;
     if (c1 % 32 != 0 || c2 % 32 != 0) return DYRA_ERR_SHAPE;
@@ -254,7 +313,7 @@ dyra_status dyra_prepare(const float *W, int64_t c1, int64_t c2, int32_t r, int3
     if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) return DYRA_ERR_NODEVICE;
 
     dyra::Factors f;
-    dyra_status s = dyra::factorize(W, c1, c2, r, k, (double)lambda, &f);
+    dyra_status s = dyra::factorize(W, c1, c2, r, k, (double)lambda, &f, k > 0 ? R0 : nullptr);
     if (s != DYRA_OK) return s;
 
     const size_t es = elem_size(dtype);
@@ -280,6 +339,7 @@ dyra_status dyra_prepare(const float *W, int64_t c1, int64_t c2, int32_t r, int3
     p->kw = kw;
     p->kc = kc;
     p->lambda = lambda;
+    p->half_steps = k > 0 ? als_half_steps : 2;
     int prev = -1;
     (void)hipGetDevice(&prev);
     if (hipSetDevice(device) != hipSuccess) {
@@ -301,6 +361,7 @@ dyra_status dyra_prepare(const float *W, int64_t c1, int64_t c2, int32_t r, int3
     };
     if ((s = upload(A, &p->Aext)) == DYRA_OK && (s = upload(V, &p->Vs)) == DYRA_OK)
         s = upload(Rt, &p->Wres_t);
+    if (s == DYRA_OK && p->half_steps > 2) s = upload(f.W_res, &p->Wres);
     if (prev >= 0) (void)hipSetDevice(prev);
     if (s != DYRA_OK) {
         dyra_plan_destroy(p);
@@ -318,6 +379,7 @@ void dyra_plan_destroy(dyra_plan *plan) {
     if (plan->Aext) (void)hipFree(plan->Aext);
     if (plan->Vs) (void)hipFree(plan->Vs);
     if (plan->Wres_t) (void)hipFree(plan->Wres_t);
+    if (plan->Wres) (void)hipFree(plan->Wres);
     if (prev >= 0) (void)hipSetDevice(prev);
     delete plan;
 }
@@ -360,12 +422,8 @@ dyra_status dyra_forward_timed(const void *X, int64_t B, int64_t n, const dyra_p
 
 const char *dyra_stage_name(const dyra_plan *plan, int64_t n, int32_t i) {
     if (!plan || n < 1 || i < 0) return nullptr;
-    switch (path_for(plan, n)) {
-    case Path::Primal: return i < 5 ? kPrimalStages[i] : nullptr;
-    case Path::Dual: return i < 3 ? kDualStages[i] : nullptr;
-    case Path::Static: return i < 2 ? kStaticStages[i] : nullptr;
-    }
-    return nullptr;
+    const std::vector<const char *> v = stage_list(plan, n);
+    return i < (int32_t)v.size() ? v[(size_t)i] : nullptr;
 }
 
 dyra_status dyra_forward_status(const dyra_plan *plan, int64_t B, int64_t n, const void *workspace, void *stream,

@@ -21,7 +21,9 @@ struct Factors {
     std::vector<double> W_res;  // [c1][c2]  W - A_s V_s^T
 };
 
+// R0_in: host float32 [k][c2] to use as R^(0) (e.g. a Gaussian draw, §2.2
+// Fig. 2), or null for the top-k right singular vectors of W_res (Appendix D).
 dyra_status factorize(const float *W, int64_t c1, int64_t c2, int32_t r, int32_t k, double lambda,
-                      Factors *out);
+                      Factors *out, const float *R0_in = nullptr);
 
 }  // namespace dyra

@@ -23,10 +23,12 @@ hipError_t launch_right(const E *Mp, const E *Wres_t, int64_t rows, int64_t c1, 
 // (columns [off, off + kc) of T's rows b*n .. b*n + n - 1, leading dimension
 // ldt).  float32 also writes Qt[b] = Q_b^T ([kc][npad], token-contiguous, zero
 // for tokens n..npad-1); bf16 leaves Qt untouched.  flags[b] = 1 if a pivot
-// broke down (then Q_b = 0).  kc in {16, 32, 48, 64}.
+// broke down (then Q_b = 0).  kc in {16, 32, 48, 64}.  Cout, if not null,
+// receives the Cholesky factor C_b ([B][kc][kc] float64, lower, identity on
+// the padding) for the L updates of further ALS steps.
 template <typename E>
 hipError_t launch_gram_q(E *T, int64_t ldt, int64_t off, int64_t B, int64_t n, int64_t npad, int kc_real, int kc,
-                         float lambda, E *Qt, int *flags, hipStream_t st);
+                         float lambda, E *Qt, int *flags, double *Cout, hipStream_t st);
 
 // Mp[b*kc + i][:] = (Q_b^T X_b)[i][:]: bf16 reads Q_b from T (as left by
 // launch_gram_q), float32 from Qt.
@@ -41,5 +43,50 @@ hipError_t launch_mprime(const E *X, const E *T, int64_t ldt, int64_t off, const
 template <typename E>
 hipError_t launch_output(const E *T, int64_t ldt, int kw, int kc, const E *Vs, const E *R1t, int64_t Ntok,
                          int64_t n, int64_t c2, const E *bias, E *Y, hipStream_t st);
+
+// Called after each kernel that a multi-kernel launcher enqueues: takes the
+// launch status, records the next timing event (if any) on the stream, and
+// returns the status to go on with.
+struct EventMark {
+    void *const *events = nullptr;
+    int32_t n_events = 0;
+    int32_t *count = nullptr;
+    hipStream_t st = nullptr;
+    hipError_t operator()(hipError_t e) const {
+        if (e != hipSuccess) return e;
+        if (events && count && *count < n_events) {
+            e = hipEventRecord((hipEvent_t)events[*count], st);
+            ++*count;
+        }
+        return e;
+    }
+};
+
+// Buffers of one L update of a further ALS step (als.hip).  kc is the padded
+// correction rank (16..64), k_real the requested one.
+template <typename E> struct AlsArgs {
+    const E *X;          // [B*n][c1]
+    int64_t B, n, c1, c2;
+    int kc, k_real;
+    float lambda;
+    const E *R1t;        // [B][c2][kc]  R' of the previous R update (unscaled)
+    E *R1row;            // [B*kc][c2]   R' by rows (workspace)
+    const E *Wres;       // [c1][c2]     W_res, row-major
+    E *Sp;               // [B*kc][c1]   S'^T = R' W_res^T (workspace)
+    float *H;            // [B][kc][kc]  R' R'^T (workspace)
+    const double *C;     // [B][kc][kc]  Cholesky factor of the previous R update
+    float *Kp;           // [B][kc][kc]  K' (workspace)
+    E *P;                // [B*kc][c1]   coefficient rows of the new L (workspace)
+    int *flags;          // [B]          set to 1 where the L update broke down
+    E *T;                // left-pass buffer; the new L goes to columns [off, off + kc)
+    int64_t ldt, off;
+};
+
+// One L update (Eq. 4) for every instance, as six kernels (transpose of R',
+// S' GEMM, H', K', P, L), each followed by mark().  last = 1: the update is
+// the final one, and the L columns receive alpha X S' Z^-1 (to be multiplied
+// by R' in the output); last = 0: they receive the new L = X S' Z^-1 C^T.
+template <typename E>
+hipError_t launch_als_lupdate(const AlsArgs<E> &a, int last, float alpha, hipStream_t st, const EventMark &mark);
 
 }  // namespace dyra

@@ -441,12 +441,17 @@ bool spd_solve(const double *Gin, int64_t k, double *B, int64_t cols) {
 }  // namespace
 
 dyra_status factorize(const float *W32, int64_t c1, int64_t c2, int32_t r, int32_t k,
-                      double lambda, Factors *out) {
+                      double lambda, Factors *out, const float *R0_in) {
     if (!W32 || !out) return DYRA_ERR_ARG;
     if (c1 <= 0 || c2 <= 0 || r < 0 || k < 0) return DYRA_ERR_ARG;
     if ((int64_t)r + k > std::min(c1, c2)) return DYRA_ERR_ARG;
     if (!(lambda >= 0.0) || !std::isfinite(lambda)) return DYRA_ERR_ARG;
-    const int64_t want = (int64_t)r + k;
+    if (R0_in) {
+        for (int64_t i = 0; i < (int64_t)k * c2; ++i)
+            if (!std::isfinite(R0_in[i])) return DYRA_ERR_NUMERIC;
+    }
+    // singular vectors needed: the static r, plus k for the default R0
+    const int64_t want = (int64_t)r + (R0_in ? 0 : k);
     out->c1 = c1;
     out->c2 = c2;
     out->r = r;
@@ -468,107 +473,114 @@ dyra_status factorize(const float *W32, int64_t c1, int64_t c2, int32_t r, int32
     out->P_L.assign((size_t)(c1 * k), 0.0);
     out->sigma.assign((size_t)want, 0.0);
     out->W_res = W;
-    if (want == 0) return DYRA_OK;
+    if (R0_in) {
+        for (int64_t i = 0; i < (int64_t)k * c2; ++i) out->R0[i] = R0_in[i];
+    }
+    if (want == 0 && !(R0_in && k > 0)) return DYRA_OK;
+    if (want > 0) {
 
-    // Gram matrix on the smaller side: rows of S are the vectors whose inner
-    // products are taken (the columns of W if c2 <= c1, else its rows).
-    const bool right_side = c2 <= c1;
-    const int64_t p = right_side ? c2 : c1;
-    const int64_t q = right_side ? c1 : c2;
-    Vec G((size_t)(p * p));
-    {
-        Vec St;
-        const double *S = W.data();
+        // Gram matrix on the smaller side: rows of S are the vectors whose inner
+        // products are taken (the columns of W if c2 <= c1, else its rows).
+        const bool right_side = c2 <= c1;
+        const int64_t p = right_side ? c2 : c1;
+        const int64_t q = right_side ? c1 : c2;
+        Vec G((size_t)(p * p));
+        {
+            Vec St;
+            const double *S = W.data();
+            if (right_side) {
+                St.resize((size_t)(c2 * c1));
+#pragma omp parallel for schedule(static)
+                for (int64_t j = 0; j < c2; ++j)
+                    for (int64_t i = 0; i < c1; ++i) St[j * c1 + i] = W[i * c2 + j];
+                S = St.data();
+            }
+            gram_rows(S, p, q, G.data());
+        }
+        Vec d(p), e(std::max<int64_t>(p, 1)), beta(std::max<int64_t>(p, 1), 0.0);
+        tridiagonalize(G.data(), p, d.data(), e.data(), beta.data());
+        Vec lam((size_t)want);
+        top_eigenvalues(d.data(), e.data(), p, want, lam.data());
+        Vec Z((size_t)(want * p));
+        tridiag_eigenvectors(d.data(), e.data(), p, lam.data(), want, Z.data());
+        back_transform(G.data(), beta.data(), p, Z.data(), want);
+
+        // Right singular vectors V [c2][want] (column j = v_j).
+        Vec V((size_t)(c2 * want));
         if (right_side) {
-            St.resize((size_t)(c2 * c1));
+            for (int64_t j = 0; j < want; ++j)
+                for (int64_t i = 0; i < c2; ++i) V[i * want + j] = Z[j * p + i];
+        } else {
+            // v_j = W^T u_j / ||W^T u_j||
 #pragma omp parallel for schedule(static)
-            for (int64_t j = 0; j < c2; ++j)
-                for (int64_t i = 0; i < c1; ++i) St[j * c1 + i] = W[i * c2 + j];
-            S = St.data();
-        }
-        gram_rows(S, p, q, G.data());
-    }
-    Vec d(p), e(std::max<int64_t>(p, 1)), beta(std::max<int64_t>(p, 1), 0.0);
-    tridiagonalize(G.data(), p, d.data(), e.data(), beta.data());
-    Vec lam((size_t)want);
-    top_eigenvalues(d.data(), e.data(), p, want, lam.data());
-    Vec Z((size_t)(want * p));
-    tridiag_eigenvectors(d.data(), e.data(), p, lam.data(), want, Z.data());
-    back_transform(G.data(), beta.data(), p, Z.data(), want);
-
-    // Right singular vectors V [c2][want] (column j = v_j).
-    Vec V((size_t)(c2 * want));
-    if (right_side) {
-        for (int64_t j = 0; j < want; ++j)
-            for (int64_t i = 0; i < c2; ++i) V[i * want + j] = Z[j * p + i];
-    } else {
-        // v_j = W^T u_j / ||W^T u_j||
-#pragma omp parallel for schedule(static)
-        for (int64_t j = 0; j < want; ++j) {
-            const double *u = Z.data() + j * p;
-            Vec t((size_t)c2, 0.0);
-            for (int64_t a = 0; a < c1; ++a) {
-                const double ua = u[a];
-                const double *wr = W.data() + a * c2;
-                for (int64_t b = 0; b < c2; ++b) t[b] += ua * wr[b];
-            }
-            double nrm = 0.0;
-            for (int64_t b = 0; b < c2; ++b) nrm += t[b] * t[b];
-            nrm = std::sqrt(nrm);
-            const double inv = nrm > 0.0 ? 1.0 / nrm : 0.0;
-            for (int64_t b = 0; b < c2; ++b) V[b * want + j] = t[b] * inv;
-        }
-        // W^T u / ||W^T u|| loses orthogonality as sigma_j / sigma_0 approaches
-        // the Gram's rounding level; re-orthonormalise those columns (twice)
-        // against all earlier ones so V_s stays an orthonormal row-space basis.
-        const double cut = 1e-4 * std::sqrt(std::max(lam[0], 0.0));
-        for (int64_t j = 0; j < want; ++j) {
-            if (std::sqrt(std::max(lam[j], 0.0)) >= cut) continue;
-            for (int attempt = 0; attempt < 3; ++attempt) {
-                double nrm = 0.0;
-                for (int pass = 0; pass < 2; ++pass) {
-                    for (int64_t i = 0; i < j; ++i) {
-                        double d = 0.0;
-                        for (int64_t b = 0; b < c2; ++b) d += V[b * want + i] * V[b * want + j];
-                        for (int64_t b = 0; b < c2; ++b) V[b * want + j] -= d * V[b * want + i];
-                    }
-                    nrm = 0.0;
-                    for (int64_t b = 0; b < c2; ++b) nrm += V[b * want + j] * V[b * want + j];
-                    nrm = std::sqrt(nrm);
-                    if (nrm > 1e-8) {
-                        for (int64_t b = 0; b < c2; ++b) V[b * want + j] /= nrm;
-                    }
+            for (int64_t j = 0; j < want; ++j) {
+                const double *u = Z.data() + j * p;
+                Vec t((size_t)c2, 0.0);
+                for (int64_t a = 0; a < c1; ++a) {
+                    const double ua = u[a];
+                    const double *wr = W.data() + a * c2;
+                    for (int64_t b = 0; b < c2; ++b) t[b] += ua * wr[b];
                 }
-                if (nrm > 1e-8) break;
-                // a null direction of W: complete the basis from a fixed start vector
-                for (int64_t b = 0; b < c2; ++b)
-                    V[b * want + j] = std::sin(0.7 * (double)(b + 1) * (double)(j + 2 + attempt));
+                double nrm = 0.0;
+                for (int64_t b = 0; b < c2; ++b) nrm += t[b] * t[b];
+                nrm = std::sqrt(nrm);
+                const double inv = nrm > 0.0 ? 1.0 / nrm : 0.0;
+                for (int64_t b = 0; b < c2; ++b) V[b * want + j] = t[b] * inv;
+            }
+            // W^T u / ||W^T u|| loses orthogonality as sigma_j / sigma_0 approaches
+            // the Gram's rounding level; re-orthonormalise those columns (twice)
+            // against all earlier ones so V_s stays an orthonormal row-space basis.
+            const double cut = 1e-4 * std::sqrt(std::max(lam[0], 0.0));
+            for (int64_t j = 0; j < want; ++j) {
+                if (std::sqrt(std::max(lam[j], 0.0)) >= cut) continue;
+                for (int attempt = 0; attempt < 3; ++attempt) {
+                    double nrm = 0.0;
+                    for (int pass = 0; pass < 2; ++pass) {
+                        for (int64_t i = 0; i < j; ++i) {
+                            double d = 0.0;
+                            for (int64_t b = 0; b < c2; ++b) d += V[b * want + i] * V[b * want + j];
+                            for (int64_t b = 0; b < c2; ++b) V[b * want + j] -= d * V[b * want + i];
+                        }
+                        nrm = 0.0;
+                        for (int64_t b = 0; b < c2; ++b) nrm += V[b * want + j] * V[b * want + j];
+                        nrm = std::sqrt(nrm);
+                        if (nrm > 1e-8) {
+                            for (int64_t b = 0; b < c2; ++b) V[b * want + j] /= nrm;
+                        }
+                    }
+                    if (nrm > 1e-8) break;
+                    // a null direction of W: complete the basis from a fixed start vector
+                    for (int64_t b = 0; b < c2; ++b)
+                        V[b * want + j] = std::sin(0.7 * (double)(b + 1) * (double)(j + 2 + attempt));
+                }
             }
         }
-    }
-    // A = W V (= U Sigma); sigma_j = ||W v_j||
-    Vec A((size_t)(c1 * want), 0.0);
+        // A = W V (= U Sigma); sigma_j = ||W v_j||
+        Vec A((size_t)(c1 * want), 0.0);
 #pragma omp parallel for schedule(static)
-    for (int64_t a = 0; a < c1; ++a) {
-        const double *wr = W.data() + a * c2;
-        double *ar = A.data() + a * want;
-        for (int64_t b = 0; b < c2; ++b) {
-            const double wab = wr[b];
-            const double *vb = V.data() + b * want;
-            for (int64_t j = 0; j < want; ++j) ar[j] += wab * vb[j];
+        for (int64_t a = 0; a < c1; ++a) {
+            const double *wr = W.data() + a * c2;
+            double *ar = A.data() + a * want;
+            for (int64_t b = 0; b < c2; ++b) {
+                const double wab = wr[b];
+                const double *vb = V.data() + b * want;
+                for (int64_t j = 0; j < want; ++j) ar[j] += wab * vb[j];
+            }
+        }
+        for (int64_t j = 0; j < want; ++j) {
+            double s = 0.0;
+            for (int64_t a = 0; a < c1; ++a) s += A[a * want + j] * A[a * want + j];
+            out->sigma[j] = std::sqrt(s);
+        }
+        for (int64_t a = 0; a < c1; ++a)
+            for (int64_t j = 0; j < r; ++j) out->A_s[a * r + j] = A[a * want + j];
+        for (int64_t b = 0; b < c2; ++b)
+            for (int64_t j = 0; j < r; ++j) out->V_s[b * r + j] = V[b * want + j];
+        if (!R0_in) {
+            for (int64_t j = 0; j < k; ++j)
+                for (int64_t b = 0; b < c2; ++b) out->R0[j * c2 + b] = V[b * want + r + j];
         }
     }
-    for (int64_t j = 0; j < want; ++j) {
-        double s = 0.0;
-        for (int64_t a = 0; a < c1; ++a) s += A[a * want + j] * A[a * want + j];
-        out->sigma[j] = std::sqrt(s);
-    }
-    for (int64_t a = 0; a < c1; ++a)
-        for (int64_t j = 0; j < r; ++j) out->A_s[a * r + j] = A[a * want + j];
-    for (int64_t b = 0; b < c2; ++b)
-        for (int64_t j = 0; j < r; ++j) out->V_s[b * r + j] = V[b * want + j];
-    for (int64_t j = 0; j < k; ++j)
-        for (int64_t b = 0; b < c2; ++b) out->R0[j * c2 + b] = V[b * want + r + j];
 
     // W_res = W - A_s V_s^T  (§2.1 Eq. 1)
     if (r > 0) {

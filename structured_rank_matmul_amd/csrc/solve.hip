@@ -102,9 +102,11 @@ __device__ __forceinline__ void elim_step(float (&g)[KC], float (&l)[KC], int kc
         fail = fail || bad;
         pk = bad ? 1.f : pk;
         const float rp = __builtin_amdgcn_rcpf(pk);
+        const float rs = __builtin_amdgcn_rsqf(pk);
         const float a = g[K] * rp;   // G rows: C[i][K] / C[K][K]
         const float bt = l[K] * rp;  // token rows: Q[t][K] / C[K][K]
-        l[K] = l[K] * __builtin_amdgcn_rsqf(pk);
+        l[K] = l[K] * rs;
+        g[K] = g[K] * rs;            // C[i][K]; column K of g is not read again
         if constexpr (K + 1 < KC) elim_batch<KC, K, K + 1>(g, l, a, bt);
         elim_step<KC, K + 1>(g, l, kc_real, th, fail);
     }
@@ -113,7 +115,8 @@ __device__ __forceinline__ void elim_step(float (&g)[KC], float (&l)[KC], int kc
 // ---------------------------------------------------------------- bf16 path
 template <int KC>
 __global__ __launch_bounds__(NT) void cholq_kernel(bf16 *__restrict__ T, int64_t ldt, int64_t off, int64_t n,
-                                                   int kc_real, float lambda, int *__restrict__ flags) {
+                                                   int kc_real, float lambda, int *__restrict__ flags,
+                                                   double *__restrict__ Cout) {
     constexpr int GS = 68;        // row stride (floats) of G in LDS
     constexpr int TT = NT;        // tokens per Gram chunk = tokens per workgroup
     constexpr int ST = TT + 8;    // row stride (bf16) of the transposed chunk [feature][token]
@@ -232,13 +235,21 @@ __global__ __launch_bounds__(NT) void cholq_kernel(bf16 *__restrict__ T, int64_t
         }
     }
     if (blockIdx.x == 0 && tid == 0) flags[b] = fail ? 1 : 0;
+    // the Cholesky factor itself (lane i holds row i of C in g[0..i]) for the
+    // L updates of further ALS steps
+    if (Cout && blockIdx.x == 0 && wave == 0 && i < KC) {
+        double *Cr = Cout + ((int64_t)b * KC + i) * KC;
+#pragma unroll
+        for (int m = 0; m < KC; ++m) Cr[m] = m <= i ? (double)g[m] : 0.0;
+    }
     DYRA_PHASE_MARK(4);
 }
 
 // ------------------------------------------------------------- float32 path
 __global__ __launch_bounds__(NT) void gram_q_f32_kernel(float *__restrict__ T, int64_t ldt, int64_t off, int64_t n,
                                                         int64_t npad, int kc_real, int kc, float lambda,
-                                                        float *__restrict__ Qt, int *__restrict__ flags) {
+                                                        float *__restrict__ Qt, int *__restrict__ flags,
+                                                        double *__restrict__ Cout) {
     typedef double AT;
     constexpr int GS = 68;
     __shared__ __align__(16) float Lt[TK * 64];
@@ -318,6 +329,11 @@ __global__ __launch_bounds__(NT) void gram_q_f32_kernel(float *__restrict__ T, i
     }
 #pragma unroll
     for (int q = 0; q < 16; ++q) g[q] = (j > i0 + 4 * q) ? AT(0) : g[q];
+    if (Cout) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            if (i0 + 4 * q < kc && j < kc) Cout[((int64_t)b * kc + i0 + 4 * q) * kc + j] = g[q];
+    }
     __syncthreads();
     // ---- C^-1 by in-place Gauss-Jordan (stays lower-triangular)
     for (int k = 0; k < kc; ++k) {
@@ -591,14 +607,14 @@ __global__ __launch_bounds__(NT) void mprime_tr_kernel(const bf16 *__restrict__ 
 
 template <>
 hipError_t launch_gram_q<bf16>(bf16 *T, int64_t ldt, int64_t off, int64_t B, int64_t n, int64_t npad, int kc_real,
-                               int kc, float lambda, bf16 *, int *flags, hipStream_t st) {
+                               int kc, float lambda, bf16 *, int *flags, double *Cout, hipStream_t st) {
     if (B <= 0) return hipSuccess;
     const dim3 grid((unsigned)((npad + NT - 1) / NT), (unsigned)B);
     switch (kc) {
-    case 16: hipLaunchKernelGGL(cholq_kernel<16>, grid, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda, flags); break;
-    case 32: hipLaunchKernelGGL(cholq_kernel<32>, grid, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda, flags); break;
-    case 48: hipLaunchKernelGGL(cholq_kernel<48>, grid, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda, flags); break;
-    case 64: hipLaunchKernelGGL(cholq_kernel<64>, grid, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda, flags); break;
+    case 16: hipLaunchKernelGGL(cholq_kernel<16>, grid, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda, flags, Cout); break;
+    case 32: hipLaunchKernelGGL(cholq_kernel<32>, grid, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda, flags, Cout); break;
+    case 48: hipLaunchKernelGGL(cholq_kernel<48>, grid, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda, flags, Cout); break;
+    case 64: hipLaunchKernelGGL(cholq_kernel<64>, grid, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda, flags, Cout); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -606,11 +622,11 @@ hipError_t launch_gram_q<bf16>(bf16 *T, int64_t ldt, int64_t off, int64_t B, int
 
 template <>
 hipError_t launch_gram_q<float>(float *T, int64_t ldt, int64_t off, int64_t B, int64_t n, int64_t npad, int kc_real,
-                                int kc, float lambda, float *Qt, int *flags, hipStream_t st) {
+                                int kc, float lambda, float *Qt, int *flags, double *Cout, hipStream_t st) {
     if (B <= 0) return hipSuccess;
     if (kc < 1 || kc > 64) return hipErrorInvalidValue;
     hipLaunchKernelGGL(gram_q_f32_kernel, dim3((unsigned)B), dim3(NT), 0, st, T, ldt, off, n, npad, kc_real, kc,
-                       lambda, Qt, flags);
+                       lambda, Qt, flags, Cout);
     return hipGetLastError();
 }
 

@@ -23,7 +23,8 @@ _DTYPES = {"f32": DYRA_F32, "float32": DYRA_F32, "bf16": DYRA_BF16, "bfloat16": 
 
 # Every symbol include/dyra.h declares.
 EXPORTED = (
-    "dyra_status_str", "dyra_factorize_host", "dyra_prepare", "dyra_plan_destroy", "dyra_plan_info",
+    "dyra_status_str", "dyra_factorize_host", "dyra_prepare", "dyra_prepare_ex", "dyra_plan_destroy",
+    "dyra_plan_info",
     "dyra_workspace_bytes", "dyra_forward", "dyra_forward_ex", "dyra_forward_status", "dyra_dense_ref",
     "dyra_forward_timed", "dyra_stage_name",
 )
@@ -54,6 +55,9 @@ def load() -> ctypes.CDLL:
     L.dyra_factorize_host.restype = ctypes.c_int
     L.dyra_prepare.argtypes = [vp, i64, i64, i32, i32, f32, ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp)]
     L.dyra_prepare.restype = ctypes.c_int
+    L.dyra_prepare_ex.argtypes = [vp, i64, i64, i32, i32, f32, ctypes.c_int, ctypes.c_int, vp, i32,
+                                  ctypes.POINTER(vp)]
+    L.dyra_prepare_ex.restype = ctypes.c_int
     L.dyra_plan_destroy.argtypes = [vp]
     L.dyra_plan_destroy.restype = None
     L.dyra_plan_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i32),
@@ -159,6 +163,25 @@ def dyra_prepare(W: np.ndarray, r: int, k: int, lam: float = 0.0, dtype="bf16", 
     h = ctypes.c_void_p()
     st = load().dyra_prepare(W.ctypes.data, c1, c2, int(r), int(k), float(lam), code, int(device), ctypes.byref(h))
     _check(st, "dyra_prepare")
+    return Plan(h.value, c1, c2, int(r), int(k), float(lam), code, int(device))
+
+
+def dyra_prepare_ex(W: np.ndarray, r: int, k: int, lam: float = 0.0, dtype="bf16", device: int = 0,
+                    R0: Optional[np.ndarray] = None, als_half_steps: int = 2) -> Plan:
+    """dyra_prepare with a given R^(0) ([k, c2], e.g. Gaussian) and the number of
+    single ALS updates (2 = t 1, 3 = t 1.5, 4 = t 2)."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    c1, c2 = W.shape
+    code = _dtype_code(dtype)
+    r0 = None
+    if R0 is not None:
+        r0 = np.ascontiguousarray(R0, dtype=np.float32)
+        if r0.shape != (int(k), c2):
+            raise ValueError(f"R0 must be [{k}, {c2}]")
+    h = ctypes.c_void_p()
+    st = load().dyra_prepare_ex(W.ctypes.data, c1, c2, int(r), int(k), float(lam), code, int(device),
+                                r0.ctypes.data if r0 is not None else None, int(als_half_steps), ctypes.byref(h))
+    _check(st, "dyra_prepare_ex")
     return Plan(h.value, c1, c2, int(r), int(k), float(lam), code, int(device))
 
 

@@ -409,3 +409,73 @@ def test_fused_alpha_scales_only_the_correction(alpha):
     np.testing.assert_allclose(yb - ya, np.broadcast_to(b, ya.shape), atol=1e-12)
     # the correction really is there: alpha changes the output
     assert orc.rel_fro(y1, y0) > 1e-3
+
+
+# ------------------------------------------------------------------ §3.3 further ALS steps, Gaussian R0
+
+def _proj(A):
+    """Orthogonal projector onto the column space of A (full column rank), by QR."""
+    Qm, _ = np.linalg.qr(A)
+    return Qm @ Qm.T
+
+
+@pytest.mark.parametrize("half_steps", [2, 3, 4, 5, 6])
+@pytest.mark.parametrize("gaussian_r0", [False, True])
+def test_als_steps_are_block_power_iteration(half_steps, gaussian_r0):
+    """At lambda = 0 every ALS update is an exact least-squares fit, so with
+    P = X W_res the alternation from R0 is block power iteration: after 2h
+    updates L R is P projected onto the columns of (P P^T)^(h-1) P R0^T, after
+    2h + 1 updates P projected on the right onto the columns of (P^T P)^h R0^T.
+    The projectors come from QR here, not from the oracle's solves."""
+    c1, c2, r_w, r_c, n = 14, 17, 3, 4, 12
+    W = synth.random_weight(c1, c2, 110).astype(np.float64)
+    X = gaussian((n, c1), 111) * np.exp(gaussian((1, c1), 112))
+    R0 = gaussian((r_c, c2), 113) if gaussian_r0 else None
+    plan = orc.offline_preparation(W, r_w, r_c, 0.0, R0=R0)
+    P = X @ plan.W_res
+    R0 = plan.R0
+    h = half_steps // 2
+    if half_steps % 2 == 0:
+        K = np.linalg.matrix_power(P @ P.T, h - 1) @ P @ R0.T
+        corr = _proj(K) @ P
+    else:
+        K = np.linalg.matrix_power(P.T @ P, h) @ R0.T
+        corr = P @ _proj(K)
+    Y = orc.inference(X, 1, n, plan, half_steps=half_steps)
+    np.testing.assert_allclose(Y - X @ plan.W_hat, corr, atol=1e-8 * np.linalg.norm(P))
+
+
+def test_more_als_steps_never_increase_the_error_and_reach_the_floor_from_gaussian_r0():
+    """Fig. 2 / Appendix E.3 setting: Gaussian R^(0); at lambda = 0 the error of
+    the correction falls with every update and approaches the Eckart-Young floor
+    of the realised residual product, at the rate of block power iteration (the
+    ratio of the (r_c+1)-th to the r_c-th singular value per two updates; 0.66 to
+    0.89 for these instances, so 80 updates)."""
+    c1, c2, r_w, r_c, B, n = 20, 26, 4, 3, 3, 15
+    W = synth.random_weight(c1, c2, 114).astype(np.float64)
+    X = gaussian((B * n, c1), 115) * np.exp(gaussian((1, c1), 116))
+    plan = orc.offline_preparation(W, r_w, r_c, 0.0, R0=gaussian((r_c, c2), 117))
+    for b in range(B):
+        Xb = X[b * n:(b + 1) * n]
+        P = Xb @ plan.W_res
+        errs = [np.linalg.norm(orc.inference(Xb, 1, n, plan, half_steps=h) - Xb @ plan.W_hat - P)
+                for h in range(2, 81)]
+        assert all(e2 <= e1 * (1 + 1e-9) for e1, e2 in zip(errs, errs[1:]))
+        assert errs[-1] <= orc.optimal_rank_error(P, r_c) * (1 + 1e-6)
+        assert errs[0] > orc.optimal_rank_error(P, r_c) * (1 + 1e-3)   # one step is not yet optimal
+
+
+def test_half_steps_with_ridge_differ_from_plain_and_keep_bias_alpha_semantics():
+    """With lambda > 0 the extra updates still change the result, and bias and
+    alpha act on the final product exactly as for one step."""
+    c1, c2, r_w, r_c, n = 16, 12, 3, 3, 10
+    W = synth.random_weight(c1, c2, 118).astype(np.float64)
+    X = gaussian((2 * n, c1), 119) * np.exp(gaussian((1, c1), 120))
+    b = gaussian((1, c2), 121)[0]
+    plan = orc.offline_preparation(W, r_w, r_c, 0.3)
+    y2 = orc.inference(X, 2, n, plan)
+    y4 = orc.inference(X, 2, n, plan, half_steps=4)
+    assert orc.rel_fro(y4, y2) > 1e-6
+    y0 = orc.inference(X, 2, n, plan, alpha=0.0)
+    y4ab = orc.inference(X, 2, n, plan, bias=b, alpha=0.5, half_steps=4)
+    np.testing.assert_allclose(y4ab - b[None, :] - y0, 0.5 * (y4 - y0), atol=1e-11)
