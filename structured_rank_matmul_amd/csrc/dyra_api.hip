@@ -83,11 +83,11 @@ Path path_for(const dyra_plan *p, int64_t n) {
 //   C      float64 [B][kc][kc]   Cholesky factors of the last R update
 //   R1row  [B*kc][c2]            R' by rows
 //   Sp     [B*kc][c1]            S'^T = R' W_res^T
-//   H, Kp  float32 [B][kc][kc]   R' R'^T and the L update's coefficients
-//   P      [B*kc][c1]            coefficient rows of the new L
+//   H      float32 [8][B][kc][kc] partial sums of R' R'^T
+//   Kp     float32 [B][kc][kc]   the L update's coefficients
 //   dual   decode workspace      (n <= 16 or n < k only)
 struct Layout {
-    size_t flags, T, Qt, Mp, R1t, C, R1row, Sp, H, Kp, P, dual, total;
+    size_t flags, T, Qt, Mp, R1t, C, R1row, Sp, H, Kp, dual, total;
     int64_t npad;
 };
 
@@ -119,11 +119,9 @@ Layout workspace_layout(const dyra_plan *p, int64_t B, int64_t n) {
             L.Sp = off;
             off += align_up(es * B * p->kc * p->c1);
             L.H = off;
-            off += align_up(sizeof(float) * kk);
+            off += align_up(sizeof(float) * kk * dyra::kAlsGramSplit);
             L.Kp = off;
             off += align_up(sizeof(float) * kk);
-            L.P = off;
-            off += align_up(es * B * p->kc * p->c1);
         }
     } else if (path_for(p, n) == Path::Dual) {
         L.dual = off;
@@ -152,7 +150,7 @@ std::vector<const char *> stage_list(const dyra_plan *p, int64_t n) {
     }
     std::vector<const char *> v = {"left", "gram_q", "mprime", "right"};
     for (int h = 2; h < p->half_steps; h += 2) {
-        for (const char *st : {"als_transpose", "als_s", "als_gram", "als_coef", "als_apply", "als_lupdate"})
+        for (const char *st : {"als_transpose", "als_s", "als_gram", "als_coef", "als_lupdate"})
             v.push_back(st);
         if (h + 1 < p->half_steps)
             for (const char *st : {"gram_q", "mprime", "right"}) v.push_back(st);
@@ -213,7 +211,7 @@ dyra_status run_forward(const E *X, int64_t B, int64_t n, const dyra_plan *p, co
                 const bool last_l = h + 1 == p->half_steps;
                 const dyra::AlsArgs<E> a{X, B, n, p->c1, p->c2, p->kc, p->k, p->lambda, R1t, (E *)(ws + L.R1row),
                                          (const E *)p->Wres, (E *)(ws + L.Sp), (float *)(ws + L.H), Cf,
-                                         (float *)(ws + L.Kp), (E *)(ws + L.P), flags, T, ldt, p->kw};
+                                         (float *)(ws + L.Kp), flags, T, ldt, p->kw};
                 if ((s = hip_status(dyra::launch_als_lupdate<E>(a, last_l ? 1 : 0, alpha, st, em))) != DYRA_OK)
                     return s;
                 if (last_l) break;

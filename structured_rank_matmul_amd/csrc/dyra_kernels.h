@@ -62,6 +62,9 @@ struct EventMark {
     }
 };
 
+// Column ranges over which the Gram matrix R' R'^T of an L update is split.
+constexpr int kAlsGramSplit = 8;
+
 // Buffers of one L update of a further ALS step (als.hip).  kc is the padded
 // correction rank (16..64), k_real the requested one.
 template <typename E> struct AlsArgs {
@@ -73,19 +76,18 @@ template <typename E> struct AlsArgs {
     E *R1row;            // [B*kc][c2]   R' by rows (workspace)
     const E *Wres;       // [c1][c2]     W_res, row-major
     E *Sp;               // [B*kc][c1]   S'^T = R' W_res^T (workspace)
-    float *H;            // [B][kc][kc]  R' R'^T (workspace)
+    float *H;            // [kAlsGramSplit][B][kc][kc]  partial sums of R' R'^T (workspace)
     const double *C;     // [B][kc][kc]  Cholesky factor of the previous R update
     float *Kp;           // [B][kc][kc]  K' (workspace)
-    E *P;                // [B*kc][c1]   coefficient rows of the new L (workspace)
     int *flags;          // [B]          set to 1 where the L update broke down
     E *T;                // left-pass buffer; the new L goes to columns [off, off + kc)
     int64_t ldt, off;
 };
 
-// One L update (Eq. 4) for every instance, as six kernels (transpose of R',
-// S' GEMM, H', K', P, L), each followed by mark().  last = 1: the update is
-// the final one, and the L columns receive alpha X S' Z^-1 (to be multiplied
-// by R' in the output); last = 0: they receive the new L = X S' Z^-1 C^T.
+// One L update (Eq. 4) for every instance, as five kernels (transpose of R',
+// S' GEMM, H', K', L), each followed by mark().  last = 1: the update is the
+// final one, and the L columns receive alpha X S' Z^-1 (to be multiplied by
+// R' in the output); last = 0: they receive the new L = X S' Z^-1 C^T.
 template <typename E>
 hipError_t launch_als_lupdate(const AlsArgs<E> &a, int last, float alpha, hipStream_t st, const EventMark &mark);
 

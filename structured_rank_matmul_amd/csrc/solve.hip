@@ -32,6 +32,7 @@
 //   mprime (float32)  the same product from Q_b^T stored token-contiguous.
 #include "dyra_kernels.h"
 
+#include "elim.h"
 #include "mfma_tile.h"
 
 namespace dyra {
@@ -64,51 +65,6 @@ __device__ __forceinline__ void load_transposed(const E *src, int64_t ld, int64_
                   : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int q = 0; q < VEC; ++q) dst[(j0 + q) * ST + tok] = v.e[q];
-    }
-}
-
-__device__ __forceinline__ float bcast(float v, int lane) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
-}
-
-// One elimination step of the lane-per-row factorisation (step K, pivot row
-// K held by lane K).  Lane i holds row i of the trailing matrix in g and its
-// token row in l.  The pivot row's entries are broadcast to SGPRs in batches
-// of 8 ahead of the FMAs that use them.
-template <int KC, int K, int M0>
-__device__ __forceinline__ void elim_batch(float (&g)[KC], float (&l)[KC], float a, float bt) {
-    constexpr int CNT = (KC - M0) < 8 ? (KC - M0) : 8;
-    float sv[CNT];
-#pragma unroll
-    for (int u = 0; u < CNT; ++u) sv[u] = bcast(g[M0 + u], K);  // trailing row K = C[m][K] C[K][K]
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < CNT; ++u) {
-        g[M0 + u] = fmaf(-a, sv[u], g[M0 + u]);
-        l[M0 + u] = fmaf(-bt, sv[u], l[M0 + u]);
-    }
-    // the batch's FMAs complete here, so its broadcasts die here (otherwise
-    // the compiler may defer the token-row FMAs and spill the SGPRs)
-#pragma unroll
-    for (int u = 0; u < CNT; ++u) asm volatile("" : "+v"(g[M0 + u]), "+v"(l[M0 + u]));
-    if constexpr (M0 + 8 < KC) elim_batch<KC, K, M0 + 8>(g, l, a, bt);
-}
-
-template <int KC, int K>
-__device__ __forceinline__ void elim_step(float (&g)[KC], float (&l)[KC], int kc_real, float th, bool &fail) {
-    if constexpr (K < KC) {
-        float pk = bcast(g[K], K);
-        const bool bad = K < kc_real && !(pk > th);  // padding pivots are 1
-        fail = fail || bad;
-        pk = bad ? 1.f : pk;
-        const float rp = __builtin_amdgcn_rcpf(pk);
-        const float rs = __builtin_amdgcn_rsqf(pk);
-        const float a = g[K] * rp;   // G rows: C[i][K] / C[K][K]
-        const float bt = l[K] * rp;  // token rows: Q[t][K] / C[K][K]
-        l[K] = l[K] * rs;
-        g[K] = g[K] * rs;            // C[i][K]; column K of g is not read again
-        if constexpr (K + 1 < KC) elim_batch<KC, K, K + 1>(g, l, a, bt);
-        elim_step<KC, K + 1>(g, l, kc_real, th, fail);
     }
 }
 
