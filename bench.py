@@ -130,6 +130,10 @@ def main():
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--no-flops-matched", action="store_true",
                     help="skip the FLOPs-matched static baseline (a second prepare and timing per layer)")
+    ap.add_argument("--no-als-steps", action="store_true",
+                    help="skip the t = 1.5 / t = 2 ALS measurement (two more prepares and timings per layer)")
+    ap.add_argument("--no-ns", action="store_true",
+                    help="skip the Newton-Schulz SPD-solve measurement (two more prepares and timings per layer)")
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run three forward steps and a calibration copy only (for rocprofv3 --pmc runs)")
@@ -315,6 +319,58 @@ def main():
             plan_s.close()
         matched["sample_instances"] = sample
 
+    # ---- further ALS steps (§3.3 ablation over t): error and time of the same
+    # layers at t = 1 (Algorithm 1), 1.5 and 2, same sampled instances
+    als_steps = None
+    if not args.no_als_steps:
+        als_steps = {}
+        sample = [0, B // 2, B - 1]
+        rows = np.concatenate([np.arange(b * n, (b + 1) * n) for b in sample])
+        for L in layers:
+            spec = L["spec"]
+            Xs = L["X"].exact[rows]
+            exact = Xs @ L["W"].astype(np.float64)
+            rec = {}
+            for hs in (2, 3, 4):
+                plan_h = L["plan"] if hs == 2 else dyra.dyra_prepare_ex(L["W"], spec.r, spec.k, 0.0, w.dtype, 0,
+                                                                        als_half_steps=hs)
+                ws_h = L["ws"] if hs == 2 else dyra.alloc_workspace(plan_h, B, n)
+                yh = torch.empty_like(L["y"])
+                t_h = time_loop(lambda: dyra.dyra_forward(L["xd"], B, n, plan_h, yh, ws_h, stream), reps, 3, stream)
+                e_h = orc.rel_fro(yh.float().cpu().numpy().astype(np.float64)[rows], exact)
+                rec[f"t={hs / 2:g}"] = {"half_steps": hs, "e": round(e_h, 5), "t_us": round(t_h * 1e6, 2)}
+                if hs != 2:
+                    plan_h.close()
+            als_steps[spec.name] = rec
+            log(f"{spec.name}: ALS steps " + "  ".join(f"{k_}: e {v['e']:.4f} t {v['t_us']:.1f} us"
+                                                      for k_, v in rec.items()))
+        als_steps["sample_instances"] = sample
+
+    # ---- §2.4's Newton-Schulz SPD solve in place of the Cholesky one: error
+    # and time at 12 and 24 steps, same sampled instances
+    ns = None
+    if not args.no_ns:
+        ns = {}
+        sample = [0, B // 2, B - 1]
+        rows = np.concatenate([np.arange(b * n, (b + 1) * n) for b in sample])
+        for L in layers:
+            spec = L["spec"]
+            Xs = L["X"].exact[rows]
+            exact = Xs @ L["W"].astype(np.float64)
+            rec = {}
+            for it in (12, 24):
+                plan_h = dyra.dyra_prepare_ex(L["W"], spec.r, spec.k, 0.0, w.dtype, 0, ns_iters=it)
+                ws_h = dyra.alloc_workspace(plan_h, B, n)
+                yh = torch.empty_like(L["y"])
+                t_h = time_loop(lambda: dyra.dyra_forward(L["xd"], B, n, plan_h, yh, ws_h, stream), reps, 3, stream)
+                e_h = orc.rel_fro(yh.float().cpu().numpy().astype(np.float64)[rows], exact)
+                rec[f"ns_iters={it}"] = {"e": round(e_h, 5), "t_us": round(t_h * 1e6, 2)}
+                plan_h.close()
+            ns[spec.name] = rec
+            log(f"{spec.name}: Newton-Schulz " + "  ".join(f"{k_}: e {v['e']:.4f} t {v['t_us']:.1f} us"
+                                                         for k_, v in rec.items()))
+        ns["sample_instances"] = sample
+
     cpu = None
     if not args.no_cpu_baseline:
         plans_orc = [L.get("orc") or orc.offline_preparation(L["W"].astype(np.float64), L["spec"].r,
@@ -349,6 +405,8 @@ def main():
         "stage_us": {L["spec"].name: {k: round(v * 1e6, 2) for k, v in L["stages"].items()} for L in layers},
         "rel_fro_error": parity,
         "flops_matched_static": matched,
+        "als_steps": als_steps,
+        "newton_schulz": ns,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -97,8 +97,9 @@ dyra_status dyra_prepare(const float *W, int64_t c1, int64_t c2, int32_t r, int3
                          float lambda, dyra_dtype dtype, int device, dyra_plan **plan_out);
 
 /*
- * dyra_prepare with the method's two further knobs (§2.2 Fig. 2 / Appendix E.3
- * Gaussian R^(0); §3.3 ablation over the ALS iteration count t):
+ * dyra_prepare with the method's further knobs (§2.2 Fig. 2 / Appendix E.3
+ * Gaussian R^(0); §3.3 ablation over the ALS iteration count t; §2.4
+ * Newton-Schulz SPD solve):
  *
  * R0              host, float32, row-major [k][c2], caller-owned, not retained;
  *                 used as R^(0) in P_L = W_res R0^T (R0 R0^T + lambda I)^-1
@@ -110,6 +111,14 @@ dyra_status dyra_prepare(const float *W, int64_t c1, int64_t c2, int32_t r, int3
  *                 dyra_prepare's choice), 3 = t 1.5 (L, R, L), 4 = t 2, up to 8;
  *                 DYRA_ERR_ARG outside [2, 8].  The output is the product of the
  *                 last L and the last R.  Ignored when k = 0.
+ * ns_iters        0: the SPD system of Eq. 5 is solved by Cholesky (§2.4's
+ *                 choice for small r).  1..64: by that many steps of the
+ *                 coupled Newton-Schulz iteration for G^-1/2 (§2.4's choice for
+ *                 large r): c = ||G||_F, Y = G / c, Z = I, T = (3I - Z Y) / 2,
+ *                 Y <- Y T, Z <- T Z, F = Z / sqrt(c), Q = L1 F.  Requires
+ *                 als_half_steps = 2 (DYRA_ERR_ARG otherwise).  An instance
+ *                 whose F is not finite is flagged (dyra_forward_status) and
+ *                 gets no correction.  The dual form does not use it.
  *
  * A plan with als_half_steps > 2 also holds W_res untransposed ([c1][c2]) and
  * needs a larger workspace; dyra_forward runs the extra steps for instances of
@@ -118,7 +127,7 @@ dyra_status dyra_prepare(const float *W, int64_t c1, int64_t c2, int32_t r, int3
  */
 dyra_status dyra_prepare_ex(const float *W, int64_t c1, int64_t c2, int32_t r, int32_t k, float lambda,
                             dyra_dtype dtype, int device, const float *R0, int32_t als_half_steps,
-                            dyra_plan **plan_out);
+                            int32_t ns_iters, dyra_plan **plan_out);
 
 /* Releases a plan and its device memory.  NULL is ignored. */
 void dyra_plan_destroy(dyra_plan *plan);

@@ -1,4 +1,4 @@
 """CPU oracle for DyRA (test infrastructure only; see dyra_oracle)."""
 from .dyra_oracle import (OraclePlan, als, dense_product, factors_instance, inference,  # noqa: F401
-                          inference_instance, offline_preparation, optimal_rank_error, rel_fro,
-                          right_factor, truncated_svd, weight_only)
+                          inference_instance, newton_schulz_inv_sqrt, offline_preparation, optimal_rank_error,
+                          rel_fro, right_factor, right_factor_ns, truncated_svd, weight_only)

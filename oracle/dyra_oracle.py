@@ -123,8 +123,41 @@ def right_factor(L1: np.ndarray, X: np.ndarray, W_res: np.ndarray, lam: float) -
     return np.linalg.solve(gram, rhs)
 
 
+def newton_schulz_inv_sqrt(G: np.ndarray, iters: int) -> np.ndarray:
+    """G^-1/2 of an SPD matrix by the coupled Newton-Schulz iteration.
+
+    §2.4 names a Newton-Schulz iterative solver for the r x r SPD system when r
+    is large (matrix products instead of a sequential factorisation) and fixes
+    nothing else.  Reading taken: the coupled iteration for the inverse square
+    root, scaled by the Frobenius norm c = ||G||_F so that G / c has its
+    eigenvalues in (0, 1]:
+        Y_0 = G / c,  Z_0 = I,
+        T_k = (3 I - Z_k Y_k) / 2,  Y_{k+1} = Y_k T_k,  Z_{k+1} = T_k Z_k,
+    Z_k -> (G / c)^-1/2, returned as Z_iters / sqrt(c).  Any F with F F^T = G^-1
+    gives the same correction L F F^T L^T X W_res as the solve of Eq. 5.
+    """
+    G = np.asarray(G, dtype=np.float64)
+    k = G.shape[0]
+    c = np.linalg.norm(G)
+    Y = G / c
+    Z = np.eye(k)
+    for _ in range(iters):
+        Tk = 0.5 * (3.0 * np.eye(k) - Z @ Y)
+        Y, Z = Y @ Tk, Tk @ Z
+    return Z / np.sqrt(c)
+
+
+def right_factor_ns(L1: np.ndarray, X: np.ndarray, W_res: np.ndarray, lam: float, iters: int) -> np.ndarray:
+    """R^(1) of Eq. 5 with G^-1 replaced by F F, F the Newton-Schulz G^-1/2
+    after `iters` steps (newton_schulz_inv_sqrt); (L1^T X) W_res in the
+    algorithm's order."""
+    r_c = L1.shape[1]
+    F = newton_schulz_inv_sqrt(L1.T @ L1 + lam * np.eye(r_c), iters)
+    return F @ (F @ ((L1.T @ X) @ W_res))
+
+
 def inference_instance(X: np.ndarray, plan: OraclePlan, bias: Optional[np.ndarray] = None,
-                       alpha: float = 1.0, half_steps: int = 2) -> np.ndarray:
+                       alpha: float = 1.0, half_steps: int = 2, ns_iters: int = 0) -> np.ndarray:
     """Algorithm 1, procedure Inference, for one instance X [n, c1].
 
     line 10: Y_base <- X W_hat
@@ -135,7 +168,8 @@ def inference_instance(X: np.ndarray, plan: OraclePlan, bias: Optional[np.ndarra
     (bias b [c2] added to every token row; alpha weights the correction only).
     half_steps > 2 continues the alternation of Eq. 4 / Eq. 5 from there (the
     §3.3 ablation over the iteration count: 3 = t 1.5, 4 = t 2) and uses the
-    product of the last L and the last R.
+    product of the last L and the last R.  ns_iters > 0 solves line 12 with the
+    Newton-Schulz G^-1/2 of §2.4 instead (one ALS step only).
     """
     X = np.asarray(X, dtype=np.float64)
     Y_base = X @ plan.W_hat
@@ -143,6 +177,11 @@ def inference_instance(X: np.ndarray, plan: OraclePlan, bias: Optional[np.ndarra
         Y_base = Y_base + np.asarray(bias, dtype=np.float64)[None, :]
     if plan.r_c == 0:
         return Y_base
+    if ns_iters > 0:
+        if half_steps != 2:
+            raise ValueError("the Newton-Schulz solve is taken for one ALS step only")
+        L1 = X @ plan.P_L
+        return Y_base + alpha * (L1 @ right_factor_ns(L1, X, plan.W_res, plan.lam, ns_iters))
     if half_steps == 2:
         L1 = X @ plan.P_L
         R1 = right_factor(L1, X, plan.W_res, plan.lam)
@@ -152,13 +191,13 @@ def inference_instance(X: np.ndarray, plan: OraclePlan, bias: Optional[np.ndarra
 
 
 def inference(X: np.ndarray, B: int, n: int, plan: OraclePlan, bias: Optional[np.ndarray] = None,
-              alpha: float = 1.0, half_steps: int = 2) -> np.ndarray:
+              alpha: float = 1.0, half_steps: int = 2, ns_iters: int = 0) -> np.ndarray:
     """Algorithm 1 Inference over B independent instances of n tokens.
 
     X is [B*n, c1] with instance b in rows [b*n, (b+1)*n).  The paper solves the
     r x r system "for each batch instance" (§2.4), so every instance gets its
     own L1, R1.  bias / alpha: §2.4's fused output; half_steps: further ALS
-    updates (see inference_instance).
+    updates; ns_iters: the Newton-Schulz solve (see inference_instance).
     """
     X = np.asarray(X, dtype=np.float64)
     if X.shape[0] != B * n:
@@ -168,7 +207,7 @@ def inference(X: np.ndarray, B: int, n: int, plan: OraclePlan, bias: Optional[np
     Y = np.empty((B * n, plan.W.shape[1]))
     for b in range(B):
         rows = slice(b * n, (b + 1) * n)
-        Y[rows] = inference_instance(X[rows], plan, bias, alpha, half_steps)
+        Y[rows] = inference_instance(X[rows], plan, bias, alpha, half_steps, ns_iters)
     return Y
 
 

@@ -24,6 +24,7 @@ struct dyra_plan {
     int32_t kw, kc;   // padded: kw = r rounded up to 32, kc = k rounded up to 16
     float lambda;
     int32_t half_steps;  // single ALS updates: 2 = Algorithm 1 (t = 1), 3 = t 1.5, 4 = t 2, ...
+    int32_t ns_iters;    // 0: Cholesky SPD solve; > 0: that many Newton-Schulz steps (§2.4)
     void *Aext;       // [kw + kc][c1]: rows 0..r-1 = A_s columns, rows kw..kw+k-1 = P_L columns
     void *Vs;         // [c2][kw]: V_s
     void *Wres_t;     // [c2][c1]: W_res transposed
@@ -38,6 +39,7 @@ constexpr size_t kAlign = 256;
 constexpr int kMaxCorrection = 64;
 constexpr int kMaxDualTokens = 16;
 constexpr int kMaxHalfSteps = 8;
+constexpr int kMaxNsIters = 64;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -85,9 +87,11 @@ Path path_for(const dyra_plan *p, int64_t n) {
 //   Sp     [B*kc][c1]            S'^T = R' W_res^T
 //   H      float32 [8][B][kc][kc] partial sums of R' R'^T
 //   Kp     float32 [B][kc][kc]   the L update's coefficients
+//   with the Newton-Schulz solve (ns_iters > 0):
+//   F      float32 [B][kc][kc]   G^-1/2 per instance
 //   dual   decode workspace      (n <= 16 or n < k only)
 struct Layout {
-    size_t flags, T, Qt, Mp, R1t, C, R1row, Sp, H, Kp, dual, total;
+    size_t flags, T, Qt, Mp, R1t, C, R1row, Sp, H, Kp, F, dual, total;
     int64_t npad;
 };
 
@@ -110,6 +114,10 @@ Layout workspace_layout(const dyra_plan *p, int64_t B, int64_t n) {
         off += align_up(es * B * p->kc * p->c1);
         L.R1t = off;
         off += align_up(es * B * p->c2 * p->kc);
+        if (p->ns_iters > 0) {
+            L.F = off;
+            off += align_up(sizeof(float) * (size_t)B * p->kc * p->kc);
+        }
         if (p->half_steps > 2) {
             const size_t kk = (size_t)B * p->kc * p->kc;
             L.C = off;
@@ -148,7 +156,15 @@ std::vector<const char *> stage_list(const dyra_plan *p, int64_t n) {
     case Path::Static: return {"left", "output"};
     case Path::Primal: break;
     }
-    std::vector<const char *> v = {"left", "gram_q", "mprime", "right"};
+    std::vector<const char *> v = {"left"};
+    if (p->ns_iters > 0) {
+        v.push_back("ns_factor");
+        v.push_back("ns_apply");
+    } else {
+        v.push_back("gram_q");
+    }
+    v.push_back("mprime");
+    v.push_back("right");
     for (int h = 2; h < p->half_steps; h += 2) {
         for (const char *st : {"als_transpose", "als_s", "als_gram", "als_coef", "als_lupdate"})
             v.push_back(st);
@@ -192,10 +208,18 @@ dyra_status run_forward(const E *X, int64_t B, int64_t n, const dyra_plan *p, co
             // R' = M' W_res (times alpha when it is the last update)
             auto r_update = [&](float alpha_r) -> dyra_status {
                 dyra_status t;
-                if ((t = hip_status(dyra::launch_gram_q<E>(T, ldt, p->kw, B, n, L.npad, p->k, p->kc, p->lambda, Qt,
-                                                           flags, Cf, st))) != DYRA_OK)
-                    return t;
-                if ((t = mark()) != DYRA_OK) return t;
+                if (p->ns_iters > 0) {
+                    if ((t = hip_status(dyra::launch_ns_solve<E>(T, ldt, p->kw, B, n, L.npad, p->k, p->kc, p->lambda,
+                                                                 p->ns_iters, (float *)(ws + L.F), flags,
+                                                                 p->dtype == DYRA_F32 ? (float *)Qt : nullptr, st,
+                                                                 em))) != DYRA_OK)
+                        return t;
+                } else {
+                    if ((t = hip_status(dyra::launch_gram_q<E>(T, ldt, p->kw, B, n, L.npad, p->k, p->kc, p->lambda,
+                                                               Qt, flags, Cf, st))) != DYRA_OK)
+                        return t;
+                    if ((t = mark()) != DYRA_OK) return t;
+                }
                 if ((t = hip_status(dyra::launch_mprime<E>(X, T, ldt, p->kw, Qt, B, n, L.npad, p->c1, p->kc, Mp,
                                                            st))) != DYRA_OK)
                     return t;
@@ -290,17 +314,19 @@ const char *dyra_status_str(dyra_status s) {
 
 dyra_status dyra_prepare(const float *W, int64_t c1, int64_t c2, int32_t r, int32_t k, float lambda,
                          dyra_dtype dtype, int device, dyra_plan **plan_out) {
-    return dyra_prepare_ex(W, c1, c2, r, k, lambda, dtype, device, nullptr, 2, plan_out);
+    return dyra_prepare_ex(W, c1, c2, r, k, lambda, dtype, device, nullptr, 2, 0, plan_out);
 }
 
 dyra_status dyra_prepare_ex(const float *W, int64_t c1, int64_t c2, int32_t r, int32_t k, float lambda,
-                            dyra_dtype dtype, int device, const float *R0, int32_t als_half_steps,
+                            dyra_dtype dtype, int device, const float *R0, int32_t als_half_steps, int32_t ns_iters,
                             dyra_plan **plan_out) {
     if (!plan_out) return DYRA_ERR_ARG;
     *plan_out = nullptr;
     if (dtype != DYRA_BF16 && dtype != DYRA_F32) return DYRA_ERR_DTYPE;
     if (!W || c1 <= 0 || c2 <= 0 || r < 0 || k < 0) return DYRA_ERR_ARG;
     if (als_half_steps < 2 || als_half_steps > kMaxHalfSteps) return DYRA_ERR_ARG;
+    if (ns_iters < 0 || ns_iters > kMaxNsIters) return DYRA_ERR_ARG;
+    if (ns_iters > 0 && als_half_steps > 2) return DYRA_ERR_ARG;  // one ALS step with the Newton-Schulz solve
     if ((int64_t)r + k > std::min(c1, c2)) return DYRA_ERR_ARG;
     if (!(lambda >= 0.f) || !std::isfinite(lambda)) return DYRA_ERR_ARG;
     if (c1 % 32 != 0 || c2 % 32 != 0) return DYRA_ERR_SHAPE;
@@ -338,6 +364,7 @@ dyra_status dyra_prepare_ex(const float *W, int64_t c1, int64_t c2, int32_t r, i
     p->kc = kc;
     p->lambda = lambda;
     p->half_steps = k > 0 ? als_half_steps : 2;
+    p->ns_iters = k > 0 ? ns_iters : 0;
     int prev = -1;
     (void)hipGetDevice(&prev);
     if (hipSetDevice(device) != hipSuccess) {

@@ -91,4 +91,15 @@ template <typename E> struct AlsArgs {
 template <typename E>
 hipError_t launch_als_lupdate(const AlsArgs<E> &a, int last, float alpha, hipStream_t st, const EventMark &mark);
 
+// §2.4's Newton-Schulz alternative to launch_gram_q (ns.hip): G = L1^T L1 +
+// lambda I per instance, F = G^-1/2 by `iters` coupled Newton-Schulz steps
+// (F [B][kc][kc] float32, workspace), then Q = L1 F in place in T's columns
+// [off, off + kc) (float32 plans also fill Qt as launch_gram_q does).
+// flags[b] = 1 where F is not finite (the correction is then dropped).  Two
+// kernels, each followed by mark().
+template <typename E>
+hipError_t launch_ns_solve(E *T, int64_t ldt, int64_t off, int64_t B, int64_t n, int64_t npad, int kc_real, int kc,
+                           float lambda, int iters, float *F, int *flags, float *Qt, hipStream_t st,
+                           const EventMark &mark);
+
 }  // namespace dyra

@@ -1,0 +1,228 @@
+// Newton-Schulz SPD solve of the per-instance correction (gfx950).
+//
+// "DyRA: Dynamic Residual Approximation for Efficient Matrix Multiplication in
+// DNNs", §2.4: for a large correction rank the r x r SPD system of Eq. 5 is
+// solved with a Newton-Schulz iteration (matrix products) instead of the
+// sequential Cholesky factorisation.  The path needs a factor F with
+// F F^T = G^-1 (G = L1^T L1 + lambda I) so that Q = L1 F replaces L1 exactly
+// as the Cholesky path's Q = L1 C^-T does; the coupled Newton-Schulz iteration
+// gives the symmetric one, F = G^-1/2:
+//     c = ||G||_F,  Y_0 = G / c,  Z_0 = I,
+//     T_k = (3 I - Z_k Y_k) / 2,  Y_{k+1} = Y_k T_k,  Z_{k+1} = T_k Z_k,
+//     F = Z_iters / sqrt(c).
+// Every iterate is a polynomial in G (symmetric, commuting) in exact
+// arithmetic; in float32 the products are formed as written (see
+// mat_product).
+//
+//   ns_factor  workgroup per instance: G by MFMA over the instance's tokens
+//              (chunks of 256, transposed through LDS as in cholq_kernel),
+//              then the iteration on 64 x 64 float32 matrices held in LDS,
+//              one 32 x 32 block of every product per wavefront
+//              (v_mfma_f32_32x32x2_f32).  Correction indices past the real
+//              rank get G = c I, which the iteration leaves at F = c^-1/2 I
+//              without touching the real block.
+//   ns_apply   workgroup per 64 tokens: Q = L1 F in place in T (float32
+//              plans also write Q^T token-contiguous for their mprime).
+// A rank-deficient G (lambda = 0) needs no special case: its null directions
+// are null directions of L1, so whatever F does there, L1 F does not see it.
+// Only a non-finite F (or G = 0) flags the instance, whose correction is then
+// dropped.
+#include "dyra_kernels.h"
+
+#include "mfma_tile.h"
+
+namespace dyra {
+
+namespace {
+
+constexpr int NT = 256;
+constexpr int MS = 68;  // row stride (floats) of the 64 x 64 matrices in LDS (16-byte aligned rows)
+
+typedef float Mat[64][MS];
+
+// D = A B (64 x 64 float32 in LDS), one 32 x 32 block per wavefront: A's
+// fragments along its rows, B's down its columns.  The product is formed
+// exactly as written, never through B^T or a symmetrised copy: the coupled
+// iteration is only stable when the rounding parts of Y and Z that break
+// their symmetry are carried along (dropping them made float32 runs diverge
+// within 20 steps at condition numbers near 1e3).  Ends with a barrier.
+__device__ __forceinline__ void mat_product(const Mat &A, const Mat &B, Mat &D, int tid) {
+    const int lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 31, lk = (lane >> 5) * 8;
+    const int wm = wave >> 1, wn = wave & 1;
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int k0 = 0; k0 < 64; k0 += 16) {
+        f32x8 fb;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) fb[q] = B[k0 + lk + q][wn * 32 + lr];
+        acc = mma16(acc, ld_frag(&A[wm * 32 + lr][k0 + lk]), fb);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) D[wm * 32 + acc_row(lane, q)][wn * 32 + lr] = acc[q];
+    __syncthreads();
+}
+
+template <typename E, int KC>
+__global__ __launch_bounds__(NT) void ns_factor_kernel(const E *__restrict__ T, int64_t ldt, int64_t off, int64_t n,
+                                                       int kc_real, float lambda, int iters, float *__restrict__ F,
+                                                       int *__restrict__ flags) {
+    constexpr int TT = NT;                          // tokens per Gram chunk
+    constexpr int ST = TT + 16 / (int)sizeof(E);    // row stride (elements) of the transposed chunk
+    __shared__ __align__(16) E Lt[64 * ST];         // [feature][token]
+    __shared__ __align__(16) float M[4][64][MS];
+    __shared__ float red[NT];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 31, lk = (lane >> 5) * 8;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t b = blockIdx.x;
+    const E *Tb = T + b * n * ldt + off;
+    for (int e = tid; e < (64 - KC) * ST; e += NT) Lt[KC * ST + e] = to_elem<E>(0.f);
+
+    // ---- G = L1_b^T L1_b over all n tokens
+    typedef typename Frag<E>::type Fr;
+    f32x16 acc = f32x16{};
+    for (int64_t c0 = 0; c0 < n; c0 += TT) {
+        __syncthreads();  // the previous chunk's reads are done
+        const int64_t t = c0 + tid;
+        for (int m = 0; m < KC; ++m) Lt[m * ST + tid] = t < n ? Tb[t * ldt + m] : to_elem<E>(0.f);
+        __syncthreads();
+#pragma unroll 4
+        for (int kk = 0; kk < TT; kk += 16)
+            acc = mma16(acc, ld_frag(Lt + (wm * 32 + lr) * ST + kk + lk), ld_frag(Lt + (wn * 32 + lr) * ST + kk + lk));
+    }
+    Mat &Y = M[0];
+    Mat &Z = M[1];
+    Mat &Tm = M[2];
+    Mat &W = M[3];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int i = wm * 32 + acc_row(lane, q), j = wn * 32 + lr;
+        Y[i][j] = (i < kc_real && j < kc_real) ? acc[q] + (i == j ? lambda : 0.f) : 0.f;
+    }
+    __syncthreads();
+    // ---- c = ||G||_F over the real block
+    float s = 0.f;
+    for (int e = tid; e < 64 * 64; e += NT) {
+        const float v = Y[e >> 6][e & 63];
+        s = fmaf(v, v, s);
+    }
+    red[tid] = s;
+    __syncthreads();
+    for (int h = NT / 2; h > 0; h >>= 1) {
+        if (tid < h) red[tid] += red[tid + h];
+        __syncthreads();
+    }
+    const float c = sqrtf(red[0]);
+    const float ic = c > 0.f ? 1.f / c : 0.f;
+    for (int e = tid; e < 64 * 64; e += NT) {
+        const int i = e >> 6, j = e & 63;
+        const bool pad = i >= kc_real || j >= kc_real;
+        Y[i][j] = pad ? (i == j ? 1.f : 0.f) : Y[i][j] * ic;  // padding: G = c I, so G / c = I
+        Z[i][j] = i == j ? 1.f : 0.f;
+    }
+    __syncthreads();
+    // ---- coupled iteration; the four buffers rotate: T = (3I - Z Y) / 2,
+    // Y <- Y T (into W), Z <- T Z (into the old Y)
+    int iy = 0, iz = 1, it = 2, iw = 3;
+    for (int k = 0; k < iters; ++k) {
+        mat_product(M[iz], M[iy], M[it], tid);
+        for (int e = tid; e < 64 * 64; e += NT) {
+            const int i = e >> 6, j = e & 63;
+            M[it][i][j] = (i == j ? 1.5f : 0.f) - 0.5f * M[it][i][j];
+        }
+        __syncthreads();
+        mat_product(M[iy], M[it], M[iw], tid);  // new Y
+        mat_product(M[it], M[iz], M[iy], tid);  // new Z, over the old Y
+        const int ny = iw, nz = iy, nw = iz;
+        iy = ny;
+        iz = nz;
+        iw = nw;
+    }
+    // ---- F = Z / sqrt(c); a non-finite F or G = 0 flags the instance
+    const float sc = c > 0.f ? rsqrtf(c) : 0.f;
+    int bad = 0;
+    float *Fb = F + b * KC * KC;
+    for (int e = tid; e < KC * KC; e += NT) {
+        const float v = M[iz][e / KC][e % KC] * sc;
+        bad |= !isfinite(v);
+        Fb[e] = v;
+    }
+    bad = __syncthreads_or(bad);
+    if (tid == 0) flags[b] = (bad || !(c > 0.f)) ? 1 : 0;
+    (void)Tm;
+    (void)W;
+}
+
+// Q = L1 F in place for 64 tokens of instance b (F = G^-1/2, symmetric up to
+// rounding, so Q Q^T = L1 G^-1 L1^T); float32 plans
+// also write Q^T token-contiguous into Qt ([B][KC][npad], zero past n).
+// Rows of a flagged instance become zero.
+template <typename E, int KC>
+__global__ __launch_bounds__(NT) void ns_apply_kernel(E *__restrict__ T, int64_t ldt, int64_t off, int64_t n,
+                                                      int64_t npad, const float *__restrict__ F,
+                                                      const int *__restrict__ flags, float *__restrict__ Qt) {
+    __shared__ float Ls[64][KC + 1];
+    __shared__ float Fs[KC][KC + 1];
+    const int tid = threadIdx.x;
+    const int64_t b = blockIdx.y, t0 = (int64_t)blockIdx.x * 64;
+    E *Tb = T + b * n * ldt + off;
+    for (int e = tid; e < KC * KC; e += NT) Fs[e / KC][e % KC] = F[b * KC * KC + e];
+    for (int e = tid; e < 64 * KC; e += NT) {
+        const int r = e / KC, m = e % KC;
+        Ls[r][m] = t0 + r < n ? (float)Tb[(t0 + r) * ldt + m] : 0.f;
+    }
+    const bool dead = flags[b] != 0;
+    __syncthreads();
+    constexpr int CPT = KC / 4;  // columns per thread
+    const int r = tid >> 2, c0 = (tid & 3) * CPT;
+    const int64_t t = t0 + r;
+    float q[CPT];
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) q[u] = 0.f;
+    for (int m = 0; m < KC; ++m) {
+        const float l = Ls[r][m];
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) q[u] = fmaf(l, Fs[m][c0 + u], q[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+        const float v = dead ? 0.f : q[u];
+        if (t < n) Tb[t * ldt + c0 + u] = to_elem<E>(v);
+        if (Qt && t < npad) Qt[(b * KC + c0 + u) * npad + t] = v;
+    }
+}
+
+}  // namespace
+
+template <typename E>
+hipError_t launch_ns_solve(E *T, int64_t ldt, int64_t off, int64_t B, int64_t n, int64_t npad, int kc_real, int kc,
+                           float lambda, int iters, float *F, int *flags, float *Qt, hipStream_t st,
+                           const EventMark &mark) {
+    if (B <= 0) return hipSuccess;
+    hipError_t e;
+    const dim3 g2((unsigned)((npad + 63) / 64), (unsigned)B);
+    switch (kc) {
+#define DYRA_NS(KC)                                                                                             \
+    case KC:                                                                                                    \
+        hipLaunchKernelGGL((ns_factor_kernel<E, KC>), dim3((unsigned)B), dim3(NT), 0, st, T, ldt, off, n, kc_real, \
+                           lambda, iters, F, flags);                                                            \
+        if ((e = mark(hipGetLastError())) != hipSuccess) return e;                                              \
+        hipLaunchKernelGGL((ns_apply_kernel<E, KC>), g2, dim3(NT), 0, st, T, ldt, off, n, npad, F, flags, Qt);  \
+        break;
+        DYRA_NS(16)
+        DYRA_NS(32)
+        DYRA_NS(48)
+        DYRA_NS(64)
+#undef DYRA_NS
+    default: return hipErrorInvalidValue;
+    }
+    return mark(hipGetLastError());
+}
+
+template hipError_t launch_ns_solve<bf16>(bf16 *, int64_t, int64_t, int64_t, int64_t, int64_t, int, int, float, int,
+                                          float *, int *, float *, hipStream_t, const EventMark &);
+template hipError_t launch_ns_solve<float>(float *, int64_t, int64_t, int64_t, int64_t, int64_t, int, int, float, int,
+                                           float *, int *, float *, hipStream_t, const EventMark &);
+
+}  // namespace dyra

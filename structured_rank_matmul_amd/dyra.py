@@ -55,7 +55,7 @@ def load() -> ctypes.CDLL:
     L.dyra_factorize_host.restype = ctypes.c_int
     L.dyra_prepare.argtypes = [vp, i64, i64, i32, i32, f32, ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp)]
     L.dyra_prepare.restype = ctypes.c_int
-    L.dyra_prepare_ex.argtypes = [vp, i64, i64, i32, i32, f32, ctypes.c_int, ctypes.c_int, vp, i32,
+    L.dyra_prepare_ex.argtypes = [vp, i64, i64, i32, i32, f32, ctypes.c_int, ctypes.c_int, vp, i32, i32,
                                   ctypes.POINTER(vp)]
     L.dyra_prepare_ex.restype = ctypes.c_int
     L.dyra_plan_destroy.argtypes = [vp]
@@ -167,9 +167,10 @@ def dyra_prepare(W: np.ndarray, r: int, k: int, lam: float = 0.0, dtype="bf16", 
 
 
 def dyra_prepare_ex(W: np.ndarray, r: int, k: int, lam: float = 0.0, dtype="bf16", device: int = 0,
-                    R0: Optional[np.ndarray] = None, als_half_steps: int = 2) -> Plan:
-    """dyra_prepare with a given R^(0) ([k, c2], e.g. Gaussian) and the number of
-    single ALS updates (2 = t 1, 3 = t 1.5, 4 = t 2)."""
+                    R0: Optional[np.ndarray] = None, als_half_steps: int = 2, ns_iters: int = 0) -> Plan:
+    """dyra_prepare with a given R^(0) ([k, c2], e.g. Gaussian), the number of
+    single ALS updates (2 = t 1, 3 = t 1.5, 4 = t 2) and the SPD solve (0 =
+    Cholesky, > 0 = that many Newton-Schulz steps)."""
     W = np.ascontiguousarray(W, dtype=np.float32)
     c1, c2 = W.shape
     code = _dtype_code(dtype)
@@ -180,7 +181,8 @@ def dyra_prepare_ex(W: np.ndarray, r: int, k: int, lam: float = 0.0, dtype="bf16
             raise ValueError(f"R0 must be [{k}, {c2}]")
     h = ctypes.c_void_p()
     st = load().dyra_prepare_ex(W.ctypes.data, c1, c2, int(r), int(k), float(lam), code, int(device),
-                                r0.ctypes.data if r0 is not None else None, int(als_half_steps), ctypes.byref(h))
+                                r0.ctypes.data if r0 is not None else None, int(als_half_steps), int(ns_iters),
+                                ctypes.byref(h))
     _check(st, "dyra_prepare_ex")
     return Plan(h.value, c1, c2, int(r), int(k), float(lam), code, int(device))
 

@@ -1,0 +1,94 @@
+"""§2.4's Newton-Schulz SPD solve (dyra_prepare_ex with ns_iters > 0) through
+the C ABI, against the float64 oracle running the same number of steps, and
+at convergence against the Cholesky path's result."""
+import numpy as np
+import pytest
+
+import oracle as orc
+from structured_rank_matmul_amd import dyra, synth
+
+from gpu_util import OWN_ERR_TOL, TOL, own_error_gap, rel, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # B, n, c1, c2, r, k, lambda, dtype, Newton-Schulz steps
+    (4, 60, 192, 320, 40, 16, 0.0, "bf16", 24),
+    (3, 150, 256, 288, 64, 32, 0.1, "f32", 24),
+    (5, 37, 128, 160, 16, 12, 0.05, "bf16", 6),     # not converged: the oracle takes the same 6 steps
+    (2, 300, 128, 416, 20, 40, 0.0, "f32", 30),     # k = 40 padded to 48
+    (3, 201, 256, 512, 64, 64, 0.0, "bf16", 24),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}n{c[1]}-{c[2]}x{c[3]}-r{c[4]}k{c[5]}-lam{c[6]}-{c[7]}-it{c[8]}")
+def test_newton_schulz_matches_oracle(case):
+    import torch
+    B, n, c1, c2, r, k, lam, dtype, iters = case
+    W = synth.random_weight(c1, c2, 81)
+    X = synth.random_matrix(B * n, c1, 82, dtype)
+    X = synth.round_activations(X.exact * np.exp(synth.random_matrix(1, c1, 83, "f32").exact), dtype)
+    plan = dyra.dyra_prepare_ex(W, r, k, lam, dtype, 0, ns_iters=iters)
+    assert dyra.stage_names(plan, n) == ["left", "ns_factor", "ns_apply", "mprime", "right", "output"]
+    ws = dyra.alloc_workspace(plan, B, n)
+    Y = dyra.dyra_forward(to_device(X), B, n, plan, workspace=ws)
+    torch.cuda.synchronize()
+    assert dyra.dyra_forward_status(plan, B, n, ws) == 0
+    y = to_host(Y)
+    op = orc.offline_preparation(W.astype(np.float64), r, k, lam)
+    ref = orc.inference(X.exact, B, n, op, ns_iters=iters)
+    chol = orc.inference(X.exact, B, n, op)
+    exact = X.exact @ W.astype(np.float64)
+    err, gap = rel(y, ref), own_error_gap(y, ref, exact)
+    print(f"ns case {case}: parity {err:.3e}  own-error gap {gap:.3e}  "
+          f"oracle NS vs Cholesky {rel(ref, chol):.2e}", flush=True)
+    assert err <= TOL[dtype]
+    assert gap <= OWN_ERR_TOL
+    plan.close()
+
+
+def test_newton_schulz_on_a_vitl_layer_equals_cholesky_path():
+    """ViT-L qkv (128 x 201 tokens, k = 64): 24 steps reach the Cholesky
+    solution to within the bf16 output's precision."""
+    import torch
+    w = synth.WORKLOADS["vitl_block"]
+    spec = w.layer("qkv")
+    W, _ = synth.make_weight(w, spec)
+    X = synth.make_activations(w, spec)
+    xd = to_device(X)
+    plan_ns = dyra.dyra_prepare_ex(W, spec.r, spec.k, 0.0, "bf16", 0, ns_iters=24)
+    plan_ch = dyra.dyra_prepare(W, spec.r, spec.k, 0.0, "bf16", 0)
+    y_ns = to_host(dyra.dyra_forward(xd, w.B, w.n, plan_ns))
+    y_ch = to_host(dyra.dyra_forward(xd, w.B, w.n, plan_ch))
+    torch.cuda.synchronize()
+    sample = [0, 64, 127]
+    rows = np.concatenate([np.arange(b * w.n, (b + 1) * w.n) for b in sample])
+    op = orc.offline_preparation(W.astype(np.float64), spec.r, spec.k, 0.0)
+    ref = orc.inference(X.exact[rows], len(sample), w.n, op, ns_iters=24)
+    print(f"vitl qkv NS 24: parity {rel(y_ns[rows], ref):.3e}  NS vs Cholesky path {rel(y_ns, y_ch):.3e}", flush=True)
+    assert rel(y_ns[rows], ref) <= TOL["bf16"]
+    assert rel(y_ns, y_ch) <= TOL["bf16"]
+    plan_ns.close()
+    plan_ch.close()
+
+
+def test_newton_schulz_zero_instance_is_flagged_and_arguments_checked():
+    import torch
+    B, n, c1, c2, r, k = 3, 40, 64, 96, 8, 16
+    W = synth.random_weight(c1, c2, 84)
+    X = synth.random_matrix(B * n, c1, 85, "bf16")
+    X.data[n:2 * n] = 0
+    plan = dyra.dyra_prepare_ex(W, r, k, 0.0, "bf16", 0, ns_iters=20)
+    ws = dyra.alloc_workspace(plan, B, n)
+    Y = dyra.dyra_forward(to_device(X), B, n, plan, workspace=ws)
+    assert dyra.dyra_forward_status(plan, B, n, ws) == 1
+    y = to_host(Y)
+    torch.cuda.synchronize()
+    assert np.all(y[n:2 * n] == 0)
+    ref = orc.inference(X.exact[:n], 1, n, orc.offline_preparation(W.astype(np.float64), r, k, 0.0), ns_iters=20)
+    assert rel(y[:n], ref) <= TOL["bf16"]
+    plan.close()
+    for kw in (dict(ns_iters=65), dict(ns_iters=-1), dict(ns_iters=10, als_half_steps=3)):
+        with pytest.raises(dyra.DyraError) as e:
+            dyra.dyra_prepare_ex(W, r, k, 0.0, "bf16", 0, **kw)
+        assert e.value.status == 1

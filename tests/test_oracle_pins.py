@@ -479,3 +479,45 @@ def test_half_steps_with_ridge_differ_from_plain_and_keep_bias_alpha_semantics()
     y0 = orc.inference(X, 2, n, plan, alpha=0.0)
     y4ab = orc.inference(X, 2, n, plan, bias=b, alpha=0.5, half_steps=4)
     np.testing.assert_allclose(y4ab - b[None, :] - y0, 0.5 * (y4 - y0), atol=1e-11)
+
+
+# ------------------------------------------------------------------ §2.4 Newton-Schulz SPD solve
+
+def _ns_scalar(mu, iters):
+    """The coupled iteration on one eigenvalue mu of G / c: y_0 = mu, z_0 = 1,
+    t = (3 - z y) / 2, y <- y t, z <- t z."""
+    y, z = mu, 1.0
+    for _ in range(iters):
+        t = 0.5 * (3.0 - z * y)
+        y, z = y * t, t * z
+    return z
+
+
+@pytest.mark.parametrize("iters", [0, 1, 3, 8, 20])
+def test_newton_schulz_acts_eigenvalue_by_eigenvalue(iters):
+    """Every iterate is a polynomial in G, so the matrix iteration is the scalar
+    recurrence applied to each eigenvalue of G / ||G||_F (eigenvectors from
+    numpy's eigh, not from the iteration)."""
+    A = gaussian((30, 9), 122) * np.exp(gaussian((1, 9), 123))
+    G = A.T @ A + 0.01 * np.eye(9)
+    lam, V = np.linalg.eigh(G)
+    c = np.linalg.norm(G)
+    expect = (V * np.array([_ns_scalar(m / c, iters) for m in lam])) @ V.T / np.sqrt(c)
+    np.testing.assert_allclose(orc.newton_schulz_inv_sqrt(G, iters), expect, atol=1e-10 * np.abs(expect).max())
+
+
+def test_newton_schulz_converges_to_the_cholesky_solution():
+    """Enough steps reach G^-1/2 (eigh) and the correction equals the one of the
+    Cholesky / LU solve of Eq. 5; few steps do not."""
+    c1, c2, r_w, r_c, n = 18, 14, 3, 5, 25
+    W = synth.random_weight(c1, c2, 124).astype(np.float64)
+    X = gaussian((2 * n, c1), 125) * np.exp(gaussian((1, c1), 126))
+    plan = orc.offline_preparation(W, r_w, r_c, 0.0)
+    y_exact = orc.inference(X, 2, n, plan)
+    y_ns = orc.inference(X, 2, n, plan, ns_iters=40)
+    assert orc.rel_fro(y_ns, y_exact) < 1e-10
+    assert orc.rel_fro(orc.inference(X, 2, n, plan, ns_iters=2), y_exact) > 1e-4
+    L1 = X[:n] @ plan.P_L
+    G = L1.T @ L1
+    lam, V = np.linalg.eigh(G)
+    np.testing.assert_allclose(orc.newton_schulz_inv_sqrt(G, 40), (V / np.sqrt(lam)) @ V.T, rtol=1e-9, atol=1e-12)
