@@ -22,6 +22,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+// 16 raw bytes (a struct vector type such as uint4 in an array stays in scratch)
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename E> struct Frag;
 template <> struct Frag<bf16> { typedef bf16x8 type; };

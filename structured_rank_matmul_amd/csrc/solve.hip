@@ -413,7 +413,6 @@ __global__ __launch_bounds__(NT) void mprime_kernel(const E *__restrict__ X, con
 // direct-to-LDS loads of the GEMMs: this kernel streams X_b once from HBM
 // and is bound by that read, not by the MFMA work.
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // (a struct type here would stay in scratch)
 
 __device__ __forceinline__ uint2 lds_tr16(const char *p) {
     const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
