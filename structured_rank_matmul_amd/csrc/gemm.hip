@@ -189,12 +189,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
         SC = (corr.kc + BK - 1) / BK;
         S = S0 + ((rend - 1) / corr.n - b_first + 1) * SC;
     }
-    // instance b, its token rows [rlo, rhi) and slice index sc of slice s >= S0
-    auto inst_of = [&](int64_t s, int64_t &b, int64_t &rlo, int64_t &rhi, int &sc) {
-        const int64_t j = s - S0;
-        const int64_t bi = j / SC;
-        sc = (int)(j - bi * SC);
-        b = b_first + bi;
+    // Correction slices come in order (instance b_first + bi, slice sc of its
+    // SC); both the loads and the MFMAs walk them in order, so each side
+    // carries its (bi, sc) as a counter rather than dividing s - S0 by SC.
+    struct CorrPos {
+        int bi = 0, sc = 0;
+        __device__ void next(int SCn) {
+            if (++sc == SCn) {
+                sc = 0;
+                ++bi;
+            }
+        }
+    } ipos, cpos;
+    // instance b of position q and its token rows [rlo, rhi)
+    auto inst_of = [&](const CorrPos &q, int64_t &b, int64_t &rlo, int64_t &rhi) {
+        b = b_first + q.bi;
         rlo = b * corr.n;
         rhi = rlo + corr.n < M ? rlo + corr.n : M;
     };
@@ -222,8 +231,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
             }
         } else {
             int64_t b, rlo, rhi;
-            int sc;
-            inst_of(s, b, rlo, rhi, sc);
+            inst_of(ipos, b, rlo, rhi);
+            const int sc = ipos.sc;
+            ipos.next(SC);
             int kl = sc * BK + fcol;
             kl = kl < corr.kc ? kl : 0;  // columns past kc are fetched from column 0 and never used
 #pragma unroll
@@ -260,8 +270,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
         int64_t rlo = 0, rhi = 0;
         if (CORR && s >= S0) {
             int64_t b;
-            int sc;
-            inst_of(s, b, rlo, rhi, sc);
+            inst_of(cpos, b, rlo, rhi);
+            const int sc = cpos.sc;
+            cpos.next(SC);
             const int kleft = (corr.kc - sc * BK) / 16;
             ksteps = kleft < KSTEPS ? kleft : KSTEPS;
             live = 0;
