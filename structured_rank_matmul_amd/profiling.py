@@ -198,7 +198,8 @@ def main(argv=None):
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
     t.add_argument("--kernel", required=True, help="regex on the kernel name")
-    t.add_argument("--copy-kernel", default="copy", help="regex on the calibration copy kernel's name")
+    t.add_argument("--copy-kernel", default="neg_kernel",
+                   help="regex on the calibration copy kernel's name (the probe copies with torch.neg)")
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
