@@ -398,7 +398,7 @@ __global__ __launch_bounds__(NT) void mprime_kernel(const E *__restrict__ X, con
 
 // ------------------------------------------------- M'_b = Q_b^T X_b, bf16
 // Workgroup (256 input features, instance b); token slices of 32 rows of X_b
-// and of Q_b are loaded into registers one slice ahead, written to a double
+// and of Q_b are loaded into registers two slices ahead, written to a double
 // buffered LDS stage row-major (as stored), and the token-contiguous MFMA
 // fragments come out of LDS through transposing reads (ds_read_b64_tr_b16: in
 // each group of 16 lanes, lane i receives element i % 4 of the 8-byte rows
@@ -413,6 +413,7 @@ __global__ __launch_bounds__(NT) void mprime_kernel(const E *__restrict__ X, con
 // direct-to-LDS loads of the GEMMs: this kernel streams X_b once from HBM
 // and is bound by that read, not by the MFMA work.
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+constexpr int kMprimeFeatures = 256;  // features per mprime workgroup (128 measured no faster)
 
 __device__ __forceinline__ uint2 lds_tr16(const char *p) {
     const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -422,11 +423,11 @@ __device__ __forceinline__ uint2 lds_tr16(const char *p) {
     return w.u;
 }
 
-template <int KC>
+template <int KC, int CW>
 __global__ __launch_bounds__(NT) void mprime_tr_kernel(const bf16 *__restrict__ X, const bf16 *__restrict__ T,
                                                        int64_t ldt, int64_t off, int64_t n, int64_t c1,
                                                        bf16 *__restrict__ Mp) {
-    constexpr int CW = 256;                 // features per workgroup
+    // CW features per workgroup, CW / 4 per wavefront
     constexpr int TS = 32;                  // tokens per slice
     constexpr int RB = CW * 2;              // bytes per X row in LDS
     constexpr int XBYTES = TS * RB;         // 16 KB
@@ -436,6 +437,8 @@ __global__ __launch_bounds__(NT) void mprime_tr_kernel(const bf16 *__restrict__ 
     constexpr int CPX = RB / 16;            // 16-byte chunks per X row
     constexpr int NKB = (KC + 31) / 32;     // 32-row blocks of M'_b
     constexpr int MS = CW + 8;              // row stride (elements) of the staged M'_b block
+    constexpr int JB = CW / 128;            // 32-feature blocks per wavefront
+    static_assert(CW == 128 || CW == 256, "feature block");
     static_assert(TS * QROW == 16 * NT && KC * MS * 2 <= 2 * STAGE, "layout");
     __shared__ __align__(16) char smem[2 * STAGE];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -448,30 +451,33 @@ __global__ __launch_bounds__(NT) void mprime_tr_kernel(const bf16 *__restrict__ 
 
     // thread tid loads X chunks q * 256 + tid (row-major over the slice) and
     // Q chunk tid; rows past n repeat row n - 1 (masked in the product),
-    // features past c1 read feature 0 (never stored)
-    u32x4 reg[LX + 1];
-    auto load = [&](int64_t s) __attribute__((always_inline)) {
+    // features past c1 read feature 0 (never stored).  Two register sets hold
+    // the next two slices, so two slices' loads are in flight during a
+    // slice's MFMAs; the slice loop is unrolled by two so that every index
+    // into the sets is a constant.
+    u32x4 reg[2][LX + 1];
+    auto load = [&](int64_t s, u32x4 (&rg)[LX + 1]) __attribute__((always_inline)) {
         const int64_t t0 = s * TS;
 #pragma unroll
         for (int q = 0; q < LX; ++q) {
             const int e = q * NT + tid, row = e / CPX, c = e % CPX;
             const int64_t t = t0 + row < n ? t0 + row : n - 1;
             const int64_t f = f0 + 8 * c < c1 ? f0 + 8 * c : 0;
-            reg[q] = *reinterpret_cast<const u32x4 *>(Xb + t * c1 + f);
+            rg[q] = *reinterpret_cast<const u32x4 *>(Xb + t * c1 + f);
         }
         const int row = tid >> 3, c = tid & 7;
         const int64_t t = t0 + row < n ? t0 + row : n - 1;
-        reg[LX] = *reinterpret_cast<const u32x4 *>(Qb + t * ldt + (8 * c < KC ? 8 * c : 0));
+        rg[LX] = *reinterpret_cast<const u32x4 *>(Qb + t * ldt + (8 * c < KC ? 8 * c : 0));
     };
-    auto stage = [&](int slot) __attribute__((always_inline)) {
+    auto stage = [&](int slot, const u32x4 (&rg)[LX + 1]) __attribute__((always_inline)) {
         char *dst = smem + slot * STAGE;
 #pragma unroll
         for (int q = 0; q < LX; ++q) {
             const int e = q * NT + tid, row = e / CPX, c = e % CPX;
-            *reinterpret_cast<u32x4 *>(dst + row * RB + ((c ^ (4 * (row & 3))) << 4)) = reg[q];
+            *reinterpret_cast<u32x4 *>(dst + row * RB + ((c ^ (4 * (row & 3))) << 4)) = rg[q];
         }
         const int row = tid >> 3, c = tid & 7;
-        *reinterpret_cast<u32x4 *>(dst + XBYTES + row * QROW + ((c ^ (4 * ((row >> 1) & 1))) << 4)) = reg[LX];
+        *reinterpret_cast<u32x4 *>(dst + XBYTES + row * QROW + ((c ^ (4 * ((row >> 1) & 1))) << 4)) = rg[LX];
     };
 
     // per-lane transposing-read offsets: 16-lane group g = lane / 16 covers
@@ -481,33 +487,35 @@ __global__ __launch_bounds__(NT) void mprime_tr_kernel(const bf16 *__restrict__ 
     auto xoff = [&](int row, int col) { return row * RB + (((col >> 3) ^ (4 * (row & 3))) << 4) + (col & 7) * 2; };
     auto qoff = [&](int row, int col) { return row * QROW + (((col >> 3) ^ (4 * ((row >> 1) & 1))) << 4) + (col & 7) * 2; };
 
-    f32x16 acc[2][NKB];
+    f32x16 acc[JB][NKB];
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+    for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
         for (int ib = 0; ib < NKB; ++ib) acc[jb][ib] = f32x16{};
 
-    // slice s: stage it (waits for its loads), barrier, request slice s + 1,
-    // multiply.  The stage written at slice s + 2 was last read at slice s,
-    // before the barrier of slice s + 1.
-    load(0);
-    for (int64_t s = 0; s < S; ++s) {
-        stage((int)(s & 1));
+    // slice s (register set and LDS stage s % 2): stage it (waits for its
+    // loads), barrier, request slice s + 2 into the set just staged, multiply.
+    // The LDS stage written at slice s + 2 was last read at slice s, before
+    // the barrier of slice s + 1.  The request is unconditional (past the last
+    // slice it rereads row n - 1): with the same loads outstanding on every
+    // path, the wait before staging a set covers that set's loads only.
+    auto slice = [&](int64_t s, int slot, u32x4 (&rg)[LX + 1]) __attribute__((always_inline)) {
+        stage(slot, rg);
         __syncthreads();
-        if (s + 1 < S) load(s + 1);
-        const char *sx = smem + (int)(s & 1) * STAGE;
+        load(s + 2, rg);
+        const char *sx = smem + slot * STAGE;
         const char *sq = sx + XBYTES;
         const int64_t t0 = s * TS;
         const bool tail = t0 + TS > n;
 #pragma unroll
         for (int h = 0; h < TS / 16; ++h) {
-            bf16x8 fx[2], fq[NKB];
+            bf16x8 fx[JB], fq[NKB];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int row = 16 * h + 8 * (g >> 1) + 4 * u + rq;
 #pragma unroll
-                for (int jb = 0; jb < 2; ++jb)
-                    reinterpret_cast<uint2 *>(&fx[jb])[u] = lds_tr16(sx + xoff(row, 64 * wave + 32 * jb + hcol));
+                for (int jb = 0; jb < JB; ++jb)
+                    reinterpret_cast<uint2 *>(&fx[jb])[u] = lds_tr16(sx + xoff(row, 32 * JB * wave + 32 * jb + hcol));
 #pragma unroll
                 for (int ib = 0; ib < NKB; ++ib)
                     reinterpret_cast<uint2 *>(&fq[ib])[u] = lds_tr16(sq + qoff(row, 32 * ib + hcol));
@@ -523,11 +531,22 @@ __global__ __launch_bounds__(NT) void mprime_tr_kernel(const bf16 *__restrict__ 
                 }
             }
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
+            for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
                 for (int ib = 0; ib < NKB; ++ib) acc[jb][ib] = mma16(acc[jb][ib], fx[jb], fq[ib]);
         }
+    };
+    load(0, reg[0]);
+    __builtin_amdgcn_sched_barrier(0);  // set 0's loads stay older than set 1's, as in the loop
+    load(1, reg[1]);
+    // pairs of slices, then an odd last one (the loop body itself has no
+    // branch around a half, which would merge load orders at its head)
+    int64_t s = 0;
+    for (; s + 1 < S; s += 2) {
+        slice(s, 0, reg[0]);
+        slice(s + 1, 1, reg[1]);
     }
+    if (s < S) slice(s, 0, reg[0]);
 
     // lane holds row kk = 32 ib + lane % 32 of M'_b and, per register group q,
     // four consecutive features; staged as [kk][feature], stored by rows
@@ -538,13 +557,13 @@ __global__ __launch_bounds__(NT) void mprime_tr_kernel(const bf16 *__restrict__ 
         const int kk = 32 * ib + (lane & 31);
         if (kk >= KC) continue;
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
+        for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 union { uint2 u; bf16 e[4]; } w;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) w.e[e] = (bf16)acc[jb][ib][4 * q + e];
-                *reinterpret_cast<uint2 *>(ms + kk * MS + 64 * wave + 32 * jb + acc_row(lane, 4 * q)) = w.u;
+                *reinterpret_cast<uint2 *>(ms + kk * MS + 32 * JB * wave + 32 * jb + acc_row(lane, 4 * q)) = w.u;
             }
     }
     __syncthreads();
@@ -589,12 +608,13 @@ template <>
 hipError_t launch_mprime<bf16>(const bf16 *X, const bf16 *T, int64_t ldt, int64_t off, const bf16 *, int64_t B,
                                int64_t n, int64_t, int64_t c1, int kc, bf16 *Mp, hipStream_t st) {
     if (B <= 0) return hipSuccess;
-    const dim3 grid((unsigned)((c1 + 255) / 256), (unsigned)B);
+    constexpr int CW = kMprimeFeatures;
+    const dim3 grid((unsigned)((c1 + CW - 1) / CW), (unsigned)B);
     switch (kc) {
-    case 16: hipLaunchKernelGGL(mprime_tr_kernel<16>, grid, dim3(NT), 0, st, X, T, ldt, off, n, c1, Mp); break;
-    case 32: hipLaunchKernelGGL(mprime_tr_kernel<32>, grid, dim3(NT), 0, st, X, T, ldt, off, n, c1, Mp); break;
-    case 48: hipLaunchKernelGGL(mprime_tr_kernel<48>, grid, dim3(NT), 0, st, X, T, ldt, off, n, c1, Mp); break;
-    case 64: hipLaunchKernelGGL(mprime_tr_kernel<64>, grid, dim3(NT), 0, st, X, T, ldt, off, n, c1, Mp); break;
+    case 16: hipLaunchKernelGGL((mprime_tr_kernel<16, CW>), grid, dim3(NT), 0, st, X, T, ldt, off, n, c1, Mp); break;
+    case 32: hipLaunchKernelGGL((mprime_tr_kernel<32, CW>), grid, dim3(NT), 0, st, X, T, ldt, off, n, c1, Mp); break;
+    case 48: hipLaunchKernelGGL((mprime_tr_kernel<48, CW>), grid, dim3(NT), 0, st, X, T, ldt, off, n, c1, Mp); break;
+    case 64: hipLaunchKernelGGL((mprime_tr_kernel<64, CW>), grid, dim3(NT), 0, st, X, T, ldt, off, n, c1, Mp); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
