@@ -428,7 +428,7 @@ hipError_t gemm_dispatch(const E *A, int64_t lda, const E *B, int64_t ldb, int64
                          const Corr<E> &corr, Epi epi, hipStream_t st) {
     switch (pick_shape(M, N)) {
     case Shape::T256x256: return gemm_launch<E, 256, 256, 4, 2, 4, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
-    case Shape::T256x160: return gemm_launch<E, 256, 160, 4, 1, 4, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
+    case Shape::T256x160: return gemm_launch<E, 256, 160, 8, 1, 4, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
     case Shape::T256x128: return gemm_launch<E, 256, 128, 4, 2, 4, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
     case Shape::T128x128: return gemm_launch<E, 128, 128, 2, 2, 4, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
     case Shape::T64x64: return gemm_launch<E, 64, 64, 2, 2, 4, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
