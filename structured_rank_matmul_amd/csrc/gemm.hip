@@ -29,6 +29,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "mfma_tile.h"
 
@@ -254,7 +255,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
     };
 
     for (int64_t p = 0; p < NS - 1 && p < S; ++p) issue(p);
-    for (int64_t s = 0; s < S; ++s) {
+    // One K slice.  CS: a correction slice (instance rows masked, possibly
+    // fewer 16-deep steps); the static slices are compiled without any of
+    // that, as one run of MFMAs.
+    auto slice = [&](int64_t s, auto CS) __attribute__((always_inline)) {
+        constexpr bool CSL = decltype(CS)::value;
         // this wave's loads of slice s have landed once at most `later` slices'
         // worth (issued after it) are outstanding; the barrier then makes every
         // wave's part visible and frees the buffer of slice s - 1
@@ -268,7 +273,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
         int ksteps = KSTEPS;
         uint32_t live = ~0u;
         int64_t rlo = 0, rhi = 0;
-        if (CORR && s >= S0) {
+        if constexpr (CSL) {
             int64_t b;
             inst_of(cpos, b, rlo, rhi);
             const int sc = cpos.sc;
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
         typename Frag<E>::type fa[KSTEPS][TM], fb[KSTEPS][TN];
 #pragma unroll
         for (int h = 0; h < KSTEPS; ++h) {
-            if (h >= ksteps) break;
+            if (CSL && h >= ksteps) break;
 #pragma unroll
             for (int j = 0; j < TN; ++j) fb[h][j] = slice_frag(sb + j * 32 * 64, h, hf, sw, (const E *)nullptr);
 #pragma unroll
@@ -298,11 +303,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int h = 0; h < KSTEPS; ++h) {
-            if (h >= ksteps) break;
+            if (CSL && h >= ksteps) break;
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 typename Frag<E>::type a = fa[h][i];
-                if (CORR && s >= S0) {
+                if constexpr (CSL) {
                     if (!((live >> i) & 1u)) continue;
                     const int64_t r = row0 + (wm * TM + i) * 32 + lr;
                     if (!(r >= rlo && r < rhi)) a = zero_frag(a);
@@ -312,6 +317,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
                     acc[i][j] = ROWS ? mma16(acc[i][j], fb[h][j], a) : mma16(acc[i][j], a, fb[h][j]);
             }
         }
+    };
+    int64_t s = 0;
+    for (; s < S0; ++s) slice(s, std::false_type{});
+    if constexpr (CORR) {
+        for (; s < S; ++s) slice(s, std::true_type{});
     }
     __syncthreads();
     // ---- epilogue.  A lane holds four consecutive elements of the store's
