@@ -8,6 +8,8 @@
 // per workgroup, and the small operands (X, T) are re-read from L2.
 #include "dyra_decode.h"
 
+#include <algorithm>
+
 #include "mfma_tile.h"
 
 namespace dyra {
@@ -17,9 +19,12 @@ namespace {
 constexpr int NT = 256;
 constexpr int kRowBlock = 64;  // rows (tokens) per workgroup, two 32-row MFMA blocks
 
+constexpr int kMaxSplits = 16;  // split-K parts of the projection
+constexpr int kMaxCorr = 64;    // largest padded correction rank
+
 int decode_splits(int64_t c1) {
     int s = 1;
-    while (s < 16 && c1 % (32 * 2 * s) == 0 && c1 / (2 * s) >= 256) s *= 2;
+    while (s < kMaxSplits && c1 % (32 * 2 * s) == 0 && c1 / (2 * s) >= 256) s *= 2;
     return s;
 }
 
@@ -58,14 +63,21 @@ __device__ __forceinline__ bf16x8 frag_from_f32(const float *p, bf16) {
 }
 __device__ __forceinline__ f32x8 frag_from_f32(const float *p, float) { return ld_frag(p); }
 
+constexpr int kUnroll = 4;     // 16-deep steps whose loads are requested together
+constexpr int kUnrollRes = 4;  // the same for each of the two W_res register sets
+
+// Fragment or zero, without a branch (the load itself always reads an address
+// in range; lanes out of range point at a clamped one).
+template <typename F> __device__ __forceinline__ F keep_if(bool ok, const F &f) { return ok ? f : F{}; }
+
 // partial[s][row][col] = sum over the s-th split of c1 of X[row][k] Aext[col][k].
 // Grid (K1/32 column blocks, splits, row blocks of 64).  The 16-deep steps of a
 // split are dealt round-robin to the four wavefronts, then reduced in LDS.
-template <typename E>
+template <typename E, bool TWO>
 __global__ __launch_bounds__(NT) void decode_project_kernel(const E *__restrict__ X, const E *__restrict__ Aext,
                                                             int64_t N, int64_t c1, int K1, int splits,
                                                             float *__restrict__ partial) {
-    __shared__ float red[kRowBlock][33];
+    __shared__ float red[NT / 64][kRowBlock * 32];  // each wavefront's partial [row][col]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 31, lk = (lane >> 5) * 8;
     const int col0 = blockIdx.x * 32;
@@ -73,28 +85,44 @@ __global__ __launch_bounds__(NT) void decode_project_kernel(const E *__restrict_
     const int64_t row0 = (int64_t)blockIdx.z * kRowBlock;
     const int64_t ks = c1 / splits;
     const int64_t kbeg = s * ks;
-    for (int e = tid; e < kRowBlock * 33; e += NT) (&red[0][0])[e] = 0.f;
-    __syncthreads();
     f32x16 acc[2] = {f32x16{}, f32x16{}};
     const int col = col0 + lr;
     const bool col_ok = col < K1;
     const int64_t ra = row0 + lr, rb = row0 + 32 + lr;
+    const bool a_ok = ra < N, b_ok = rb < N;
+    const E *pb = Aext + (int64_t)(col_ok ? col : 0) * c1 + lk;
+    const E *pa0 = X + (a_ok ? ra : row0) * c1 + lk;
+    const E *pa1 = X + (b_ok ? rb : row0) * c1 + lk;
     typedef typename Frag<E>::type F;
-    for (int64_t k = kbeg + 16 * wave; k < kbeg + ks; k += 64) {
-        F fb = col_ok ? ld_frag(Aext + (int64_t)col * c1 + k + lk) : F{};
-        F fa0 = ra < N ? ld_frag(X + ra * c1 + k + lk) : F{};
-        F fa1 = rb < N ? ld_frag(X + rb * c1 + k + lk) : F{};
-        acc[0] = mma16(acc[0], fa0, fb);
-        acc[1] = mma16(acc[1], fa1, fb);
+    // kUnroll steps' loads are requested before their MFMAs
+    for (int64_t k0 = kbeg + 16 * wave; k0 < kbeg + ks; k0 += 64 * kUnroll) {
+        F fb[kUnroll], fa0[kUnroll], fa1[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t k = k0 + 64 * u;
+            const bool kin = k < kbeg + ks;
+            const int64_t kk = kin ? k : kbeg;
+            fb[u] = keep_if(kin && col_ok, ld_frag(pb + kk));
+            fa0[u] = keep_if(kin && a_ok, ld_frag(pa0 + kk));
+            if constexpr (TWO) fa1[u] = keep_if(kin && b_ok, ld_frag(pa1 + kk));
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            acc[0] = mma16(acc[0], fa0[u], fb[u]);
+            if constexpr (TWO) acc[1] = mma16(acc[1], fa1[u], fb[u]);
+        }
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int t = 0; t < 16; ++t) atomicAdd(&red[h * 32 + acc_row(lane, t)][lr], acc[h][t]);
+        for (int t = 0; t < 16; ++t) red[wave][(h * 32 + acc_row(lane, t)) * 32 + lr] = acc[h][t];
     __syncthreads();
     for (int e = tid; e < kRowBlock * 32; e += NT) {
         const int r = e >> 5, c = e & 31;
-        if (row0 + r < N && col0 + c < K1) partial[((int64_t)s * N + row0 + r) * K1 + col0 + c] = red[r][c];
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) v += red[w][e];
+        if (row0 + r < N && col0 + c < K1) partial[((int64_t)s * N + row0 + r) * K1 + col0 + c] = v;
     }
 }
 
@@ -111,22 +139,28 @@ __global__ __launch_bounds__(NT) void decode_coef_kernel(const float *__restrict
                                                          int *__restrict__ flags) {
     __shared__ double K[16][16];
     __shared__ double V[16][16];
+    __shared__ float Ls[16][kMaxCorr + 1];  // the instance's L1 rows (the Gram's operand)
     const int tid = threadIdx.x;
     const int64_t b = blockIdx.x;
     const int64_t r0 = b * n;
     for (int64_t e = tid; e < n * K1; e += NT) {
         const int64_t i = e / K1, c = e - (e / K1) * K1;
+        // every split's value requested before the first add (one load latency)
+        float v[kMaxSplits];
+#pragma unroll
+        for (int q = 0; q < kMaxSplits; ++q) v[q] = q < splits ? partial[((int64_t)q * N + r0 + i) * K1 + c] : 0.f;
         float s = 0.f;
-        for (int q = 0; q < splits; ++q) s += partial[((int64_t)q * N + r0 + i) * K1 + c];
+#pragma unroll
+        for (int q = 0; q < kMaxSplits; ++q) s += v[q];
         T[(r0 + i) * K1 + c] = s;
+        if (c >= kw) Ls[i][c - kw] = s;
     }
     __syncthreads();
     const int nn = (int)n;
     for (int e = tid; e < nn * nn; e += NT) {
         const int i = e / nn, j = e - (e / nn) * nn;
         double s = 0.0;
-        for (int c = 0; c < k_real; ++c)
-            s += (double)T[(r0 + i) * K1 + kw + c] * (double)T[(r0 + j) * K1 + kw + c];
+        for (int c = 0; c < k_real; ++c) s += (double)Ls[i][c] * (double)Ls[j][c];
         K[i][j] = s;
     }
     __syncthreads();
@@ -189,65 +223,128 @@ __global__ __launch_bounds__(NT) void decode_coef_kernel(const float *__restrict
 // (§2.4's fused output with bias and correction weight alpha).  Grid (c2/32,
 // row blocks of whole instances).  The 16-deep steps of both contractions are
 // dealt round-robin to the four wavefronts and reduced in LDS.
-template <typename E>
+template <typename E, bool TWO>
 __global__ __launch_bounds__(NT) void decode_output_kernel(const E *__restrict__ X, const float *__restrict__ T,
                                                            const float *__restrict__ coef,
                                                            const E *__restrict__ Vs, const E *__restrict__ Wres_t,
                                                            int64_t N, int64_t n, int64_t c1, int64_t c2, int K1,
                                                            int kw, int64_t rows_blk, const E *__restrict__ bias,
                                                            float alpha, E *__restrict__ Y) {
-    __shared__ float Zs[kRowBlock][33];
-    __shared__ float Ss[kRowBlock][33];
+    __shared__ float part[NT / 64][kRowBlock * 32];  // each wavefront's partial [row][col]
+    __shared__ float Zs[kRowBlock][33];              // X W_res of the block, summed
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 31, lk = (lane >> 5) * 8;
     const int64_t col0 = (int64_t)blockIdx.x * 32;
     const int64_t row0 = (int64_t)blockIdx.y * rows_blk;
     const int64_t row_end = (row0 + rows_blk < N) ? row0 + rows_blk : N;
-    for (int e = tid; e < kRowBlock * 33; e += NT) {
-        (&Zs[0][0])[e] = 0.f;
-        (&Ss[0][0])[e] = 0.f;
-    }
-    __syncthreads();
     typedef typename Frag<E>::type F;
     const int64_t col = col0 + lr;
     const bool col_ok = col < c2;
     const int64_t ra = row0 + lr, rb = row0 + 32 + lr;
     const bool a_ok = ra < row_end, b_ok = rb < row_end;
     f32x16 z0 = f32x16{}, z1 = f32x16{}, s0 = f32x16{}, s1 = f32x16{};
-    for (int64_t k = 16 * wave; k < c1; k += 64) {
-        F fb = col_ok ? ld_frag(Wres_t + col * c1 + k + lk) : F{};
-        F fa0 = a_ok ? ld_frag(X + ra * c1 + k + lk) : F{};
-        F fa1 = b_ok ? ld_frag(X + rb * c1 + k + lk) : F{};
-        z0 = mma16(z0, fa0, fb);
-        z1 = mma16(z1, fa1, fb);
+    // both contractions request kUnroll steps' loads of the streamed W_res /
+    // V_s columns before their MFMAs
+    const int64_t colc = col_ok ? col : 0, rac = a_ok ? ra : row0, rbc = b_ok ? rb : row0;
+    {
+        // W_res is the long stream: two register sets, the next batch's loads
+        // requested before the current batch's MFMAs.  Loads are unconditional
+        // (steps past c1 reread step 0); the zeroing happens at the MFMA, so a
+        // batch's data is waited for only there.
+        constexpr int U = kUnrollRes;
+        const E *pb = Wres_t + colc * c1 + lk, *pa0 = X + rac * c1 + lk, *pa1 = X + rbc * c1 + lk;
+        auto load = [&](int64_t k0, F (&fb)[U], F (&fa0)[U], F (&fa1)[U]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t k = k0 + 64 * u;
+                const int64_t kk = k < c1 ? k : 0;
+                fb[u] = ld_frag(pb + kk);
+                fa0[u] = ld_frag(pa0 + kk);
+                if constexpr (TWO) fa1[u] = ld_frag(pa1 + kk);
+            }
+        };
+        auto mma = [&](int64_t k0, const F (&fb)[U], const F (&fa0)[U], const F (&fa1)[U])
+                       __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool kin = k0 + 64 * u < c1;
+                const F b = keep_if(kin && col_ok, fb[u]);
+                z0 = mma16(z0, keep_if(a_ok, fa0[u]), b);
+                if constexpr (TWO) z1 = mma16(z1, keep_if(b_ok, fa1[u]), b);
+            }
+        };
+        F ab[U], a0[U], a1[U], bb[U], b0[U], b1[U];
+        constexpr int64_t BS = 64 * U;  // K advance of one batch
+        int64_t k0 = 16 * wave;
+        load(k0, ab, a0, a1);
+        __builtin_amdgcn_sched_barrier(0);
+        for (; k0 < c1; k0 += 2 * BS) {
+            load(k0 + BS, bb, b0, b1);
+            mma(k0, ab, a0, a1);
+            __builtin_amdgcn_sched_barrier(0);
+            load(k0 + 2 * BS, ab, a0, a1);
+            mma(k0 + BS, bb, b0, b1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
-    for (int k = 16 * wave; k < kw; k += 64) {
-        F fb = col_ok ? ld_frag(Vs + col * kw + k + lk) : F{};
-        F fa0 = a_ok ? frag_from_f32(T + ra * K1 + k + lk, E{}) : F{};
-        F fa1 = b_ok ? frag_from_f32(T + rb * K1 + k + lk, E{}) : F{};
-        s0 = mma16(s0, fa0, fb);
-        s1 = mma16(s1, fa1, fb);
+    {
+        const E *pb = Vs + colc * kw + lk;
+        const float *pa0 = T + rac * K1 + lk, *pa1 = T + rbc * K1 + lk;
+        for (int k0 = 16 * wave; k0 < kw; k0 += 64 * kUnroll) {
+            F fb[kUnroll], fa0[kUnroll], fa1[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int k = k0 + 64 * u;
+                const bool kin = k < kw;
+                const int kk = kin ? k : 0;
+                fb[u] = keep_if(kin && col_ok, ld_frag(pb + kk));
+                fa0[u] = keep_if(kin && a_ok, frag_from_f32(pa0 + kk, E{}));
+                if constexpr (TWO) fa1[u] = keep_if(kin && b_ok, frag_from_f32(pa1 + kk, E{}));
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                s0 = mma16(s0, fa0[u], fb[u]);
+                if constexpr (TWO) s1 = mma16(s1, fa1[u], fb[u]);
+            }
+        }
     }
+    // Z = X W_res summed over the wavefronts' steps into Zs
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
         const int r = acc_row(lane, t);
-        atomicAdd(&Zs[r][lr], z0[t]);
-        atomicAdd(&Zs[32 + r][lr], z1[t]);
-        atomicAdd(&Ss[r][lr], s0[t]);
-        atomicAdd(&Ss[32 + r][lr], s1[t]);
+        part[wave][r * 32 + lr] = z0[t];
+        part[wave][(32 + r) * 32 + lr] = z1[t];
+    }
+    __syncthreads();
+    for (int e = tid; e < kRowBlock * 32; e += NT) {
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) v += part[w][e];
+        Zs[e >> 5][e & 31] = v;
+    }
+    __syncthreads();
+    // S = T_s V_s^T partials in the same buffer (its Z reads are done)
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        const int r = acc_row(lane, t);
+        part[wave][r * 32 + lr] = s0[t];
+        part[wave][(32 + r) * 32 + lr] = s1[t];
     }
     __syncthreads();
     for (int e = tid; e < kRowBlock * 32; e += NT) {
         const int r = e >> 5, c = e & 31;
         const int64_t row = row0 + r;
         if (row >= row_end || col0 + c >= c2) continue;
+        float sv = 0.f;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) sv += part[w][e];
         const int64_t b = row / n;
         const int i = (int)(row - b * n);
         const int rb0 = (int)(b * n - row0);
         const float *Cb = coef + b * n * n;
         float z = 0.f;
         for (int j = 0; j < (int)n; ++j) z += Cb[i * n + j] * Zs[rb0 + j][c];
-        float v = Ss[r][c] + alpha * z;
+        float v = sv + alpha * z;
         if (bias) v += (float)bias[col0 + c];
         Y[row * c2 + col0 + c] = to_elem<E>(v);
     }
@@ -264,8 +361,12 @@ template <typename E> hipError_t launch_decode_project(const DecodeArgs<E> &a, h
     const int64_t N = a.B * a.n;
     const int K1 = a.kw + a.kc;
     dim3 grid((unsigned)((K1 + 31) / 32), (unsigned)L.splits, (unsigned)((N + kRowBlock - 1) / kRowBlock));
-    hipLaunchKernelGGL((decode_project_kernel<E>), grid, dim3(NT), 0, st, a.X, a.Aext, N, a.c1, K1, L.splits,
-                       (float *)(a.ws + L.partial));
+    if (N > 32)
+        hipLaunchKernelGGL((decode_project_kernel<E, true>), grid, dim3(NT), 0, st, a.X, a.Aext, N, a.c1, K1,
+                           L.splits, (float *)(a.ws + L.partial));
+    else
+        hipLaunchKernelGGL((decode_project_kernel<E, false>), grid, dim3(NT), 0, st, a.X, a.Aext, N, a.c1, K1,
+                           L.splits, (float *)(a.ws + L.partial));
     return hipGetLastError();
 }
 
@@ -283,9 +384,15 @@ template <typename E> hipError_t launch_decode_output(const DecodeArgs<E> &a, hi
     const int64_t N = a.B * a.n;
     const int64_t rb = rows_per_block(a.n);
     dim3 grid((unsigned)((a.c2 + 31) / 32), (unsigned)((N + rb - 1) / rb));
-    hipLaunchKernelGGL((decode_output_kernel<E>), grid, dim3(NT), 0, st, a.X, (const float *)(a.ws + L.T),
-                       (const float *)(a.ws + L.coef), a.Vs, a.Wres_t, N, a.n, a.c1, a.c2, a.kw + a.kc, a.kw, rb,
-                       a.bias, a.alpha, a.Y);
+    // the second 32-row MFMA block only when some row block has rows there
+    if (std::min<int64_t>(rb, N) > 32)
+        hipLaunchKernelGGL((decode_output_kernel<E, true>), grid, dim3(NT), 0, st, a.X,
+                           (const float *)(a.ws + L.T), (const float *)(a.ws + L.coef), a.Vs, a.Wres_t, N, a.n,
+                           a.c1, a.c2, a.kw + a.kc, a.kw, rb, a.bias, a.alpha, a.Y);
+    else
+        hipLaunchKernelGGL((decode_output_kernel<E, false>), grid, dim3(NT), 0, st, a.X,
+                           (const float *)(a.ws + L.T), (const float *)(a.ws + L.coef), a.Vs, a.Wres_t, N, a.n,
+                           a.c1, a.c2, a.kw + a.kc, a.kw, rb, a.bias, a.alpha, a.Y);
     return hipGetLastError();
 }
 

@@ -245,6 +245,16 @@ def llama_decode(m: int) -> Workload:
                     description=f"Llama-style 8B MLP decode, {m} x 1 token, r=1024, k=64")
 
 
+def workload(name: str) -> Workload:
+    """A workload by name: one of WORKLOADS or llama_decode_m<m>."""
+    if name in WORKLOADS:
+        return WORKLOADS[name]
+    prefix = "llama_decode_m"
+    if name.startswith(prefix) and name[len(prefix):].isdigit() and int(name[len(prefix):]) > 0:
+        return llama_decode(int(name[len(prefix):]))
+    raise KeyError(f"unknown workload {name!r}; known: {sorted(WORKLOADS)} and llama_decode_m<m>")
+
+
 def layer_index(w: Workload, spec: LayerSpec) -> int:
     return w.layers.index(spec)
 

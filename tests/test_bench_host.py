@@ -1,0 +1,44 @@
+"""Host-side pieces of bench.py: workload lookup, the dual-form rule and the
+algorithmic FLOP and byte counts its roofline record uses."""
+import dataclasses
+
+import pytest
+
+import bench
+from structured_rank_matmul_amd import synth
+
+
+def test_workload_lookup():
+    assert synth.workload("vitl_block") is synth.WORKLOADS["vitl_block"]
+    w = synth.workload("llama_decode_m16")
+    assert (w.B, w.n) == (16, 1)
+    assert [s.name for s in w.layers] == [s.name for s in synth.WORKLOADS["llama_prefill"].layers]
+    for bad in ("llama_decode_m0", "llama_decode_mx", "nope"):
+        with pytest.raises(KeyError):
+            synth.workload(bad)
+
+
+def test_dual_form_rule():
+    # the library takes the n x n form at n <= 16 tokens or n < k
+    spec = synth.WORKLOADS["vitl_block"].layers[0]          # k = 64
+    assert bench.dual_form(spec, 1) and bench.dual_form(spec, 16) and bench.dual_form(spec, 63)
+    assert not bench.dual_form(spec, 64) and not bench.dual_form(spec, 201)
+    small_k = dataclasses.replace(spec, k=8)
+    assert bench.dual_form(small_k, 16) and not bench.dual_form(small_k, 17)
+    assert not bench.dual_form(dataclasses.replace(spec, k=0), 1)   # k = 0: static path
+
+
+def test_decode_counts():
+    # decode FLOPs: 2N c1 (r+k) + 2N c1 c2 + 2N r c2 plus the n x n terms
+    spec = synth.workload("llama_decode_m1").layers[0]
+    N = 1
+    expect = 2 * N * spec.c1 * (spec.r + spec.k) + 2 * N * spec.c1 * spec.c2 + 2 * N * spec.r * spec.c2
+    got = bench.dyra_flops(spec, 1, 1)
+    assert expect <= got <= expect * 1.001
+    # the dominant bytes are W_res and V_s streamed once
+    by = bench.stage_bytes(spec, 1, 1, 2)["decode_output"]
+    assert by >= 2 * (spec.c1 * spec.c2 + spec.c2 * spec.r)
+    # the primal count is the stage sum of its five kernels
+    v = synth.WORKLOADS["vitl_block"].layers[1]
+    fl = bench.stage_flops(v, 128, 201)
+    assert bench.dyra_flops(v, 128, 201) == sum(fl[s] for s in bench.PRIMAL_STAGES)
