@@ -8,13 +8,13 @@
 // factored static part).
 //
 // A workgroup owns a BM x BN output tile and its WM x WN wavefronts each own a
-// (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks.  K advances in slices of 64
-// bytes per operand row (32 bf16 / 16 fp32 elements).  Slices move from global
-// memory straight into LDS (global_load_lds_dwordx4, no register staging), NS
-// of them in flight, so a slice's loads have NS - 1 slices of MFMA work to
-// land; one barrier per slice.  In LDS a slice row is four 16-byte chunks and
-// chunk c of row r sits at position c ^ ((r >> 2) & 3): the 16 rows that a
-// quarter wavefront reads with ds_read_b128 then fall on distinct banks.  Tiles
+// (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks.  K advances in slices of SB
+// bytes per operand row: 128 (whole cache lines) or, for the 256 x 256 tiles,
+// 64.  Slices move from global memory straight into LDS
+// (global_load_lds_dwordx4, no register staging), NS of them in flight, so a
+// slice's loads have NS - 1 slices of MFMA work to land; one barrier per slice.
+// In LDS a slice row is SB / 16 chunks of 16 bytes, swizzled so that the 16
+// rows a quarter wavefront reads with ds_read_b128 fall on distinct banks.  Tiles
 // are handed out XCD by XCD: workgroup ids are dealt round-robin over the 8
 // XCDs, so id i works on tile (i % 8) * ceil(T/8) + i / 8 and each XCD's L2
 // sees a contiguous band of tiles that share operand panels.
@@ -37,17 +37,19 @@ namespace dyra {
 
 namespace {
 
-// One K slice is 64 bytes of every operand row.
-template <typename E> constexpr int gemm_bk() { return 64 / (int)sizeof(E); }
+// One K slice is SB bytes of every operand row: 128 (whole cache lines) or 64
+// (shapes whose registers cannot hold the fragments of 128 plus their
+// accumulators).
+template <typename E, int SB> constexpr int gemm_bk() { return SB / (int)sizeof(E); }
 
 // MFMA operand fragment of 16-deep step h from a swizzled LDS slice row
-// (row_base = the row's first byte, sw = (row >> 2) & 3, hf = lane / 32).
+// (row_base = the row's first byte, sw = the row's chunk swizzle, hf = lane / 32).
 __device__ __forceinline__ bf16x8 slice_frag(const char *row_base, int h, int hf, int sw, const bf16 *) {
     return *reinterpret_cast<const bf16x8 *>(row_base + (((2 * h + hf) ^ sw) << 4));
 }
-__device__ __forceinline__ f32x8 slice_frag(const char *row_base, int, int hf, int sw, const float *) {
-    const f32x4 lo = *reinterpret_cast<const f32x4 *>(row_base + (((2 * hf) ^ sw) << 4));
-    const f32x4 hi = *reinterpret_cast<const f32x4 *>(row_base + (((2 * hf + 1) ^ sw) << 4));
+__device__ __forceinline__ f32x8 slice_frag(const char *row_base, int h, int hf, int sw, const float *) {
+    const f32x4 lo = *reinterpret_cast<const f32x4 *>(row_base + (((4 * h + 2 * hf) ^ sw) << 4));
+    const f32x4 hi = *reinterpret_cast<const f32x4 *>(row_base + (((4 * h + 2 * hf + 1) ^ sw) << 4));
     f32x8 r;
     r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
     r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
@@ -117,7 +119,7 @@ template <typename E> struct R1tStore {
 
 constexpr size_t kLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
 
-template <int BM, int BN, int NS> constexpr size_t stage_bytes() { return (size_t)NS * (BM + BN) * 64; }
+template <int BM, int BN, int NS, int SB> constexpr size_t stage_bytes() { return (size_t)NS * (BM + BN) * SB; }
 // LDS of the staged epilogue: the whole tile as [BM][BN + 4] (ROWS) or
 // [BN][BM + 4] elements; tiles that do not fit store straight from registers.
 template <typename E, int BM, int BN, bool ROWS> constexpr size_t epi_bytes() {
@@ -139,32 +141,41 @@ template <typename E> struct Corr {
 // ROWS = true: the epilogue receives four consecutive columns of one row (the
 // MFMA is issued with the operands swapped, so a lane holds a row of the
 // block); ROWS = false: four consecutive rows of one column.  K must be a
-// multiple of the slice (32 bf16 / 16 fp32).
-template <typename E, int BM, int BN, int WM, int WN, int NS, bool ROWS, bool CORR, class Epi>
+// multiple of 16 (a last slice may be short).
+template <typename E, int BM, int BN, int WM, int WN, int NS, int SB, bool ROWS, bool CORR, class Epi>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict__ A, int64_t lda,
                                                             const E *__restrict__ B, int64_t ldb, int64_t M,
                                                             int64_t N, int64_t K, int tiles_n, int ntiles,
                                                             int per_xcd, Corr<E> corr, Epi epi) {
     constexpr int NW = WM * WN;
     constexpr int NT = 64 * NW;
-    constexpr int BK = gemm_bk<E>();
+    constexpr int BK = gemm_bk<E, SB>();
+    constexpr int RPB = 1024 / SB;  // rows per 1 KB load block
+    static_assert(SB == 64 || SB == 128, "slice bytes");
     constexpr int VEC = 16 / (int)sizeof(E);
     constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
-    constexpr int IA = BM / 16, ITOT = (BM + BN) / 16;  // 1 KB load blocks (16 rows) per slice
+    constexpr int IA = BM / RPB, ITOT = (BM + BN) / RPB;  // 1 KB load blocks per slice
     constexpr int IPW = (ITOT + NW - 1) / NW, IMIN = ITOT / NW;
-    constexpr int STAGE = (BM + BN) * 64;  // bytes per slice
-    constexpr int KSTEPS = BK / 16;        // 16-deep MFMA steps per slice
-    static_assert(TM >= 1 && TN >= 1 && IMIN >= 1 && NS >= 2 && NS <= 4, "tile shape");
+    constexpr int STAGE = (BM + BN) * SB;  // bytes per slice
+    constexpr int KSTEPS = BK / 16;         // 16-deep MFMA steps per slice
+    static_assert(TM >= 1 && TN >= 1 && IMIN >= 1 && NS >= 2 && NS <= 4 && NW % 2 == 0, "tile shape");
     extern __shared__ __align__(16) char smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int lr = lane & 31, hf = lane >> 5;
-    const int sw = (lr >> 2) & 3;  // swizzle of the rows this lane reads
-    // a load block is 16 rows x 64 bytes; lane l fills 16-byte position l of it,
-    // i.e. row l / 4, and so fetches chunk (l % 4) ^ ((l / 16) % 4) of that row
-    const int frow = lane >> 2;
-    const int fcol = ((lane & 3) ^ ((lane >> 4) & 3)) * VEC;
+    // Slice row r holds chunk c at position c ^ sw(r): the 16 rows a quarter
+    // wavefront reads with ds_read_b128 then fall on distinct banks.
+    //   SB = 128: sw(r) = (r >> 1) & 7.  A load block is 8 rows; lane l fills
+    //     position l % 8 of row l / 8, so block j's lane l fetches chunk
+    //     (l % 8) ^ ((4 j + l / 16) % 8); j and the wavefront have the same
+    //     parity (the wavefront count is even): one column per lane.
+    //   SB = 64: sw(r) = (r >> 2) & 3.  A load block is 16 rows; lane l fills
+    //     position l % 4 of row l / 4 and fetches chunk (l % 4) ^ ((l / 16) % 4).
+    const int sw = SB == 128 ? (lr >> 1) & 7 : (lr >> 2) & 3;  // swizzle of the rows this lane reads
+    const int frow = SB == 128 ? lane >> 3 : lane >> 2;
+    const int fcol = (SB == 128 ? ((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7))
+                                : ((lane & 3) ^ ((lane >> 4) & 3))) * VEC;
     // persistent: workgroup i runs on XCD i % 8 and walks that XCD's band of
     // tiles; the stores of one tile drain while the next tile computes
     const int xcd = (int)(blockIdx.x % 8), slot = (int)(blockIdx.x / 8), nslots = (int)(gridDim.x / 8);
@@ -181,7 +192,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
     // static slices, then SC correction slices per instance of the tile
-    const int64_t S0 = K / BK;
+    const int64_t S0 = (K + BK - 1) / BK;
+    const int tail_steps = (int)(K % BK) / 16;  // 16-deep steps of a short last static slice
     int64_t S = S0, b_first = 0;
     int SC = 1;
     if constexpr (CORR) {
@@ -209,26 +221,38 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
         rhi = rlo + corr.n < M ? rlo + corr.n : M;
     };
     // static-slice source of this wave's q-th load block (rows clamped into
-    // range: rows past M or N are computed and never stored)
+    // range: rows past M or N are computed and never stored).  For SB = 64 the
+    // lane's column is folded in here; SB = 128 adds it per slice (each form
+    // measured faster for its shapes).
+    constexpr int64_t FC_IN_BASE = SB == 64;
     const E *base[IPW];
 #pragma unroll
     for (int q = 0; q < IPW; ++q) {
         const int j = wave + q * NW;
         if (j < IA) {
-            const int64_t r = row0 + 16 * j + frow;
-            base[q] = A + (r < M ? r : M - 1) * lda + fcol;
+            const int64_t r = row0 + RPB * j + frow;
+            base[q] = A + (r < M ? r : M - 1) * lda + (FC_IN_BASE ? fcol : 0);
         } else {
-            const int64_t r = col0 + 16 * (j - IA) + frow;
-            base[q] = B + (r < N ? r : N - 1) * ldb + fcol;
+            const int64_t r = col0 + RPB * (j - IA) + frow;
+            base[q] = B + (r < N ? r : N - 1) * ldb + (FC_IN_BASE ? fcol : 0);
         }
     }
     auto issue = [&](int64_t s) {
         char *dst = smem + (int)(s % NS) * STAGE;
         if (!CORR || s < S0) {
+            // a K tail shorter than the slice fetches its missing columns from
+            // column 0; they meet no MFMA
+            int64_t off;
+            if constexpr (FC_IN_BASE) {
+                off = (s + 1) * BK <= K ? s * BK : (s * BK + fcol < K ? s * BK : -(int64_t)fcol);
+            } else {
+                const int64_t kc0 = s * BK + fcol;
+                off = kc0 < K ? kc0 : 0;
+            }
 #pragma unroll
             for (int q = 0; q < IPW; ++q) {
                 const int j = wave + q * NW;
-                if (q < IMIN || j < ITOT) lds_dma16(base[q] + s * BK, dst + j * 1024);
+                if (q < IMIN || j < ITOT) lds_dma16(base[q] + off, dst + j * 1024);
             }
         } else {
             int64_t b, rlo, rhi;
@@ -243,10 +267,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
                 if (!(q < IMIN || j < ITOT)) continue;
                 const E *g;
                 if (j < IA) {
-                    const int64_t r = row0 + 16 * j + frow;
+                    const int64_t r = row0 + RPB * j + frow;
                     g = A + (r < M ? r : M - 1) * lda + corr.kcol + kl;
                 } else {
-                    const int64_t r = col0 + 16 * (j - IA) + frow;
+                    const int64_t r = col0 + RPB * (j - IA) + frow;
                     g = corr.R1t + (b * N + (r < N ? r : N - 1)) * corr.kc + kl;
                 }
                 lds_dma16(g, dst + j * 1024);
@@ -258,8 +282,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
     // One K slice.  CS: a correction slice (instance rows masked, possibly
     // fewer 16-deep steps); the static slices are compiled without any of
     // that, as one run of MFMAs.
-    auto slice = [&](int64_t s, auto CS) __attribute__((always_inline)) {
-        constexpr bool CSL = decltype(CS)::value;
+    auto slice = [&](int64_t s, auto KS) __attribute__((always_inline)) {
+        constexpr int KIND = decltype(KS)::value;  // 0 static, 1 short last static slice, 2 correction
+        constexpr bool CSL = KIND == 2;
         // this wave's loads of slice s have landed once at most `later` slices'
         // worth (issued after it) are outstanding; the barrier then makes every
         // wave's part visible and frees the buffer of slice s - 1
@@ -270,7 +295,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
         barrier_only();
         if (s + NS - 1 < S) issue(s + NS - 1);
 
-        int ksteps = KSTEPS;
+        int ksteps = KIND == 1 ? tail_steps : KSTEPS;
         uint32_t live = ~0u;
         int64_t rlo = 0, rhi = 0;
         if constexpr (CSL) {
@@ -287,41 +312,48 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
                 live |= (rb < rhi && rb + 32 > rlo) ? (1u << i) : 0u;
             }
         }
-        const char *sa = smem + (int)(s % NS) * STAGE + ((wm * TM) * 32 + lr) * 64;
-        const char *sb = smem + (int)(s % NS) * STAGE + BM * 64 + ((wn * TN) * 32 + lr) * 64;
-        // all fragments of the slice are requested before the first MFMA, so
-        // only the first step waits on LDS latency
-        typename Frag<E>::type fa[KSTEPS][TM], fb[KSTEPS][TN];
+        const char *sa = smem + (int)(s % NS) * STAGE + ((wm * TM) * 32 + lr) * SB;
+        const char *sb = smem + (int)(s % NS) * STAGE + BM * SB + ((wn * TN) * 32 + lr) * SB;
+        // the fragments of two 16-deep steps are requested before their first
+        // MFMA, so each pair waits on LDS latency once
+        constexpr int KG = KSTEPS < 2 ? KSTEPS : 2;
 #pragma unroll
-        for (int h = 0; h < KSTEPS; ++h) {
-            if (CSL && h >= ksteps) break;
+        for (int h0 = 0; h0 < KSTEPS; h0 += KG) {
+            if (KIND != 0 && h0 >= ksteps) break;
+            typename Frag<E>::type fa[KG][TM], fb[KG][TN];
 #pragma unroll
-            for (int j = 0; j < TN; ++j) fb[h][j] = slice_frag(sb + j * 32 * 64, h, hf, sw, (const E *)nullptr);
+            for (int g = 0; g < KG; ++g) {
+                const int h = h0 + g;
+                if (KIND != 0 && h >= ksteps) break;
 #pragma unroll
-            for (int i = 0; i < TM; ++i) fa[h][i] = slice_frag(sa + i * 32 * 64, h, hf, sw, (const E *)nullptr);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+                for (int j = 0; j < TN; ++j) fb[g][j] = slice_frag(sb + j * 32 * SB, h, hf, sw, (const E *)nullptr);
 #pragma unroll
-        for (int h = 0; h < KSTEPS; ++h) {
-            if (CSL && h >= ksteps) break;
+                for (int i = 0; i < TM; ++i) fa[g][i] = slice_frag(sa + i * 32 * SB, h, hf, sw, (const E *)nullptr);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                typename Frag<E>::type a = fa[h][i];
-                if constexpr (CSL) {
-                    if (!((live >> i) & 1u)) continue;
-                    const int64_t r = row0 + (wm * TM + i) * 32 + lr;
-                    if (!(r >= rlo && r < rhi)) a = zero_frag(a);
+            for (int g = 0; g < KG; ++g) {
+                if (KIND != 0 && h0 + g >= ksteps) break;
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    typename Frag<E>::type a = fa[g][i];
+                    if constexpr (CSL) {
+                        if (!((live >> i) & 1u)) continue;
+                        const int64_t r = row0 + (wm * TM + i) * 32 + lr;
+                        if (!(r >= rlo && r < rhi)) a = zero_frag(a);
+                    }
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = ROWS ? mma16(acc[i][j], fb[g][j], a) : mma16(acc[i][j], a, fb[g][j]);
                 }
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = ROWS ? mma16(acc[i][j], fb[h][j], a) : mma16(acc[i][j], a, fb[h][j]);
             }
         }
     };
     int64_t s = 0;
-    for (; s < S0; ++s) slice(s, std::false_type{});
+    for (; s < S0 - (tail_steps ? 1 : 0); ++s) slice(s, std::integral_constant<int, 0>{});
+    if (tail_steps) slice(s++, std::integral_constant<int, 1>{});
     if constexpr (CORR) {
-        for (; s < S; ++s) slice(s, std::true_type{});
+        for (; s < S; ++s) slice(s, std::integral_constant<int, 2>{});
     }
     __syncthreads();
     // ---- epilogue.  A lane holds four consecutive elements of the store's
@@ -377,19 +409,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
     }
 }
 
-template <typename E, int BM, int BN, int NS, bool ROWS> constexpr size_t gemm_smem() {
-    return (epi_staged<E, BM, BN, ROWS>() && epi_bytes<E, BM, BN, ROWS>() > stage_bytes<BM, BN, NS>())
+template <typename E, int BM, int BN, int NS, int SB, bool ROWS> constexpr size_t gemm_smem() {
+    return (epi_staged<E, BM, BN, ROWS>() && epi_bytes<E, BM, BN, ROWS>() > stage_bytes<BM, BN, NS, SB>())
                ? epi_bytes<E, BM, BN, ROWS>()
-               : stage_bytes<BM, BN, NS>();
+               : stage_bytes<BM, BN, NS, SB>();
 }
 
-template <typename E, int BM, int BN, int WM, int WN, int NS, bool ROWS, bool CORR, class Epi>
+template <typename E, int BM, int BN, int WM, int WN, int NS, int SB, bool ROWS, bool CORR, class Epi>
 hipError_t gemm_launch(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N, int64_t K,
                        const Corr<E> &corr, Epi epi, hipStream_t st) {
-    static_assert(gemm_smem<E, BM, BN, NS, ROWS>() <= kLdsBytes, "LDS");
-    if (K % gemm_bk<E>() != 0) return hipErrorInvalidValue;
-    auto kfn = gemm_kernel<E, BM, BN, WM, WN, NS, ROWS, CORR, Epi>;
-    constexpr size_t smem = gemm_smem<E, BM, BN, NS, ROWS>();
+    static_assert(gemm_smem<E, BM, BN, NS, SB, ROWS>() <= kLdsBytes, "LDS");
+    if (K % 16 != 0) return hipErrorInvalidValue;
+    auto kfn = gemm_kernel<E, BM, BN, WM, WN, NS, SB, ROWS, CORR, Epi>;
+    constexpr size_t smem = gemm_smem<E, BM, BN, NS, SB, ROWS>();
     static int per_cu = 0;  // resident workgroups per CU
     if (per_cu == 0) {
         hipError_t e = hipFuncSetAttribute((const void *)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
@@ -437,11 +469,11 @@ template <typename E, bool ROWS, bool CORR, class Epi>
 hipError_t gemm_dispatch(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N, int64_t K,
                          const Corr<E> &corr, Epi epi, hipStream_t st) {
     switch (pick_shape(M, N)) {
-    case Shape::T256x256: return gemm_launch<E, 256, 256, 4, 2, 4, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
-    case Shape::T256x160: return gemm_launch<E, 256, 160, 8, 1, 4, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
-    case Shape::T256x128: return gemm_launch<E, 256, 128, 4, 2, 4, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
-    case Shape::T128x128: return gemm_launch<E, 128, 128, 2, 2, 4, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
-    case Shape::T64x64: return gemm_launch<E, 64, 64, 2, 2, 4, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
+    case Shape::T256x256: return gemm_launch<E, 256, 256, 4, 2, 4, 64, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
+    case Shape::T256x160: return gemm_launch<E, 256, 160, 8, 1, 3, 128, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
+    case Shape::T256x128: return gemm_launch<E, 256, 128, 4, 2, 3, 128, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
+    case Shape::T128x128: return gemm_launch<E, 128, 128, 2, 2, 4, 128, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
+    case Shape::T64x64: return gemm_launch<E, 64, 64, 2, 2, 4, 128, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
     }
     return hipErrorInvalidValue;
 }
