@@ -9,8 +9,8 @@
 //
 // A workgroup owns a BM x BN output tile and its WM x WN wavefronts each own a
 // (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks.  K advances in slices of SB
-// bytes per operand row: 128 (whole cache lines) or, for the 256 x 256 tiles,
-// 64.  Slices move from global memory straight into LDS
+// bytes per operand row: 128 (whole cache lines) or, for the 256 x 256 tiles
+// with correction slices, 64.  Slices move from global memory straight into LDS
 // (global_load_lds_dwordx4, no register staging), NS of them in flight, so a
 // slice's loads have NS - 1 slices of MFMA work to land; one barrier per slice.
 // In LDS a slice row is SB / 16 chunks of 16 bytes, swizzled so that the 16
@@ -261,17 +261,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
             ipos.next(SC);
             int kl = sc * BK + fcol;
             kl = kl < corr.kc ? kl : 0;  // columns past kc are fetched from column 0 and never used
+            // A rows: the static source shifted to Q's columns; B rows: R1_b
+            const int64_t offA = corr.kcol + kl - (FC_IN_BASE ? fcol : 0);
+            const E *gB = corr.R1t + b * N * corr.kc + kl;
 #pragma unroll
             for (int q = 0; q < IPW; ++q) {
                 const int j = wave + q * NW;
                 if (!(q < IMIN || j < ITOT)) continue;
                 const E *g;
                 if (j < IA) {
-                    const int64_t r = row0 + RPB * j + frow;
-                    g = A + (r < M ? r : M - 1) * lda + corr.kcol + kl;
+                    g = base[q] + offA;
                 } else {
-                    const int64_t r = col0 + RPB * (j - IA) + frow;
-                    g = corr.R1t + (b * N + (r < N ? r : N - 1)) * corr.kc + kl;
+                    // (32-bit: N counts output features, N * kc < 2^31)
+                    const int r = (int)col0 + RPB * (j - IA) + frow;
+                    g = gB + (int64_t)((r < N ? r : (int)N - 1) * corr.kc);
                 }
                 lds_dma16(g, dst + j * 1024);
             }
@@ -469,7 +472,12 @@ template <typename E, bool ROWS, bool CORR, class Epi>
 hipError_t gemm_dispatch(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N, int64_t K,
                          const Corr<E> &corr, Epi epi, hipStream_t st) {
     switch (pick_shape(M, N)) {
-    case Shape::T256x256: return gemm_launch<E, 256, 256, 4, 2, 4, 64, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
+    case Shape::T256x256:
+        // the correction kernel and float32 keep 64-byte slices (128 would
+        // spill them)
+        if constexpr (CORR || sizeof(E) == 4)
+            return gemm_launch<E, 256, 256, 4, 2, 4, 64, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
+        else return gemm_launch<E, 256, 256, 4, 2, 2, 128, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
     case Shape::T256x160: return gemm_launch<E, 256, 160, 8, 1, 3, 128, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
     case Shape::T256x128: return gemm_launch<E, 256, 128, 4, 2, 3, 128, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
     case Shape::T128x128: return gemm_launch<E, 128, 128, 2, 2, 4, 128, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
