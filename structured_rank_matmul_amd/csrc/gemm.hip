@@ -78,7 +78,9 @@ template <typename E> __device__ __forceinline__ typename Pack4<E>::type pack4(c
 // (row-major stores) or of four consecutive rows of column j (R1t stores).
 // store4 then writes the rounded four.
 
-// Row-major D: store4(i, j, p) writes columns j..j+3 of row i.  With a bias
+// Row-major D: store4(i, j, p) writes columns j..j+3 of row i, as a
+// non-temporal store (the outputs of these products are not read again by the
+// kernel; streaming them keeps them from evicting cached operands).  With a bias
 // (the fused linear layer of §2.4: Y = X_tmp A^T + b + alpha L R) every row
 // gets bias[j] added to column j before rounding.
 template <typename E> struct RowStore {
@@ -94,7 +96,14 @@ template <typename E> struct RowStore {
         }
     }
     __device__ __forceinline__ void store4(int64_t i, int64_t j, const typename Pack4<E>::type &p) const {
-        *reinterpret_cast<typename Pack4<E>::type *>(D + i * ldd + j) = p;
+        if constexpr (sizeof(E) == 2) {
+            typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
+            const u32x2v v = {p.x, p.y};
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x2v *>(D + i * ldd + j));
+        } else {
+            const u32x4 v = {p.x, p.y, p.z, p.w};
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(D + i * ldd + j));
+        }
     }
 };
 
