@@ -9,8 +9,8 @@
 //
 // A workgroup owns a BM x BN output tile and its WM x WN wavefronts each own a
 // (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks.  K advances in slices of SB
-// bytes per operand row: 128 (whole cache lines) or, for the 256 x 256 tiles
-// with correction slices, 64.  Slices move from global memory straight into LDS
+// bytes per operand row: 128 (whole cache lines) or, for float32 256 x 256
+// tiles, 64.  Slices move from global memory straight into LDS
 // (global_load_lds_dwordx4, no register staging), NS of them in flight, so a
 // slice's loads have NS - 1 slices of MFMA work to land; one barrier per slice.
 // In LDS a slice row is SB / 16 chunks of 16 bytes, swizzled so that the 16
@@ -328,7 +328,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
         const char *sb = smem + (int)(s % NS) * STAGE + BM * SB + ((wn * TN) * 32 + lr) * SB;
         // the fragments of two 16-deep steps are requested before their first
         // MFMA, so each pair waits on LDS latency once
-        constexpr int KG = KSTEPS < 2 ? KSTEPS : 2;
+        // (the 256 x 256 correction kernel reads one step at a time: two
+        // steps' fragments do not fit beside its accumulators and addresses)
+        constexpr int KG = (CORR && SB == 128 && BM * BN >= 65536) ? 1 : (KSTEPS < 2 ? KSTEPS : 2);
 #pragma unroll
         for (int h0 = 0; h0 < KSTEPS; h0 += KG) {
             if (KIND != 0 && h0 >= ksteps) break;
@@ -482,9 +484,8 @@ hipError_t gemm_dispatch(const E *A, int64_t lda, const E *B, int64_t ldb, int64
                          const Corr<E> &corr, Epi epi, hipStream_t st) {
     switch (pick_shape(M, N)) {
     case Shape::T256x256:
-        // the correction kernel and float32 keep 64-byte slices (128 would
-        // spill them)
-        if constexpr (CORR || sizeof(E) == 4)
+        // float32 keeps 64-byte slices (128 would spill it)
+        if constexpr (sizeof(E) == 4)
             return gemm_launch<E, 256, 256, 4, 2, 4, 64, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
         else return gemm_launch<E, 256, 256, 4, 2, 2, 128, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
     case Shape::T256x160: return gemm_launch<E, 256, 160, 8, 1, 3, 128, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
