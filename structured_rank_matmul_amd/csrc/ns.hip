@@ -85,7 +85,22 @@ __global__ __launch_bounds__(NT) void ns_factor_kernel(const E *__restrict__ T, 
     for (int64_t c0 = 0; c0 < n; c0 += TT) {
         __syncthreads();  // the previous chunk's reads are done
         const int64_t t = c0 + tid;
-        for (int m = 0; m < KC; ++m) Lt[m * ST + tid] = t < n ? Tb[t * ldt + m] : to_elem<E>(0.f);
+        // the token's KC values as 16-byte loads, issued unconditionally (a
+        // token past n rereads token n - 1 and is zeroed): guarded loads
+        // compile to one branch and one full wait each
+        constexpr int NV = KC * (int)sizeof(E) / 16;
+        const E *row = Tb + (t < n ? t : n - 1) * ldt;
+        u32x4 raw[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) raw[v] = *reinterpret_cast<const u32x4 *>(row + v * (16 / (int)sizeof(E)));
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            union { u32x4 u; E e[16 / sizeof(E)]; } w;
+            w.u = raw[v];
+#pragma unroll
+            for (int q = 0; q < 16 / (int)sizeof(E); ++q)
+                Lt[(v * (16 / (int)sizeof(E)) + q) * ST + tid] = t < n ? w.e[q] : to_elem<E>(0.f);
+        }
         __syncthreads();
 #pragma unroll 4
         for (int kk = 0; kk < TT; kk += 16)

@@ -60,9 +60,12 @@ __device__ __forceinline__ void load_transposed(const E *src, int64_t ld, int64_
         const int tok = c % TK;
         const int j0 = (c / TK) * VEC;
         union { uint4 u; E e[VEC]; } v;
-        v.u = (t0 + tok < tokens && col0 + j0 < cols_valid)
-                  ? *reinterpret_cast<const uint4 *>(src + (t0 + tok) * ld + col0 + j0)
-                  : make_uint4(0, 0, 0, 0);
+        // unconditional load of a clamped entry, zeroed after (a guarded load
+        // compiles to a branch and a full wait)
+        const bool ok = t0 + tok < tokens && col0 + j0 < cols_valid;
+        v.u = *reinterpret_cast<const uint4 *>(src + (t0 + tok < tokens ? t0 + tok : tokens - 1) * ld +
+                                               (col0 + j0 < cols_valid ? col0 + j0 : 0));
+        if (!ok) v.u = make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int q = 0; q < VEC; ++q) dst[(j0 + q) * ST + tok] = v.e[q];
     }
@@ -226,9 +229,13 @@ __global__ __launch_bounds__(NT) void gram_q_f32_kernel(float *__restrict__ T, i
     // ---- G = L1_b^T L1_b, token slices staged row-major in Lt ([token][feature])
     for (int64_t t0 = 0; t0 < n; t0 += TK) {
         __syncthreads();
+        // loads are unconditional (clamped to a valid entry, zeroed after):
+        // a guarded load compiles to a branch and a full wait per element
         for (int e = tid; e < TK * 64; e += NT) {
             const int tt = e >> 6, c = e & 63;
-            Lt[tt * 64 + c] = (t0 + tt < n && c < kc) ? Lb[(t0 + tt) * ldt + c] : 0.f;
+            const bool ok = t0 + tt < n && c < kc;
+            const float v = Lb[(t0 + tt < n ? t0 + tt : n - 1) * ldt + (c < kc ? c : 0)];
+            Lt[tt * 64 + c] = ok ? v : 0.f;
         }
         __syncthreads();
         const int tc = (int)((n - t0) < TK ? (n - t0) : TK);
@@ -327,8 +334,12 @@ __global__ __launch_bounds__(NT) void gram_q_f32_kernel(float *__restrict__ T, i
     float *Qb = Qt + b * kc * npad;
     for (int64_t t = tid; t < npad; t += NT) {
         AT l[64];
+        const int64_t tc = t < n ? t : n - 1;
 #pragma unroll
-        for (int c = 0; c < 64; ++c) l[c] = (t < n && c < kc) ? (AT)Lb[t * ldt + c] : AT(0);
+        for (int c = 0; c < 64; ++c) {
+            const float v = Lb[tc * ldt + (c < kc ? c : 0)];
+            l[c] = (t < n && c < kc) ? (AT)v : AT(0);
+        }
         for (int i = 0; i < kc; ++i) {
             AT sum = AT(0);
 #pragma unroll
