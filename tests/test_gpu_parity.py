@@ -62,6 +62,14 @@ def test_dense_ref_matches_exact(dtype, N, c1, c2):
     assert rel(to_host(Y), to_host(Yt)) <= (5e-3 if dtype == "bf16" else 1e-6)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("N,c1,c2", [(8192, 352, 4096), (8192, 352, 3072), (25600, 352, 320)])
+def test_dense_ref_k_tail_on_large_tiles(dtype, N, c1, c2):
+    """K = 352 is 5.5 slices of 64 bf16 elements: the last slice is short.
+    These sizes select the 256 x 256, 256 x 128 and 256 x 160 tiles."""
+    test_dense_ref_matches_exact(dtype, N, c1, c2)
+
+
 def test_dense_ref_empty_is_noop():
     import torch
     Wt = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda:0")
@@ -91,6 +99,16 @@ def test_forward_small(dtype, case):
     W = synth.random_weight(c1, c2, 11 + c1, p=0.5)
     X = synth.random_matrix(B * n, c1, 12 + n, dtype)
     run_case(W, X, B, n, r, k, 0.0, dtype)
+
+
+def test_forward_k_tail_on_large_tiles():
+    """32 instances of 201 tokens into 4096 outputs select the 256 x 256
+    output tiles with correction slices; r = 96 leaves a short last static
+    slice there (K = 96) and c1 = 352 one in the left pass."""
+    B, n, c1, c2, r, k = 32, 201, 352, 4096, 96, 64
+    W = synth.random_weight(c1, c2, 61, p=0.6)
+    X = synth.random_matrix(B * n, c1, 62, "bf16")
+    run_case(W, X, B, n, r, k, 0.0, "bf16")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
