@@ -70,6 +70,25 @@ def test_dense_ref_k_tail_on_large_tiles(dtype, N, c1, c2):
     test_dense_ref_matches_exact(dtype, N, c1, c2)
 
 
+def _random_gemm_shapes(count=12, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        N = int(rng.integers(1, 3000))
+        c1 = 32 * int(rng.integers(1, 24))   # odd multiples of 32 leave a short last slice
+        c2 = 32 * int(rng.integers(1, 80))
+        out.append((N, c1, c2))
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("N,c1,c2", _random_gemm_shapes())
+def test_dense_ref_random_shapes(dtype, N, c1, c2):
+    """Seeded random shapes: ragged rows and columns against every tile size,
+    K an odd or even multiple of 32."""
+    test_dense_ref_matches_exact(dtype, N, c1, c2)
+
+
 def test_dense_ref_empty_is_noop():
     import torch
     Wt = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda:0")
