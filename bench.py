@@ -118,7 +118,10 @@ def time_loop(fn, steps, warmup, stream, per_step=False):
 
 
 def cpu_baseline(workload, plans_orc, X_host, budget_s):
-    """Oracle inference on the first instances of every layer until ~budget_s of CPU time."""
+    """Oracle inference, instance by instance through every layer, until ~budget_s of CPU time.
+
+    When the whole batch takes less than the budget the instances are taken again
+    from the first, so that the sample is long enough to time; at most 8 passes."""
     import oracle as orc
     try:
         from threadpoolctl import threadpool_info
@@ -127,18 +130,23 @@ def cpu_baseline(workload, plans_orc, X_host, budget_s):
         threads = os.cpu_count()
     n = workload.n
     done, t_total = 0, 0.0
-    while done < workload.B:
+    while done < 8 * workload.B:
+        b = done % workload.B
         t0 = time.perf_counter()
         for li, spec in enumerate(workload.layers):
-            Xb = X_host[li][done * n:(done + 1) * n]
+            Xb = X_host[li][b * n:(b + 1) * n]
             orc.inference(Xb, 1, n, plans_orc[li])
         t_total += time.perf_counter() - t0
         done += 1
         if t_total >= budget_s:
             break
     tokens = done * n
+    if done <= workload.B:
+        what = f"{done} of {workload.B} instances"
+    else:
+        what = f"{done / workload.B:.2f} passes over the {workload.B} instances"
     return {"value": tokens / t_total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {workload.B} instances ({tokens} tokens) through all {len(workload.layers)} "
+            "sample": f"{what} ({tokens} tokens) through all {len(workload.layers)} "
                       f"layers, float64 numpy, {t_total:.1f} s"}
 
 

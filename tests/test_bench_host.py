@@ -42,3 +42,22 @@ def test_decode_counts():
     v = synth.WORKLOADS["vitl_block"].layers[1]
     fl = bench.stage_flops(v, 128, 201)
     assert bench.dyra_flops(v, 128, 201) == sum(fl[s] for s in bench.PRIMAL_STAGES)
+
+
+def test_cpu_baseline_cycles_to_budget():
+    # a batch that finishes well inside the budget is taken again from the first
+    # instance, at most 8 passes; the rate counts every instance done
+    import types
+
+    import numpy as np
+
+    import oracle as orc
+    W = np.random.default_rng(3).standard_normal((16, 24))
+    plan = orc.offline_preparation(W, 4, 2, 0.0)
+    X = np.random.default_rng(4).standard_normal((2 * 5, 16))
+    w = types.SimpleNamespace(B=2, n=5, layers=[None])
+    r = bench.cpu_baseline(w, [plan], [X], budget_s=60.0)
+    assert r["kind"] == "oracle" and r["value"] > 0
+    assert r["sample"].startswith("8.00 passes over the 2 instances (80 tokens)")
+    r = bench.cpu_baseline(w, [plan], [X], budget_s=0.0)
+    assert r["sample"].startswith("1 of 2 instances (5 tokens)")
