@@ -35,6 +35,12 @@ Readings taken where the paper is silent (all listed with the design notes):
   * Where lambda = 0 and L^(1)'s Gram is singular (fewer tokens than the
     correction rank), L^(1) R^(1) is taken as its lambda -> 0+ limit, the
     minimum-norm least-squares solution, which is unique as a product.
+  * BLAST as the structured approximation (Appendix B, BLAST): the page prints
+    the block coupling S_ij as an r x r matrix, but the BLAST ranks swept in
+    Appendix D reach the FLOPs reductions of Fig. 4 only with a diagonal
+    coupling (an r x r one would cost more than the dense product at the
+    larger ranks), so S_ij = diag(s_ij) is taken.  The paper leaves the fit of
+    the factors open; they are inputs here.
   * Eq. 6 and Algorithm 1 carry no bias and no scale.  §2.4's fused linear
     layer adds a bias b and weights the correction by alpha; both are optional
     arguments here, and alpha = 1 without a bias is Eq. 6.
@@ -60,6 +66,7 @@ class OraclePlan:
     lam: float
     r_w: int
     r_c: int
+    nb: int = 0          # BLAST blocks per side (0: the truncated-SVD W_hat)
 
 
 def truncated_svd(W: np.ndarray, r: int):
@@ -92,6 +99,17 @@ def offline_preparation(W: np.ndarray, r_w: int, r_c: int, lam: float = 0.0,
     else:
         A_s, Vt_s = np.zeros((c1, 0)), np.zeros((0, c2))
     W_hat = A_s @ Vt_s
+    W_res, R0, P_L = _residual_projection(W, W_hat, r_c, lam, R0)
+    return OraclePlan(W=W, W_hat=W_hat, W_res=W_res, A_s=A_s, V_s=Vt_s.T.copy(), R0=R0,
+                      P_L=P_L, lam=float(lam), r_w=r_w, r_c=r_c)
+
+
+def _residual_projection(W: np.ndarray, W_hat: np.ndarray, r_c: int, lam: float,
+                         R0: Optional[np.ndarray]):
+    """Algorithm 1 Offline Preparation after the structured approximation:
+    W_res <- W - W_hat (Eq. 1); R^(0) (default: top-r_c right singular vectors
+    of W_res, Appendix D); P_L <- (W_res R0^T)(R0 R0^T + lambda I)^-1 (Eq. 7)."""
+    c1, c2 = W.shape
     W_res = W - W_hat
     if R0 is None:
         if r_c > 0:
@@ -103,8 +121,52 @@ def offline_preparation(W: np.ndarray, r_w: int, r_c: int, lam: float = 0.0,
     gram = R0 @ R0.T + lam * np.eye(r_c)
     # P_L = (W_res R0^T) gram^-1, written as a solve against gram^T = gram
     P_L = np.linalg.solve(gram.T, (W_res @ R0.T).T).T if r_c > 0 else np.zeros((c1, 0))
-    return OraclePlan(W=W, W_hat=W_hat, W_res=W_res, A_s=A_s, V_s=Vt_s.T.copy(), R0=R0,
-                      P_L=P_L, lam=float(lam), r_w=r_w, r_c=r_c)
+    return W_res, R0, P_L
+
+
+def blast_matrix(U: np.ndarray, S: np.ndarray, V: np.ndarray, nb: int) -> np.ndarray:
+    """The BLAST structured matrix W_hat [c1, c2] from its factors (Appendix B, BLAST).
+
+    W is cut into an nb x nb grid of p x q blocks (p = c1 / nb, q = c2 / nb).
+    Block (i, j) is U_i diag(s_ij) V_j^T, where U_i [p, r] (rows i p .. i p + p - 1
+    of U [c1, r]) is shared by block row i, V_j [q, r] (rows of V [c2, r]) by
+    block column j, and s_ij = S[i, j] [r] is the block's own coupling.
+    """
+    U = np.asarray(U, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    c1, r = U.shape
+    c2 = V.shape[0]
+    if nb < 1 or c1 % nb or c2 % nb or V.shape[1] != r or S.shape != (nb, nb, r):
+        raise ValueError("BLAST factor shapes do not match")
+    p, q = c1 // nb, c2 // nb
+    W_hat = np.zeros((c1, c2))
+    for i in range(nb):
+        for j in range(nb):
+            U_i = U[i * p:(i + 1) * p]
+            V_j = V[j * q:(j + 1) * q]
+            W_hat[i * p:(i + 1) * p, j * q:(j + 1) * q] = (U_i * S[i, j]) @ V_j.T
+    return W_hat
+
+
+def offline_preparation_blast(W: np.ndarray, U: np.ndarray, S: np.ndarray, V: np.ndarray, nb: int,
+                              r_c: int, lam: float = 0.0, R0: Optional[np.ndarray] = None) -> OraclePlan:
+    """Algorithm 1 Offline Preparation with a BLAST W_hat (Appendix B; §1 and
+    §2.3 pair DyRA with any structured approximation).
+
+    1. W_hat <- the BLAST matrix of the given factors (their fit is the
+       caller's: the paper obtains them by minimising ||W - W_hat||);
+    2-4. as for the truncated SVD: W_res, R^(0), P_L (Eq. 1, Appendix D, Eq. 7).
+    """
+    W = np.asarray(W, dtype=np.float64)
+    c1, c2 = W.shape
+    r = np.asarray(U).shape[1]
+    if not (r_c >= 0 and r_c <= min(c1, c2)):
+        raise ValueError("ranks out of range")
+    W_hat = blast_matrix(U, S, V, nb)
+    W_res, R0, P_L = _residual_projection(W, W_hat, r_c, lam, R0)
+    return OraclePlan(W=W, W_hat=W_hat, W_res=W_res, A_s=np.zeros((c1, 0)), V_s=np.zeros((c2, 0)),
+                      R0=R0, P_L=P_L, lam=float(lam), r_w=r, r_c=r_c, nb=nb)
 
 
 def right_factor(L1: np.ndarray, X: np.ndarray, W_res: np.ndarray, lam: float) -> np.ndarray:

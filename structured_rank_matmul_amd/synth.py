@@ -14,6 +14,13 @@ of R), ``m = min(c1, c2)`` and a power-law spectrum ``s_i = i^-p``.  They are
 drawn in float64 and handed to the library as float32; the float32 array is
 the weight (the oracle upcasts exactly that array).
 
+BLAST-structured weights (the second static family the paper pairs with
+DyRA) are drawn from factors: block (i, j) of an nb x nb grid is
+``U_i diag(s_ij) V_j^T`` with Gaussian ``U_i``, ``V_j`` and couplings
+``s_ij`` on a power-law decay, plus a power-law residual of a set relative
+size.  The drawn factors are then known inputs for the static part; no fit
+is made here.
+
 Activations are drawn in float64 and rounded once to the compute dtype
 (float32 round-to-nearest-even, then bfloat16 round-to-nearest-even for bf16
 configs).  The rounded values are the input; ``exact`` returns them upcast to
@@ -115,6 +122,59 @@ def draw_weight(c1: int, c2: int, p: float, kaiming: bool, rng: np.random.Genera
     q2 = haar_orthogonal(rng, c2, m)
     w = (q1 * s) @ q2.T
     return np.ascontiguousarray(w.astype(np.float32)), s
+
+
+ROLE_BLAST = 4
+
+
+@dataclasses.dataclass
+class BlastWeight:
+    """A BLAST-structured weight and its factors (all as handed to the library)."""
+    W: np.ndarray    # float32 [c1, c2]
+    U: np.ndarray    # float32 [c1, r]   block row i = rows i*c1/nb ..
+    S: np.ndarray    # float32 [nb, nb, r] diagonal couplings s_ij
+    V: np.ndarray    # float32 [c2, r]   block column j = rows j*c2/nb ..
+    nb: int
+
+
+def draw_blast_weight(c1: int, c2: int, nb: int, r: int, rng: np.random.Generator, p: float = 0.7,
+                      residual: float = 0.35) -> BlastWeight:
+    """W = [U_i diag(s_ij) V_j^T]_ij + E with ||E||_F = residual * ||structured part||_F.
+
+    U_i [c1/nb, r] and V_j [c2/nb, r] are Gaussian with unit-norm expected
+    columns; s_ij[c] = (c + 1)^-p (1 + 0.5 g), g standard normal per block and
+    rank index; E has Haar singular vectors and the spectrum i^-p.  The
+    factors are rounded to float32 first and the structured part is formed
+    from the rounded values, so they describe the float32 W's structure up to
+    W's own rounding.
+    """
+    if nb < 1 or c1 % nb or c2 % nb:
+        raise ValueError("block count must divide both dimensions")
+    pr, qr = c1 // nb, c2 // nb
+    U = (rng.standard_normal((c1, r)) / np.sqrt(pr)).astype(np.float32)
+    V = (rng.standard_normal((c2, r)) / np.sqrt(qr)).astype(np.float32)
+    decay = power_spectrum(r, p)
+    S = (decay[None, None, :] * (1.0 + 0.5 * rng.standard_normal((nb, nb, r)))).astype(np.float32)
+    Ub = U.astype(np.float64).reshape(nb, pr, r)
+    Vb = V.astype(np.float64).reshape(nb, qr, r)
+    structured = np.einsum("iac,ijc,jbc->iajb", Ub, S.astype(np.float64), Vb).reshape(c1, c2)
+    m = min(c1, c2)
+    E = (haar_orthogonal(rng, c1, m) * power_spectrum(m, p)) @ haar_orthogonal(rng, c2, m).T
+    E *= residual * np.linalg.norm(structured) / np.linalg.norm(E)
+    W = np.ascontiguousarray((structured + E).astype(np.float32))
+    return BlastWeight(W=W, U=U, S=S, V=V, nb=nb)
+
+
+def make_blast_weight(w: "Workload", spec: "LayerSpec", nb: int, r: int, seed: int = 0) -> BlastWeight:
+    """A BLAST-structured stand-in for one layer's weight (rank r, nb x nb blocks)."""
+    rng = rng_for(seed, w.cfg_id, layer_index(w, spec), ROLE_BLAST + 10 * nb)
+    return draw_blast_weight(spec.c1, spec.c2, nb, r, rng, p=spec.p)
+
+
+def random_blast_weight(c1: int, c2: int, nb: int, r: int, seed: int, residual: float = 0.35) -> BlastWeight:
+    """A small BLAST-structured weight for tests."""
+    rng = rng_for(seed, 97, c1 * 100003 + c2, ROLE_BLAST + 10 * nb)
+    return draw_blast_weight(c1, c2, nb, r, rng, residual=residual)
 
 
 # ---------------------------------------------------------------- activations

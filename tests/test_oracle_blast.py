@@ -1,0 +1,127 @@
+"""Pins of the oracle's BLAST static approximation (Appendix B) and of DyRA on
+top of it.
+
+The BLAST matrix is checked against hand-worked integer examples, against the
+special cases where it is an ordinary matrix product (one block; all couplings
+one), and against its defining invariant (block row i lies in span(U_i), block
+column j in span(V_j)).  DyRA with a BLAST W_hat is held to the same theorems
+as with a truncated SVD: the exact product when the residual has rank r_c, no
+worse than the static part alone, and never better than Eckart-Young.
+"""
+import numpy as np
+import pytest
+
+import oracle as orc
+from structured_rank_matmul_amd import synth
+
+from test_oracle_pins import gaussian, known_svd_weight, read_golden
+
+
+@pytest.mark.parametrize("case", ["A", "B"])
+def test_hand_worked_blocks(case):
+    g = read_golden("blast_blocks.txt")
+    nb = g[f"{case}_nb"]
+    r = g[f"{case}_U"].shape[1]
+    S = g[f"{case}_S"].reshape(nb, nb, r)
+    W_hat = orc.blast_matrix(g[f"{case}_U"], S, g[f"{case}_V"], nb)
+    assert np.array_equal(W_hat, g[f"{case}_W"])
+
+
+def test_one_block_is_the_truncated_svd():
+    # nb = 1 with U = left singular vectors, s = singular values, V = right
+    # singular vectors gives the rank-r truncated SVD: the whole DyRA plan then
+    # equals the low-rank one (up to the sign freedom of R0, which Y ignores)
+    c1, c2, r, k = 48, 40, 10, 6
+    s = synth.power_spectrum(min(c1, c2), 0.7)
+    W, q1, q2 = known_svd_weight(c1, c2, s, 5)
+    X = gaussian((3 * 20, c1), 6)
+    for lam in (0.0, 0.2):
+        low = orc.offline_preparation(W, r, k, lam)
+        bl = orc.offline_preparation_blast(W, q1[:, :r], s[None, None, :r], q2[:, :r], 1, k, lam)
+        assert np.allclose(bl.W_hat, low.W_hat, atol=1e-12)
+        assert np.allclose(orc.inference(X, 3, 20, bl), orc.inference(X, 3, 20, low), atol=1e-10)
+
+
+def test_unit_couplings_give_the_global_product():
+    # s_ij = 1 for every block: block (i, j) = U_i V_j^T, i.e. W_hat = U V^T
+    c1, c2, nb, r = 24, 36, 3, 5
+    U, V = gaussian((c1, r), 7), gaussian((c2, r), 8)
+    W_hat = orc.blast_matrix(U, np.ones((nb, nb, r)), V, nb)
+    assert np.allclose(W_hat, U @ V.T, atol=1e-12)
+
+
+def test_block_rows_and_columns_share_their_bases():
+    c1, c2, nb, r = 32, 48, 4, 3
+    b = synth.random_blast_weight(c1, c2, nb, r, 9)
+    W_hat = orc.blast_matrix(b.U, b.S, b.V, nb)
+    p, q = c1 // nb, c2 // nb
+    for i in range(nb):
+        Ui = b.U[i * p:(i + 1) * p].astype(np.float64)
+        row = W_hat[i * p:(i + 1) * p]
+        # projection onto span(U_i) leaves the block row unchanged
+        assert np.allclose(Ui @ np.linalg.lstsq(Ui, row, rcond=None)[0], row, atol=1e-10)
+        assert np.linalg.matrix_rank(row, tol=1e-9) <= r
+    for j in range(nb):
+        Vj = b.V[j * q:(j + 1) * q].astype(np.float64)
+        col = W_hat[:, j * q:(j + 1) * q].T
+        assert np.allclose(Vj @ np.linalg.lstsq(Vj, col, rcond=None)[0], col, atol=1e-10)
+    # and an off-diagonal block changes with its own coupling only
+    S2 = b.S.astype(np.float64).copy()
+    S2[1, 2] *= 2.0
+    W2 = orc.blast_matrix(b.U, S2, b.V, nb)
+    diff = np.abs(W2 - W_hat) > 1e-12
+    assert diff[p:2 * p, 2 * q:3 * q].any()
+    diff[p:2 * p, 2 * q:3 * q] = False
+    assert not diff.any()
+
+
+def test_drawn_weight_matches_its_factors():
+    # the generator's structured part (an einsum of its own) is the oracle's
+    # BLAST matrix, and the residual has the requested relative size
+    b = synth.random_blast_weight(64, 96, 4, 8, 1)
+    W_hat = orc.blast_matrix(b.U, b.S, b.V, 4)
+    assert abs(orc.rel_fro(b.W, W_hat) - 0.35) < 1e-5
+    b0 = synth.random_blast_weight(64, 96, 4, 8, 2, residual=0.0)
+    assert orc.rel_fro(b0.W, orc.blast_matrix(b0.U, b0.S, b0.V, 4)) < 1e-6
+
+
+def test_exact_when_residual_has_rank_rc():
+    # W = W_hat + E with rank(E) = r_c: R0 spans E's row space, L1 = X P_L has
+    # full column rank, and the correction restores X W exactly (lambda = 0)
+    c1, c2, nb, r, k, n = 32, 40, 4, 3, 5, 12
+    b = synth.random_blast_weight(c1, c2, nb, r, 11, residual=0.0)
+    W_hat = orc.blast_matrix(b.U, b.S, b.V, nb)
+    E = gaussian((c1, k), 12) @ gaussian((k, c2), 13)
+    W = W_hat + E
+    plan = orc.offline_preparation_blast(W, b.U, b.S, b.V, nb, k, 0.0)
+    X = gaussian((2 * n, c1), 14)
+    assert orc.rel_fro(orc.inference(X, 2, n, plan), X @ W) < 1e-10
+    # without the correction the error is that of E alone
+    plan0 = orc.offline_preparation_blast(W, b.U, b.S, b.V, nb, 0, 0.0)
+    assert abs(orc.rel_fro(orc.inference(X, 2, n, plan0), X @ W) - orc.rel_fro(X @ W_hat, X @ W)) < 1e-12
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.3])
+def test_correction_helps_and_stays_above_the_floor(lam):
+    c1, c2, nb, r, k, B, n = 48, 64, 4, 6, 8, 4, 24
+    b = synth.random_blast_weight(c1, c2, nb, r, 15)
+    plan = orc.offline_preparation_blast(b.W, b.U, b.S, b.V, nb, k, lam)
+    X = gaussian((B * n, c1), 16)
+    XW = X @ plan.W
+    Y = orc.inference(X, B, n, plan)
+    assert orc.rel_fro(Y, XW) <= orc.rel_fro(orc.weight_only(X, plan), XW) + 1e-12
+    for bi in range(B):
+        Xb = X[bi * n:(bi + 1) * n]
+        L1, R1 = orc.factors_instance(Xb, plan)
+        floor = orc.optimal_rank_error(Xb @ plan.W_res, k)
+        assert np.linalg.norm(Xb @ plan.W_res - L1 @ R1) >= floor - 1e-9
+
+
+def test_factor_shapes_validated():
+    U, V = np.zeros((8, 2)), np.zeros((12, 2))
+    with pytest.raises(ValueError):
+        orc.blast_matrix(U, np.zeros((2, 2, 2)), V, 3)       # 3 does not divide 8
+    with pytest.raises(ValueError):
+        orc.blast_matrix(U, np.zeros((2, 2, 3)), V, 2)       # coupling rank mismatch
+    with pytest.raises(ValueError):
+        orc.blast_matrix(U, np.zeros((2, 2, 2)), np.zeros((12, 3)), 2)
