@@ -129,6 +129,50 @@ dyra_status dyra_prepare_ex(const float *W, int64_t c1, int64_t c2, int32_t r, i
                             dyra_dtype dtype, int device, const float *R0, int32_t als_half_steps,
                             int32_t ns_iters, dyra_plan **plan_out);
 
+/*
+ * The host part of dyra_prepare_blast alone, for checking it without a GPU:
+ * W_res = W - W_hat [c1][c2], R0 [k][c2] and P_L [c1][k] (float64, row-major,
+ * caller-owned; any output may be NULL).  Arguments and errors as for
+ * dyra_prepare_blast, without the device, dtype and shape-limit checks.
+ */
+dyra_status dyra_factorize_blast_host(const float *W, int64_t c1, int64_t c2, int32_t nb, int32_t rb,
+                                      const float *U, const float *S, const float *V, int32_t k,
+                                      double lambda, double *W_res, double *R0, double *P_L);
+
+/*
+ * Algorithm 1, Offline Preparation, with a BLAST structured approximation in
+ * place of the truncated SVD (Appendix B, BLAST; §1 and §2.3 pair DyRA with
+ * any structured W_hat).  W is cut into an nb x nb grid of (c1/nb) x (c2/nb)
+ * blocks, and block (i, j) of W_hat is U_i diag(s_ij) V_j^T.  The block
+ * coupling is taken as diagonal: the paper leaves its shape ambiguous, and
+ * only the diagonal form reaches the FLOPs reductions it reports for the
+ * BLAST ranks it sweeps.  The paper fits the factors by minimising
+ * ||W - W_hat||_F and leaves the method open, so the caller supplies them.
+ *
+ * W   host float32 row-major [c1][c2] (X @ W orientation), as for dyra_prepare.
+ * U   host float32 row-major [c1][rb]: rows i*c1/nb .. (i+1)*c1/nb - 1 are U_i.
+ * S   host float32 [nb][nb][rb]: S[i][j][:] = s_ij, the diagonal of block (i, j).
+ * V   host float32 row-major [c2][rb]: rows j*c2/nb .. (j+1)*c2/nb - 1 are V_j.
+ * nb  1..4 blocks per side; c1 and c2 multiples of 32 * nb.
+ * rb  BLAST rank >= 1; padded to 32 it must fit 256 16-byte chunks (rb <= 2048
+ *     for bf16, 1024 for float32).
+ * k   correction rank 0..64, k <= min(c1, c2); lambda >= 0 and finite.
+ *
+ * W_res = W - W_hat, R0 = the top-k right singular vectors of W_res
+ * (Appendix D) and P_L (Eq. 7) are formed on the host in float64.  The
+ * forward runs the static product as X_i U_i per block row, the mix
+ * H_j = sum_i (X_i U_i) diag(s_ij), and H_j V_j^T per block column, with the
+ * correction added in the block-column products.  One ALS step with the
+ * Cholesky solve; no dual form: with lambda = 0 a forward with fewer tokens per
+ * instance than k returns DYRA_ERR_SHAPE.  dyra_plan_info reports r = rb.
+ * Errors as dyra_prepare, plus DYRA_ERR_SHAPE for nb, rb or dimensions out of
+ * range; DYRA_ERR_NUMERIC for non-finite factors.  The factors are read
+ * during the call only.
+ */
+dyra_status dyra_prepare_blast(const float *W, int64_t c1, int64_t c2, int32_t nb, int32_t rb,
+                               const float *U, const float *S, const float *V, int32_t k, float lambda,
+                               dyra_dtype dtype, int device, dyra_plan **plan_out);
+
 /* Releases a plan and its device memory.  NULL is ignored. */
 void dyra_plan_destroy(dyra_plan *plan);
 

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 OUT = os.path.join(PKG, "libdyra.so")
 BUILD = os.path.join(ROOT, "_build")
 
-HIP_SOURCES = ["dyra_api.hip", "gemm.hip", "solve.hip", "dyra_decode.hip", "als.hip", "ns.hip"]
+HIP_SOURCES = ["dyra_api.hip", "gemm.hip", "solve.hip", "dyra_decode.hip", "als.hip", "ns.hip", "blast.hip"]
 CXX_SOURCES = ["host_factorize.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

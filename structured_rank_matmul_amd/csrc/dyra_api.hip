@@ -29,6 +29,12 @@ struct dyra_plan {
     void *Vs;         // [c2][kw]: V_s
     void *Wres_t;     // [c2][c1]: W_res transposed
     void *Wres;       // [c1][c2]: W_res (only with half_steps > 2, for the L updates)
+    // BLAST W_hat (Appendix B), nb > 0: kw = nb * rbp, Aext holds P_L alone
+    // ([kc][c1]) and Vs is V [c2][rbp]
+    int32_t nb;       // blocks per side (0: truncated-SVD W_hat)
+    int32_t rbp;      // BLAST rank rounded up to 32
+    void *Ublk;       // [nb * rbp][c1 / nb]: row i * rbp + c = column c of U_i
+    void *Smix;       // float32 [nb][nb][rbp]: the couplings s_ij
 };
 
 namespace {
@@ -40,6 +46,7 @@ constexpr int kMaxCorrection = 64;
 constexpr int kMaxDualTokens = 16;
 constexpr int kMaxHalfSteps = 8;
 constexpr int kMaxNsIters = 64;
+constexpr int kMaxBlastBlocks = 4;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -71,6 +78,7 @@ enum class Path { Primal, Dual, Static };
 // ill-conditioned (n close to k).
 Path path_for(const dyra_plan *p, int64_t n) {
     if (p->kc == 0) return Path::Static;
+    if (p->nb > 0) return Path::Primal;  // BLAST plans have no dual form
     return (n < p->k || n <= kMaxDualTokens) ? Path::Dual : Path::Primal;
 }
 
@@ -139,6 +147,23 @@ Layout workspace_layout(const dyra_plan *p, int64_t B, int64_t n) {
     return L;
 }
 
+// A device copy of `src` rounded to `dtype` (round to nearest even); the
+// current device receives it.
+dyra_status upload_rounded(const std::vector<double> &src, dyra_dtype dtype, void **dst) {
+    const size_t es = elem_size(dtype);
+    const size_t bytes = std::max<size_t>(src.size() * es, 16);
+    if (hipMalloc(dst, bytes) != hipSuccess) return DYRA_ERR_NOMEM;
+    std::vector<unsigned char> host(bytes, 0);
+    if (dtype == DYRA_BF16) {
+        uint16_t *h = (uint16_t *)host.data();
+        for (size_t i = 0; i < src.size(); ++i) h[i] = bf16_bits(src[i]);
+    } else {
+        float *h = (float *)host.data();
+        for (size_t i = 0; i < src.size(); ++i) h[i] = (float)src[i];
+    }
+    return hipMemcpy(*dst, host.data(), bytes, hipMemcpyHostToDevice) == hipSuccess ? DYRA_OK : DYRA_ERR_HIP;
+}
+
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 dyra_status hip_status(hipError_t e) { return e == hipSuccess ? DYRA_OK : DYRA_ERR_HIP; }
@@ -153,10 +178,13 @@ dyra_status check_device(int device) {
 std::vector<const char *> stage_list(const dyra_plan *p, int64_t n) {
     switch (path_for(p, n)) {
     case Path::Dual: return {"decode_project", "decode_coef", "decode_output"};
-    case Path::Static: return {"left", "output"};
+    case Path::Static:
+        if (p->nb > 0) return {"left", "blast_mix", "output"};
+        return {"left", "output"};
     case Path::Primal: break;
     }
     std::vector<const char *> v = {"left"};
+    if (p->nb > 0) v.push_back("blast_mix");
     if (p->ns_iters > 0) {
         v.push_back("ns_factor");
         v.push_back("ns_apply");
@@ -191,13 +219,33 @@ dyra_status run_forward(const E *X, int64_t B, int64_t n, const dyra_plan *p, co
     if ((s = mark()) != DYRA_OK) return s;
     const Path path = path_for(p, n);
     if (path != Path::Dual) {
-        // T = X [A_s | P_L]^T: the static projection and L1 in one pass over X
         E *T = (E *)(ws + L.T);
         const int64_t ldt = p->kw + p->kc;
-        if ((s = hip_status(dyra::launch_gemm_store<E>(X, p->c1, Aext, p->c1, N, ldt, p->c1, T, ldt, st))) !=
-            DYRA_OK)
-            return s;
-        if ((s = mark()) != DYRA_OK) return s;
+        if (p->nb == 0) {
+            // T = X [A_s | P_L]^T: the static projection and L1 in one pass over X
+            if ((s = hip_status(dyra::launch_gemm_store<E>(X, p->c1, Aext, p->c1, N, ldt, p->c1, T, ldt, st))) !=
+                DYRA_OK)
+                return s;
+            if ((s = mark()) != DYRA_OK) return s;
+        } else {
+            // BLAST: Z_i = X_i U_i into T's block i, L1 = X P_L next to them,
+            // then H_j = sum_i Z_i diag(s_ij) in place
+            const int64_t pb = p->c1 / p->nb;
+            const E *Ub = (const E *)p->Ublk;
+            for (int i = 0; i < p->nb; ++i)
+                if ((s = hip_status(dyra::launch_gemm_store<E>(X + i * pb, p->c1, Ub + (int64_t)i * p->rbp * pb, pb,
+                                                               N, p->rbp, pb, T + (int64_t)i * p->rbp, ldt, st))) !=
+                    DYRA_OK)
+                    return s;
+            if (p->kc > 0 && (s = hip_status(dyra::launch_gemm_store<E>(X, p->c1, Aext, p->c1, N, p->kc, p->c1,
+                                                                       T + p->kw, ldt, st))) != DYRA_OK)
+                return s;
+            if ((s = mark()) != DYRA_OK) return s;
+            if ((s = hip_status(dyra::launch_blast_mix<E>(T, ldt, N, p->nb, p->rbp, (const float *)p->Smix, st))) !=
+                DYRA_OK)
+                return s;
+            if ((s = mark()) != DYRA_OK) return s;
+        }
         E *R1t = nullptr;
         if (path == Path::Primal) {
             E *Qt = (E *)(ws + L.Qt);
@@ -243,9 +291,22 @@ dyra_status run_forward(const E *X, int64_t B, int64_t n, const dyra_plan *p, co
             }
         }
         const int kc = path == Path::Primal ? p->kc : 0;
-        if ((s = hip_status(dyra::launch_output<E>(T, ldt, p->kw, kc, Vs, R1t, N, n, p->c2, bias, Y, st))) !=
-            DYRA_OK)
-            return s;
+        if (p->nb == 0) {
+            if ((s = hip_status(dyra::launch_output<E>(T, ldt, p->kw, kc, Vs, R1t, N, n, p->c2, bias, Y, st))) !=
+                DYRA_OK)
+                return s;
+        } else {
+            // BLAST: Y_j = H_j V_j^T + L1 R1_b[:, block j], one GEMM per block column
+            const int64_t qb = p->c2 / p->nb;
+            for (int j = 0; j < p->nb; ++j) {
+                const int64_t h0 = (int64_t)j * p->rbp;
+                if ((s = hip_status(dyra::launch_output_ex<E>(
+                         T + h0, ldt, p->rbp, Vs + j * qb * p->rbp, p->rbp, (int)(p->kw - h0), kc,
+                         R1t ? R1t + j * qb * p->kc : nullptr, p->c2 * p->kc, N, n, qb, bias ? bias + j * qb : nullptr,
+                         Y + j * qb, p->c2, st))) != DYRA_OK)
+                    return s;
+            }
+        }
         if ((s = mark()) != DYRA_OK) return s;
     } else {
         dyra::DecodeArgs<E> a{X, B, n, p->c1, p->c2, p->kw, p->kc, p->k, p->lambda, Aext, Vs, Wres_t, Y,
@@ -278,6 +339,9 @@ dyra_status forward_impl(const void *X, int64_t B, int64_t n, const dyra_plan *p
     const Path path = path_for(p, n);
     if (path == Path::Dual && n > kMaxDualTokens) return DYRA_ERR_SHAPE;  // n < k with k > 16 tokens
     if (path == Path::Dual && p->half_steps > 2) return DYRA_ERR_SHAPE;   // one ALS step only in the dual form
+    // BLAST plans solve the k x k system in every case: it is singular for
+    // fewer tokens than k without a ridge term
+    if (p->nb > 0 && p->kc > 0 && p->lambda == 0.f && n < p->k) return DYRA_ERR_SHAPE;
     const Layout L = workspace_layout(p, B, n);
     if (!workspace || workspace_bytes < L.total) return DYRA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return DYRA_ERR_ALIGN;
@@ -340,7 +404,6 @@ dyra_status dyra_prepare_ex(const float *W, int64_t c1, int64_t c2, int32_t r, i
     dyra_status s = dyra::factorize(W, c1, c2, r, k, (double)lambda, &f, k > 0 ? R0 : nullptr);
     if (s != DYRA_OK) return s;
 
-    const size_t es = elem_size(dtype);
     const size_t nA = (size_t)(kw + kc) * c1, nV = (size_t)c2 * kw, nR = (size_t)c2 * c1;
     std::vector<double> A(nA, 0.0), V(nV, 0.0), Rt(nR, 0.0);
     for (int64_t a = 0; a < c1; ++a) {
@@ -371,22 +434,86 @@ dyra_status dyra_prepare_ex(const float *W, int64_t c1, int64_t c2, int32_t r, i
         delete p;
         return DYRA_ERR_NODEVICE;
     }
-    auto upload = [&](const std::vector<double> &src, void **dst) -> dyra_status {
-        const size_t bytes = std::max<size_t>(src.size() * es, 16);
-        if (hipMalloc(dst, bytes) != hipSuccess) return DYRA_ERR_NOMEM;
-        std::vector<unsigned char> host(bytes, 0);
-        if (dtype == DYRA_BF16) {
-            uint16_t *h = (uint16_t *)host.data();
-            for (size_t i = 0; i < src.size(); ++i) h[i] = bf16_bits(src[i]);
-        } else {
-            float *h = (float *)host.data();
-            for (size_t i = 0; i < src.size(); ++i) h[i] = (float)src[i];
-        }
-        return hipMemcpy(*dst, host.data(), bytes, hipMemcpyHostToDevice) == hipSuccess ? DYRA_OK : DYRA_ERR_HIP;
-    };
+    auto upload = [&](const std::vector<double> &src, void **dst) { return upload_rounded(src, dtype, dst); };
     if ((s = upload(A, &p->Aext)) == DYRA_OK && (s = upload(V, &p->Vs)) == DYRA_OK)
         s = upload(Rt, &p->Wres_t);
     if (s == DYRA_OK && p->half_steps > 2) s = upload(f.W_res, &p->Wres);
+    if (prev >= 0) (void)hipSetDevice(prev);
+    if (s != DYRA_OK) {
+        dyra_plan_destroy(p);
+        return s;
+    }
+    *plan_out = p;
+    return DYRA_OK;
+}
+
+dyra_status dyra_prepare_blast(const float *W, int64_t c1, int64_t c2, int32_t nb, int32_t rb, const float *U,
+                               const float *S, const float *V, int32_t k, float lambda, dyra_dtype dtype, int device,
+                               dyra_plan **plan_out) {
+    if (!plan_out) return DYRA_ERR_ARG;
+    *plan_out = nullptr;
+    if (dtype != DYRA_BF16 && dtype != DYRA_F32) return DYRA_ERR_DTYPE;
+    if (!W || !U || !S || !V || c1 <= 0 || c2 <= 0 || nb < 1 || rb < 1 || k < 0) return DYRA_ERR_ARG;
+    if (k > std::min(c1, c2)) return DYRA_ERR_ARG;
+    if (!(lambda >= 0.f) || !std::isfinite(lambda)) return DYRA_ERR_ARG;
+    if (nb > kMaxBlastBlocks) return DYRA_ERR_SHAPE;
+    if (c1 % (32 * (int64_t)nb) != 0 || c2 % (32 * (int64_t)nb) != 0) return DYRA_ERR_SHAPE;
+    if (k > kMaxCorrection) return DYRA_ERR_SHAPE;
+    const int32_t rbp = (int32_t)round_up(rb, 32);
+    if ((int64_t)rbp * (int64_t)elem_size(dtype) > 16 * 256) return DYRA_ERR_SHAPE;  // the mix kernel's row chunks
+    const int32_t kc = k > 0 ? (int32_t)round_up(k, 16) : 0;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) return DYRA_ERR_NODEVICE;
+
+    dyra::Factors f;
+    dyra_status s = dyra::factorize_blast(W, c1, c2, nb, rb, U, S, V, k, (double)lambda, &f);
+    if (s != DYRA_OK) return s;
+
+    const int64_t pb = c1 / nb;
+    std::vector<double> Ub((size_t)nb * rbp * pb, 0.0), Vp((size_t)c2 * rbp, 0.0), Pt((size_t)kc * c1, 0.0),
+        Rt((size_t)c2 * c1, 0.0);
+    std::vector<float> Sm((size_t)nb * nb * rbp, 0.f);
+    for (int64_t a = 0; a < c1; ++a) {
+        const int64_t i = a / pb, ai = a % pb;
+        for (int32_t c = 0; c < rb; ++c) Ub[((size_t)i * rbp + c) * pb + ai] = U[a * rb + c];
+        for (int32_t c = 0; c < k; ++c) Pt[(size_t)c * c1 + a] = f.P_L[a * k + c];
+    }
+    for (int64_t b = 0; b < c2; ++b)
+        for (int32_t c = 0; c < rb; ++c) Vp[(size_t)b * rbp + c] = V[b * rb + c];
+    for (int64_t ij = 0; ij < (int64_t)nb * nb; ++ij)
+        for (int32_t c = 0; c < rb; ++c) Sm[(size_t)ij * rbp + c] = S[ij * rb + c];
+    for (int64_t a = 0; a < c1; ++a)
+        for (int64_t b = 0; b < c2; ++b) Rt[(size_t)b * c1 + a] = f.W_res[a * c2 + b];
+
+    dyra_plan *p = new (std::nothrow) dyra_plan{};
+    if (!p) return DYRA_ERR_NOMEM;
+    p->device = device;
+    p->dtype = dtype;
+    p->c1 = c1;
+    p->c2 = c2;
+    p->r = rb;
+    p->k = k;
+    p->kw = nb * rbp;
+    p->kc = kc;
+    p->lambda = lambda;
+    p->half_steps = 2;
+    p->ns_iters = 0;
+    p->nb = nb;
+    p->rbp = rbp;
+    int prev = -1;
+    (void)hipGetDevice(&prev);
+    if (hipSetDevice(device) != hipSuccess) {
+        delete p;
+        return DYRA_ERR_NODEVICE;
+    }
+    if ((s = upload_rounded(Ub, dtype, &p->Ublk)) == DYRA_OK && (s = upload_rounded(Vp, dtype, &p->Vs)) == DYRA_OK &&
+        (s = upload_rounded(Pt, dtype, &p->Aext)) == DYRA_OK)
+        s = upload_rounded(Rt, dtype, &p->Wres_t);
+    if (s == DYRA_OK) {
+        if (hipMalloc(&p->Smix, Sm.size() * sizeof(float)) != hipSuccess) s = DYRA_ERR_NOMEM;
+        else if (hipMemcpy(p->Smix, Sm.data(), Sm.size() * sizeof(float), hipMemcpyHostToDevice) != hipSuccess)
+            s = DYRA_ERR_HIP;
+    }
     if (prev >= 0) (void)hipSetDevice(prev);
     if (s != DYRA_OK) {
         dyra_plan_destroy(p);
@@ -405,6 +532,8 @@ void dyra_plan_destroy(dyra_plan *plan) {
     if (plan->Vs) (void)hipFree(plan->Vs);
     if (plan->Wres_t) (void)hipFree(plan->Wres_t);
     if (plan->Wres) (void)hipFree(plan->Wres);
+    if (plan->Ublk) (void)hipFree(plan->Ublk);
+    if (plan->Smix) (void)hipFree(plan->Smix);
     if (prev >= 0) (void)hipSetDevice(prev);
     delete plan;
 }

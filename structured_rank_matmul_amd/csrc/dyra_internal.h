@@ -26,4 +26,11 @@ struct Factors {
 dyra_status factorize(const float *W, int64_t c1, int64_t c2, int32_t r, int32_t k, double lambda,
                       Factors *out, const float *R0_in = nullptr);
 
+// Preparation with a BLAST W_hat (Appendix B) from the caller's factors:
+// U [c1][rb] (block row i = rows i*c1/nb ..), S [nb][nb][rb] (diagonal
+// couplings s_ij), V [c2][rb]; all float32 host arrays.  Fills W_res, R0 and
+// P_L (A_s, V_s and sigma stay empty).
+dyra_status factorize_blast(const float *W, int64_t c1, int64_t c2, int32_t nb, int32_t rb, const float *U,
+                            const float *S, const float *V, int32_t k, double lambda, Factors *out);
+
 }  // namespace dyra

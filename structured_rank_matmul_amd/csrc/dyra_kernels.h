@@ -44,6 +44,22 @@ template <typename E>
 hipError_t launch_output(const E *T, int64_t ldt, int kw, int kc, const E *Vs, const E *R1t, int64_t Ntok,
                          int64_t n, int64_t c2, const E *bias, E *Y, hipStream_t st);
 
+// The general form of launch_output: Y (leading dimension ldy) = A[:, 0:K]
+// B^T + bias + A[:, kcol:kcol+kc] R1_b, where R1t + b * rstride is instance
+// b's [N][kc] block; A and B have leading dimensions lda, ldb.  Used per
+// block column of a BLAST W_hat.
+template <typename E>
+hipError_t launch_output_ex(const E *A, int64_t lda, int64_t K, const E *B, int64_t ldb, int kcol, int kc,
+                            const E *R1t, int64_t rstride, int64_t Ntok, int64_t n, int64_t N, const E *bias, E *Y,
+                            int64_t ldy, hipStream_t st);
+
+// BLAST middle step (blast.hip): H_j = sum_i Z_i diag(s_ij) in place over
+// T's columns [0, nb * rbp) (block i's Z, then block j's H, at columns
+// [i rbp, i rbp + rbp)); Smix float32 [nb][nb][rbp].  nb <= 4, rbp a
+// multiple of 32 with at most 256 16-byte chunks.
+template <typename E>
+hipError_t launch_blast_mix(E *T, int64_t ldt, int64_t N, int nb, int rbp, const float *Smix, hipStream_t st);
+
 // Called after each kernel that a multi-kernel launcher enqueues: takes the
 // launch status, records the next timing event (if any) on the stream, and
 // returns the status to go on with.

@@ -145,6 +145,7 @@ template <typename E> struct Corr {
     const E *R1t;
     int64_t n;
     int kcol, kc;
+    int64_t rstride;  // elements from one instance's R1t block to the next
 };
 
 // ROWS = true: the epilogue receives four consecutive columns of one row (the
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
             kl = kl < corr.kc ? kl : 0;  // columns past kc are fetched from column 0 and never used
             // A rows: the static source shifted to Q's columns; B rows: R1_b
             const int64_t offA = corr.kcol + kl - (FC_IN_BASE ? fcol : 0);
-            const E *gB = corr.R1t + b * N * corr.kc + kl;
+            const E *gB = corr.R1t + b * corr.rstride + kl;
 #pragma unroll
             for (int q = 0; q < IPW; ++q) {
                 const int j = wave + q * NW;
@@ -514,13 +515,20 @@ hipError_t launch_right(const E *Mp, const E *Wres_t, int64_t rows, int64_t c1, 
 }
 
 template <typename E>
-hipError_t launch_output(const E *T, int64_t ldt, int kw, int kc, const E *Vs, const E *R1t, int64_t Ntok,
-                         int64_t n, int64_t c2, const E *bias, E *Y, hipStream_t st) {
+hipError_t launch_output_ex(const E *A, int64_t lda, int64_t K, const E *B, int64_t ldb, int kcol, int kc,
+                            const E *R1t, int64_t rstride, int64_t Ntok, int64_t n, int64_t N, const E *bias, E *Y,
+                            int64_t ldy, hipStream_t st) {
     if (Ntok <= 0) return hipSuccess;
     if (kc > 0 && (n < 1 || kc > 64 || kc % 16 != 0)) return hipErrorInvalidValue;
-    const RowStore<E> epi{Y, c2, bias, c2};
-    if (kc == 0) return gemm_dispatch<E, true, false>(T, ldt, Vs, kw, Ntok, c2, kw, Corr<E>{}, epi, st);
-    return gemm_dispatch<E, true, true>(T, ldt, Vs, kw, Ntok, c2, kw, Corr<E>{R1t, n, kw, kc}, epi, st);
+    const RowStore<E> epi{Y, ldy, bias, N};
+    if (kc == 0) return gemm_dispatch<E, true, false>(A, lda, B, ldb, Ntok, N, K, Corr<E>{}, epi, st);
+    return gemm_dispatch<E, true, true>(A, lda, B, ldb, Ntok, N, K, Corr<E>{R1t, n, kcol, kc, rstride}, epi, st);
+}
+
+template <typename E>
+hipError_t launch_output(const E *T, int64_t ldt, int kw, int kc, const E *Vs, const E *R1t, int64_t Ntok,
+                         int64_t n, int64_t c2, const E *bias, E *Y, hipStream_t st) {
+    return launch_output_ex<E>(T, ldt, kw, Vs, kw, kw, kc, R1t, c2 * kc, Ntok, n, c2, bias, Y, c2, st);
 }
 
 template hipError_t launch_gemm_store<bf16>(const bf16 *, int64_t, const bf16 *, int64_t, int64_t, int64_t, int64_t,
@@ -531,6 +539,12 @@ template hipError_t launch_right<bf16>(const bf16 *, const bf16 *, int64_t, int6
                                        hipStream_t);
 template hipError_t launch_right<float>(const float *, const float *, int64_t, int64_t, int64_t, int, float, float *,
                                         hipStream_t);
+template hipError_t launch_output_ex<bf16>(const bf16 *, int64_t, int64_t, const bf16 *, int64_t, int, int,
+                                           const bf16 *, int64_t, int64_t, int64_t, int64_t, const bf16 *, bf16 *,
+                                           int64_t, hipStream_t);
+template hipError_t launch_output_ex<float>(const float *, int64_t, int64_t, const float *, int64_t, int, int,
+                                            const float *, int64_t, int64_t, int64_t, int64_t, const float *,
+                                            float *, int64_t, hipStream_t);
 template hipError_t launch_output<bf16>(const bf16 *, int64_t, int, int, const bf16 *, const bf16 *, int64_t,
                                         int64_t, int64_t, const bf16 *, bf16 *, hipStream_t);
 template hipError_t launch_output<float>(const float *, int64_t, int, int, const float *, const float *, int64_t,

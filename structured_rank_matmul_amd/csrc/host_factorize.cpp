@@ -440,16 +440,25 @@ bool spd_solve(const double *Gin, int64_t k, double *B, int64_t cols) {
 
 }  // namespace
 
-dyra_status factorize(const float *W32, int64_t c1, int64_t c2, int32_t r, int32_t k,
-                      double lambda, Factors *out, const float *R0_in) {
-    if (!W32 || !out) return DYRA_ERR_ARG;
-    if (c1 <= 0 || c2 <= 0 || r < 0 || k < 0) return DYRA_ERR_ARG;
-    if ((int64_t)r + k > std::min(c1, c2)) return DYRA_ERR_ARG;
-    if (!(lambda >= 0.0) || !std::isfinite(lambda)) return DYRA_ERR_ARG;
-    if (R0_in) {
-        for (int64_t i = 0; i < (int64_t)k * c2; ++i)
-            if (!std::isfinite(R0_in[i])) return DYRA_ERR_NUMERIC;
+namespace {
+
+// Float64 copy of a float32 array; false if any value is not finite.
+bool widen(const float *src, int64_t count, Vec &dst) {
+    dst.resize((size_t)count);
+    bool finite = true;
+#pragma omp parallel for schedule(static) reduction(&& : finite)
+    for (int64_t i = 0; i < count; ++i) {
+        const double w = src[i];
+        finite = finite && std::isfinite(w);
+        dst[(size_t)i] = w;
     }
+    return finite;
+}
+
+// Lines 2-5 of the Offline Preparation on a float64 W (arguments checked by
+// the callers): the rank-r truncated SVD as W_hat, W_res, R0 and P_L.
+dyra_status factorize_core(Vec &&W, int64_t c1, int64_t c2, int32_t r, int32_t k, double lambda, Factors *out,
+                           const float *R0_in) {
     // singular vectors needed: the static r, plus k for the default R0
     const int64_t want = (int64_t)r + (R0_in ? 0 : k);
     out->c1 = c1;
@@ -457,15 +466,6 @@ dyra_status factorize(const float *W32, int64_t c1, int64_t c2, int32_t r, int32
     out->r = r;
     out->k = k;
     out->lambda = lambda;
-    Vec W((size_t)(c1 * c2));
-    bool finite = true;
-#pragma omp parallel for schedule(static) reduction(&& : finite)
-    for (int64_t i = 0; i < c1 * c2; ++i) {
-        const double w = W32[i];
-        finite = finite && std::isfinite(w);
-        W[i] = w;
-    }
-    if (!finite) return DYRA_ERR_NUMERIC;
 
     out->A_s.assign((size_t)(c1 * r), 0.0);
     out->V_s.assign((size_t)(c2 * r), 0.0);
@@ -626,6 +626,56 @@ dyra_status factorize(const float *W32, int64_t c1, int64_t c2, int32_t r, int32
     return DYRA_OK;
 }
 
+}  // namespace
+
+dyra_status factorize(const float *W32, int64_t c1, int64_t c2, int32_t r, int32_t k,
+                      double lambda, Factors *out, const float *R0_in) {
+    if (!W32 || !out) return DYRA_ERR_ARG;
+    if (c1 <= 0 || c2 <= 0 || r < 0 || k < 0) return DYRA_ERR_ARG;
+    if ((int64_t)r + k > std::min(c1, c2)) return DYRA_ERR_ARG;
+    if (!(lambda >= 0.0) || !std::isfinite(lambda)) return DYRA_ERR_ARG;
+    if (R0_in) {
+        for (int64_t i = 0; i < (int64_t)k * c2; ++i)
+            if (!std::isfinite(R0_in[i])) return DYRA_ERR_NUMERIC;
+    }
+    Vec W;
+    if (!widen(W32, c1 * c2, W)) return DYRA_ERR_NUMERIC;
+    return factorize_core(std::move(W), c1, c2, r, k, lambda, out, R0_in);
+}
+
+// BLAST (Appendix B): W_hat's block (i, j) is U_i diag(s_ij) V_j^T.  W_res =
+// W - W_hat is formed here, and the rest of the preparation is the r = 0 case
+// of the truncated-SVD one on W_res: R0 = its top-k right singular vectors,
+// P_L from Eq. 7.
+dyra_status factorize_blast(const float *W32, int64_t c1, int64_t c2, int32_t nb, int32_t rb, const float *U32,
+                            const float *S32, const float *V32, int32_t k, double lambda, Factors *out) {
+    if (!W32 || !U32 || !S32 || !V32 || !out) return DYRA_ERR_ARG;
+    if (c1 <= 0 || c2 <= 0 || nb < 1 || rb < 1 || k < 0) return DYRA_ERR_ARG;
+    if (c1 % nb != 0 || c2 % nb != 0 || k > std::min(c1, c2)) return DYRA_ERR_ARG;
+    if (!(lambda >= 0.0) || !std::isfinite(lambda)) return DYRA_ERR_ARG;
+    Vec W, U, S, V;
+    if (!widen(W32, c1 * c2, W) || !widen(U32, c1 * rb, U) || !widen(S32, (int64_t)nb * nb * rb, S) ||
+        !widen(V32, c2 * rb, V))
+        return DYRA_ERR_NUMERIC;
+    const int64_t p = c1 / nb, q = c2 / nb;
+#pragma omp parallel for schedule(static)
+    for (int64_t a = 0; a < c1; ++a) {
+        const int64_t i = a / p;
+        Vec us((size_t)rb);
+        for (int64_t j = 0; j < nb; ++j) {
+            const double *s = S.data() + (i * nb + j) * rb;
+            for (int32_t c = 0; c < rb; ++c) us[(size_t)c] = U[(size_t)(a * rb + c)] * s[c];
+            for (int64_t b = j * q; b < (j + 1) * q; ++b) {
+                const double *v = V.data() + b * rb;
+                double acc = 0.0;
+                for (int32_t c = 0; c < rb; ++c) acc += us[(size_t)c] * v[c];
+                W[(size_t)(a * c2 + b)] -= acc;
+            }
+        }
+    }
+    return factorize_core(std::move(W), c1, c2, 0, k, lambda, out, nullptr);
+}
+
 }  // namespace dyra
 
 extern "C" dyra_status dyra_factorize_host(const float *W, int64_t c1, int64_t c2, int32_t r,
@@ -639,5 +689,17 @@ extern "C" dyra_status dyra_factorize_host(const float *W, int64_t c1, int64_t c
     if (R0) std::copy(f.R0.begin(), f.R0.end(), R0);
     if (P_L) std::copy(f.P_L.begin(), f.P_L.end(), P_L);
     if (sigma) std::copy(f.sigma.begin(), f.sigma.end(), sigma);
+    return DYRA_OK;
+}
+
+extern "C" dyra_status dyra_factorize_blast_host(const float *W, int64_t c1, int64_t c2, int32_t nb, int32_t rb,
+                                                 const float *U, const float *S, const float *V, int32_t k,
+                                                 double lambda, double *W_res, double *R0, double *P_L) {
+    dyra::Factors f;
+    const dyra_status st = dyra::factorize_blast(W, c1, c2, nb, rb, U, S, V, k, lambda, &f);
+    if (st != DYRA_OK) return st;
+    if (W_res) std::copy(f.W_res.begin(), f.W_res.end(), W_res);
+    if (R0) std::copy(f.R0.begin(), f.R0.end(), R0);
+    if (P_L) std::copy(f.P_L.begin(), f.P_L.end(), P_L);
     return DYRA_OK;
 }

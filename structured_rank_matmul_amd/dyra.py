@@ -26,7 +26,7 @@ EXPORTED = (
     "dyra_status_str", "dyra_factorize_host", "dyra_prepare", "dyra_prepare_ex", "dyra_plan_destroy",
     "dyra_plan_info",
     "dyra_workspace_bytes", "dyra_forward", "dyra_forward_ex", "dyra_forward_status", "dyra_dense_ref",
-    "dyra_forward_timed", "dyra_stage_name",
+    "dyra_forward_timed", "dyra_stage_name", "dyra_prepare_blast", "dyra_factorize_blast_host",
 )
 
 
@@ -58,6 +58,11 @@ def load() -> ctypes.CDLL:
     L.dyra_prepare_ex.argtypes = [vp, i64, i64, i32, i32, f32, ctypes.c_int, ctypes.c_int, vp, i32, i32,
                                   ctypes.POINTER(vp)]
     L.dyra_prepare_ex.restype = ctypes.c_int
+    L.dyra_prepare_blast.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, i32, f32, ctypes.c_int, ctypes.c_int,
+                                     ctypes.POINTER(vp)]
+    L.dyra_prepare_blast.restype = ctypes.c_int
+    L.dyra_factorize_blast_host.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, i32, f64, dp, dp, dp]
+    L.dyra_factorize_blast_host.restype = ctypes.c_int
     L.dyra_plan_destroy.argtypes = [vp]
     L.dyra_plan_destroy.restype = None
     L.dyra_plan_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i32),
@@ -185,6 +190,44 @@ def dyra_prepare_ex(W: np.ndarray, r: int, k: int, lam: float = 0.0, dtype="bf16
                                 ctypes.byref(h))
     _check(st, "dyra_prepare_ex")
     return Plan(h.value, c1, c2, int(r), int(k), float(lam), code, int(device))
+
+
+def dyra_factorize_blast_host(W: np.ndarray, U: np.ndarray, S: np.ndarray, V: np.ndarray, nb: int, k: int,
+                              lam: float = 0.0) -> Dict[str, np.ndarray]:
+    """The library's host BLAST preparation alone: W_res, R0, P_L (float64)."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    U = np.ascontiguousarray(U, dtype=np.float32)
+    S = np.ascontiguousarray(S, dtype=np.float32)
+    V = np.ascontiguousarray(V, dtype=np.float32)
+    c1, c2 = W.shape
+    rb = U.shape[1]
+    out = {"W_res": np.zeros((c1, c2)), "R0": np.zeros((k, c2)), "P_L": np.zeros((c1, k))}
+    dp = ctypes.POINTER(ctypes.c_double)
+    st = load().dyra_factorize_blast_host(W.ctypes.data, c1, c2, int(nb), int(rb), U.ctypes.data, S.ctypes.data,
+                                          V.ctypes.data, int(k), float(lam),
+                                          *[out[n].ctypes.data_as(dp) for n in ("W_res", "R0", "P_L")])
+    _check(st, "dyra_factorize_blast_host")
+    return out
+
+
+def dyra_prepare_blast(W: np.ndarray, U: np.ndarray, S: np.ndarray, V: np.ndarray, nb: int, k: int,
+                       lam: float = 0.0, dtype="bf16", device: int = 0) -> Plan:
+    """Offline Preparation with a BLAST W_hat from the given factors: U [c1, rb],
+    S [nb, nb, rb] (diagonal couplings), V [c2, rb]; all float32 on the host."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    c1, c2 = W.shape
+    U = np.ascontiguousarray(U, dtype=np.float32)
+    V = np.ascontiguousarray(V, dtype=np.float32)
+    S = np.ascontiguousarray(S, dtype=np.float32)
+    rb = U.shape[1] if U.ndim == 2 else -1
+    if U.shape != (c1, rb) or V.shape != (c2, rb) or S.shape != (int(nb), int(nb), rb):
+        raise ValueError(f"BLAST factors must be U [{c1}, rb], S [{nb}, {nb}, rb], V [{c2}, rb]")
+    code = _dtype_code(dtype)
+    h = ctypes.c_void_p()
+    st = load().dyra_prepare_blast(W.ctypes.data, c1, c2, int(nb), int(rb), U.ctypes.data, S.ctypes.data,
+                                   V.ctypes.data, int(k), float(lam), code, int(device), ctypes.byref(h))
+    _check(st, "dyra_prepare_blast")
+    return Plan(h.value, c1, c2, int(rb), int(k), float(lam), code, int(device))
 
 
 def dyra_workspace_bytes(plan: Plan, B: int, n: int) -> int:

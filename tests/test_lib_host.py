@@ -155,3 +155,51 @@ def test_factorize_vit_shape_against_oracle():
     plan = orc.offline_preparation(W.astype(np.float64), spec.r, spec.k)
     assert np.abs(f["A_s"] @ f["V_s"].T - plan.W_hat).max() < 1e-9 * s[0]
     assert np.abs(f["P_L"] @ f["R0"] - plan.P_L @ plan.R0).max() < 1e-9 * s[0]
+
+
+# ------------------------------------------------------------------ BLAST preparation (host part)
+
+def _blast_status(W, c1, c2, nb, rb, U, S, V, k, lam=0.0, dtype=1, device=0):
+    h = ctypes.c_void_p()
+    ptr = lambda a: a.ctypes.data if a is not None else None
+    return dyra.load().dyra_prepare_blast(ptr(W), c1, c2, nb, rb, ptr(U), ptr(S), ptr(V), k, lam, dtype, device,
+                                          ctypes.byref(h))
+
+
+def test_prepare_blast_rejects_bad_arguments():
+    c1, c2, nb, rb = 256, 128, 4, 8
+    b = synth.random_blast_weight(c1, c2, nb, rb, 3)
+    W, U, S, V = b.W, b.U, b.S, b.V
+    assert _blast_status(None, c1, c2, nb, rb, U, S, V, 8) == 1        # null W
+    assert _blast_status(W, c1, c2, nb, rb, None, S, V, 8) == 1        # null U
+    assert _blast_status(W, c1, c2, 0, rb, U, S, V, 8) == 1            # no blocks
+    assert _blast_status(W, c1, c2, nb, 0, U, S, V, 8) == 1            # rank 0
+    assert _blast_status(W, c1, c2, nb, rb, U, S, V, -1) == 1          # negative k
+    assert _blast_status(W, c1, c2, nb, rb, U, S, V, 8, lam=-1.0) == 1
+    assert _blast_status(W, c1, c2, nb, rb, U, S, V, 8, dtype=9) == 3
+    assert _blast_status(W, c1, c2, 8, rb, U, S, V, 8) == 2            # more than 4 blocks
+    assert _blast_status(W, c1, c2, nb, rb, U, S, V, 80) == 2          # k above 64
+    W2 = np.zeros((192, 128), np.float32)
+    assert _blast_status(W2, 192, 128, nb, rb, U, S, V, 8) == 2        # c1 not a multiple of 32 nb
+    big = np.zeros((c1, 2080), np.float32)
+    assert _blast_status(W, c1, c2, nb, 2080, big, S, V, 8) == 2       # rank past the mix kernel's row
+
+
+def test_factorize_blast_host_matches_oracle():
+    c1, c2, nb, rb, k = 96, 64, 2, 6, 5
+    b = synth.random_blast_weight(c1, c2, nb, rb, 21)
+    for lam in (0.0, 0.25):
+        got = dyra.dyra_factorize_blast_host(b.W, b.U, b.S, b.V, nb, k, lam)
+        ref = orc.offline_preparation_blast(b.W, b.U, b.S, b.V, nb, k, lam)
+        assert np.allclose(got["W_res"], ref.W_res, atol=1e-12 * np.abs(ref.W_res).max())
+        # R0 is fixed up to signs (and rotations within ties); P_L R0 is not
+        assert np.allclose(got["P_L"] @ got["R0"], ref.P_L @ ref.R0, atol=1e-9)
+        assert np.allclose(got["R0"] @ got["R0"].T, np.eye(k), atol=1e-10)
+
+
+def test_factorize_blast_host_rejects_non_finite_factors():
+    b = synth.random_blast_weight(64, 64, 2, 4, 22)
+    U = b.U.copy()
+    U[3, 1] = np.nan
+    with pytest.raises(dyra.DyraError):
+        dyra.dyra_factorize_blast_host(b.W, U, b.S, b.V, 2, 4)
