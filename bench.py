@@ -150,6 +150,70 @@ def cpu_baseline(workload, plans_orc, X_host, budget_s):
                       f"layers, float64 numpy, {t_total:.1f} s"}
 
 
+def blast_record(w, layers, args, stream, reps, t_dense, log):
+    """DyRA with a BLAST W_hat: per-layer plans on BLAST-structured stand-in
+    weights, the whole-step time, the per-stage times, the mix kernel's
+    bandwidth, and parity and error on sampled instances."""
+    import torch
+    import oracle as orc
+    from structured_rank_matmul_amd import dyra, synth
+    B, n, N = w.B, w.n, w.B * w.n
+    nb = args.blast_blocks
+    es = 2 if w.dtype == "bf16" else 4
+    legs = []
+    for L in layers:
+        spec = L["spec"]
+        bw = synth.make_blast_weight(w, spec, nb, spec.r)
+        t0 = time.perf_counter()
+        plan = dyra.dyra_prepare_blast(bw.W, bw.U, bw.S, bw.V, nb, spec.k, 0.0, w.dtype, 0)
+        log(f"prepared BLAST {spec.name} in {time.perf_counter() - t0:.1f} s")
+        legs.append(dict(spec=spec, bw=bw, plan=plan, ws=dyra.alloc_workspace(plan, B, n),
+                         y=torch.empty_like(L["y"]), xd=L["xd"], X=L["X"]))
+
+    def step():
+        for G in legs:
+            dyra.dyra_forward(G["xd"], B, n, G["plan"], G["y"], G["ws"], stream)
+
+    t_blast = time_loop(step, args.steps, args.warmup, stream)
+    rec = {"blocks": nb, "ms_per_step": round(t_blast * 1e3, 4), "speedup_vs_dense": round(t_dense / t_blast, 4),
+           "layers": {}}
+    mix_bytes, mix_t = 0.0, 0.0
+    sample = [0, B // 2, B - 1]
+    rows = np.concatenate([np.arange(b * n, (b + 1) * n) for b in sample])
+    for G in legs:
+        spec = G["spec"]
+        names = dyra.stage_names(G["plan"], n)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        acc = np.zeros(len(names))
+        for it in range(reps + 1):
+            dyra.dyra_forward_timed(G["xd"], B, n, G["plan"], G["y"], G["ws"], evs, stream)
+            torch.cuda.synchronize()
+            if it:
+                acc += [evs[i].elapsed_time(evs[i + 1]) / 1e3 for i in range(len(names))]
+        per = {nm: acc[i] / reps for i, nm in enumerate(names)}
+        rbp = -(-spec.r // 32) * 32
+        mix_bytes += 2.0 * N * nb * rbp * es          # Z read, H written
+        mix_t += per["blast_mix"]
+        lrec = {"rank": spec.r, "k": spec.k, "stage_us": {k_: round(v * 1e6, 2) for k_, v in per.items()}}
+        if not args.no_parity:
+            bw = G["bw"]
+            op = orc.offline_preparation_blast(bw.W, bw.U, bw.S, bw.V, nb, spec.k, 0.0)
+            Xs = G["X"].exact[rows]
+            ref = orc.inference(Xs, len(sample), n, op)
+            y = G["y"].float().cpu().numpy().astype(np.float64)[rows]
+            exact = Xs @ bw.W.astype(np.float64)
+            e_gpu, e_orc = orc.rel_fro(y, exact), orc.rel_fro(ref, exact)
+            lrec.update({"rel_fro_vs_oracle": float(f"{orc.rel_fro(y, ref):.3e}"), "e_dyra": round(e_gpu, 5),
+                         "e_dyra_oracle": round(e_orc, 5),
+                         "e_weight_only": round(orc.rel_fro(orc.weight_only(Xs, op), exact), 5)})
+        rec["layers"][spec.name] = lrec
+        log(f"BLAST {spec.name}: " + "  ".join(f"{k_} {v * 1e6:.1f}us" for k_, v in per.items()))
+        G["plan"].close()
+    rec["blast_mix_gbps"] = round(mix_bytes / mix_t / 1e9, 1)
+    rec["sample_instances"] = sample
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +229,9 @@ def main():
                     help="skip the t = 1.5 / t = 2 ALS measurement (two more prepares and timings per layer)")
     ap.add_argument("--no-ns", action="store_true",
                     help="skip the Newton-Schulz SPD-solve measurement (two more prepares and timings per layer)")
+    ap.add_argument("--no-blast", action="store_true",
+                    help="skip the BLAST static-approximation measurement (a second weight and plan per layer)")
+    ap.add_argument("--blast-blocks", type=int, default=4, help="BLAST blocks per side")
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run three forward steps and a calibration copy only (for rocprofv3 --pmc runs)")
@@ -410,6 +477,15 @@ def main():
                                                          for k_, v in rec.items()))
         ns["sample_instances"] = sample
 
+    # ---- BLAST static approximation (Appendix B) in place of the truncated
+    # SVD: an nb x nb block grid of the same static rank r (so the static
+    # FLOPs match the low-rank path's, plus the mix), on a BLAST-structured
+    # stand-in weight of each layer; step time, stages and error on the same
+    # sampled instances
+    blast = None
+    if not args.no_blast and not dual:
+        blast = blast_record(w, layers, args, stream, reps, t_dense, log)
+
     cpu = None
     if not args.no_cpu_baseline:
         plans_orc = [L.get("orc") or orc.offline_preparation(L["W"].astype(np.float64), L["spec"].r,
@@ -446,6 +522,7 @@ def main():
         "flops_matched_static": matched,
         "als_steps": als_steps,
         "newton_schulz": ns,
+        "blast": blast,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

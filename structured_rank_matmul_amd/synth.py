@@ -155,9 +155,12 @@ def draw_blast_weight(c1: int, c2: int, nb: int, r: int, rng: np.random.Generato
     V = (rng.standard_normal((c2, r)) / np.sqrt(qr)).astype(np.float32)
     decay = power_spectrum(r, p)
     S = (decay[None, None, :] * (1.0 + 0.5 * rng.standard_normal((nb, nb, r)))).astype(np.float32)
-    Ub = U.astype(np.float64).reshape(nb, pr, r)
-    Vb = V.astype(np.float64).reshape(nb, qr, r)
-    structured = np.einsum("iac,ijc,jbc->iajb", Ub, S.astype(np.float64), Vb).reshape(c1, c2)
+    # block column j of the structured part: [U_1 diag(s_1j); ...; U_nb diag(s_nbj)] V_j^T
+    U64, S64 = U.astype(np.float64), S.astype(np.float64)
+    structured = np.empty((c1, c2))
+    for j in range(nb):
+        scaled = (U64.reshape(nb, pr, r) * S64[:, j, None, :]).reshape(c1, r)
+        structured[:, j * qr:(j + 1) * qr] = scaled @ V[j * qr:(j + 1) * qr].astype(np.float64).T
     m = min(c1, c2)
     E = (haar_orthogonal(rng, c1, m) * power_spectrum(m, p)) @ haar_orthogonal(rng, c2, m).T
     E *= residual * np.linalg.norm(structured) / np.linalg.norm(E)
