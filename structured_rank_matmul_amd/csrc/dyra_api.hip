@@ -232,11 +232,18 @@ dyra_status run_forward(const E *X, int64_t B, int64_t n, const dyra_plan *p, co
             // then H_j = sum_i Z_i diag(s_ij) in place
             const int64_t pb = p->c1 / p->nb;
             const E *Ub = (const E *)p->Ublk;
-            for (int i = 0; i < p->nb; ++i)
-                if ((s = hip_status(dyra::launch_gemm_store<E>(X + i * pb, p->c1, Ub + (int64_t)i * p->rbp * pb, pb,
-                                                               N, p->rbp, pb, T + (int64_t)i * p->rbp, ldt, st))) !=
-                    DYRA_OK)
+            if (dyra::gemm_groupable(N, (int64_t)p->nb * p->rbp, p->rbp)) {
+                // one launch: column group i reads X's columns from i * pb
+                if ((s = hip_status(dyra::launch_gemm_store_grouped<E>(X, p->c1, Ub, pb, N, (int64_t)p->nb * p->rbp,
+                                                                       pb, p->rbp, pb, T, ldt, st))) != DYRA_OK)
                     return s;
+            } else {
+                for (int i = 0; i < p->nb; ++i)
+                    if ((s = hip_status(dyra::launch_gemm_store<E>(X + i * pb, p->c1, Ub + (int64_t)i * p->rbp * pb,
+                                                                   pb, N, p->rbp, pb, T + (int64_t)i * p->rbp, ldt,
+                                                                   st))) != DYRA_OK)
+                        return s;
+            }
             if (p->kc > 0 && (s = hip_status(dyra::launch_gemm_store<E>(X, p->c1, Aext, p->c1, N, p->kc, p->c1,
                                                                        T + p->kw, ldt, st))) != DYRA_OK)
                 return s;
@@ -298,13 +305,21 @@ dyra_status run_forward(const E *X, int64_t B, int64_t n, const dyra_plan *p, co
         } else {
             // BLAST: Y_j = H_j V_j^T + L1 R1_b[:, block j], one GEMM per block column
             const int64_t qb = p->c2 / p->nb;
-            for (int j = 0; j < p->nb; ++j) {
-                const int64_t h0 = (int64_t)j * p->rbp;
-                if ((s = hip_status(dyra::launch_output_ex<E>(
-                         T + h0, ldt, p->rbp, Vs + j * qb * p->rbp, p->rbp, (int)(p->kw - h0), kc,
-                         R1t ? R1t + j * qb * p->kc : nullptr, p->c2 * p->kc, N, n, qb, bias ? bias + j * qb : nullptr,
-                         Y + j * qb, p->c2, st))) != DYRA_OK)
+            if (dyra::gemm_groupable(N, p->c2, (int)qb)) {
+                // one launch: column group j reads H_j from T's column j * rbp
+                if ((s = hip_status(dyra::launch_output_ex<E>(T, ldt, p->rbp, Vs, p->rbp, p->kw, kc, R1t,
+                                                              p->c2 * p->kc, N, n, p->c2, bias, Y, p->c2, (int)qb,
+                                                              p->rbp, st))) != DYRA_OK)
                     return s;
+            } else {
+                for (int j = 0; j < p->nb; ++j) {
+                    const int64_t h0 = (int64_t)j * p->rbp;
+                    if ((s = hip_status(dyra::launch_output_ex<E>(
+                             T + h0, ldt, p->rbp, Vs + j * qb * p->rbp, p->rbp, (int)(p->kw - h0), kc,
+                             R1t ? R1t + j * qb * p->kc : nullptr, p->c2 * p->kc, N, n, qb,
+                             bias ? bias + j * qb : nullptr, Y + j * qb, p->c2, 0, 0, st))) != DYRA_OK)
+                        return s;
+                }
             }
         }
         if ((s = mark()) != DYRA_OK) return s;

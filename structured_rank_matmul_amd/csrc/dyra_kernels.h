@@ -46,12 +46,25 @@ hipError_t launch_output(const E *T, int64_t ldt, int kw, int kc, const E *Vs, c
 
 // The general form of launch_output: Y (leading dimension ldy) = A[:, 0:K]
 // B^T + bias + A[:, kcol:kcol+kc] R1_b, where R1t + b * rstride is instance
-// b's [N][kc] block; A and B have leading dimensions lda, ldb.  Used per
-// block column of a BLAST W_hat.
+// b's [N][kc] block; A and B have leading dimensions lda, ldb.  With
+// gcols > 0 the static A operand is grouped: output columns
+// [g gcols, g gcols + gcols) read A's columns from g * gstride on (the
+// correction columns stay at kcol).  Used for a BLAST W_hat's block columns.
 template <typename E>
 hipError_t launch_output_ex(const E *A, int64_t lda, int64_t K, const E *B, int64_t ldb, int kcol, int kc,
                             const E *R1t, int64_t rstride, int64_t Ntok, int64_t n, int64_t N, const E *bias, E *Y,
-                            int64_t ldy, hipStream_t st);
+                            int64_t ldy, int gcols, int64_t gstride, hipStream_t st);
+
+// launch_gemm_store with a grouped A operand: D[:, g gcols .. g gcols +
+// gcols - 1] = A[:, g gstride .. g gstride + K - 1] B[g gcols ..]^T.  One
+// launch for a block-diagonal product.
+template <typename E>
+hipError_t launch_gemm_store_grouped(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N,
+                                     int64_t K, int gcols, int64_t gstride, E *D, int64_t ldd, hipStream_t st);
+
+// Whether an M x N product can be grouped in column groups of gcols (a tile
+// shape that divides gcols exists).
+bool gemm_groupable(int64_t M, int64_t N, int gcols);
 
 // BLAST middle step (blast.hip): H_j = sum_i Z_i diag(s_ij) in place over
 // T's columns [0, nb * rbp) (block i's Z, then block j's H, at columns

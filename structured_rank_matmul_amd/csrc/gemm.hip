@@ -146,13 +146,19 @@ template <typename E> struct Corr {
     int64_t n;
     int kcol, kc;
     int64_t rstride;  // elements from one instance's R1t block to the next
+    // Grouped A operand (any kernel): output columns [g*gcols, g*gcols + gcols)
+    // read A from column g*gstride on (each tile lies in one group); gcols = 0
+    // for none.  The correction columns stay at kcol from A itself.
+    int gcols = 0;
+    int64_t gstride = 0;
 };
 
 // ROWS = true: the epilogue receives four consecutive columns of one row (the
 // MFMA is issued with the operands swapped, so a lane holds a row of the
 // block); ROWS = false: four consecutive rows of one column.  K must be a
 // multiple of 16 (a last slice may be short).
-template <typename E, int BM, int BN, int WM, int WN, int NS, int SB, bool ROWS, bool CORR, class Epi>
+template <typename E, int BM, int BN, int WM, int WN, int NS, int SB, bool ROWS, bool CORR, class Epi,
+          bool GROUPED>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict__ A, int64_t lda,
                                                             const E *__restrict__ B, int64_t ldb, int64_t M,
                                                             int64_t N, int64_t K, int tiles_n, int ntiles,
@@ -235,13 +241,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
     // lane's column is folded in here; SB = 128 adds it per slice (each form
     // measured faster for its shapes).
     constexpr int64_t FC_IN_BASE = SB == 64;
+    int64_t aoff = 0;  // grouped A operand: this tile's group offset (a template switch: the
+                       // extra registers made the ungrouped correction kernels spill)
+    if constexpr (GROUPED) aoff = (int64_t)((int)col0 / corr.gcols) * corr.gstride;
     const E *base[IPW];
 #pragma unroll
     for (int q = 0; q < IPW; ++q) {
         const int j = wave + q * NW;
         if (j < IA) {
             const int64_t r = row0 + RPB * j + frow;
-            base[q] = A + (r < M ? r : M - 1) * lda + (FC_IN_BASE ? fcol : 0);
+            base[q] = A + (r < M ? r : M - 1) * lda + aoff + (FC_IN_BASE ? fcol : 0);
         } else {
             const int64_t r = col0 + RPB * (j - IA) + frow;
             base[q] = B + (r < N ? r : N - 1) * ldb + (FC_IN_BASE ? fcol : 0);
@@ -272,7 +281,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
             int kl = sc * BK + fcol;
             kl = kl < corr.kc ? kl : 0;  // columns past kc are fetched from column 0 and never used
             // A rows: the static source shifted to Q's columns; B rows: R1_b
-            const int64_t offA = corr.kcol + kl - (FC_IN_BASE ? fcol : 0);
+            const int64_t offA = corr.kcol + kl - (FC_IN_BASE ? fcol : 0) - (GROUPED ? aoff : 0);
             const E *gB = corr.R1t + b * corr.rstride + kl;
 #pragma unroll
             for (int q = 0; q < IPW; ++q) {
@@ -430,12 +439,14 @@ template <typename E, int BM, int BN, int NS, int SB, bool ROWS> constexpr size_
                : stage_bytes<BM, BN, NS, SB>();
 }
 
-template <typename E, int BM, int BN, int WM, int WN, int NS, int SB, bool ROWS, bool CORR, class Epi>
+template <typename E, int BM, int BN, int WM, int WN, int NS, int SB, bool ROWS, bool CORR, bool GROUPED,
+          class Epi>
 hipError_t gemm_launch(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N, int64_t K,
                        const Corr<E> &corr, Epi epi, hipStream_t st) {
     static_assert(gemm_smem<E, BM, BN, NS, SB, ROWS>() <= kLdsBytes, "LDS");
     if (K % 16 != 0) return hipErrorInvalidValue;
-    auto kfn = gemm_kernel<E, BM, BN, WM, WN, NS, SB, ROWS, CORR, Epi>;
+    if (GROUPED && corr.gcols <= 0) return hipErrorInvalidValue;
+    auto kfn = gemm_kernel<E, BM, BN, WM, WN, NS, SB, ROWS, CORR, Epi, GROUPED>;
     constexpr size_t smem = gemm_smem<E, BM, BN, NS, SB, ROWS>();
     static int per_cu = 0;  // resident workgroups per CU
     if (per_cu == 0) {
@@ -461,38 +472,52 @@ hipError_t gemm_launch(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t
 // traffic per MFMA (weights from timings of the shapes on gfx950).
 enum class Shape { T256x256, T256x160, T256x128, T128x128, T64x64 };
 
-Shape pick_shape(int64_t M, int64_t N) {
-    if (N <= 64) return Shape::T64x64;
+// gcols > 0: only shapes whose tile width divides gcols (a tile must not
+// straddle two groups of a grouped A operand).
+bool pick_shape(int64_t M, int64_t N, int gcols, Shape &best) {
+    best = Shape::T64x64;
+    const bool fits64 = gcols <= 0 || gcols % 64 == 0;
+    if (N <= 64) return fits64;
     struct C { Shape s; int bm, bn; double w; } cands[] = {
         {Shape::T256x256, 256, 256, 1.0}, {Shape::T256x160, 256, 160, 1.2}, {Shape::T256x128, 256, 128, 1.16},
         {Shape::T128x128, 128, 128, 1.3}};
-    Shape best = Shape::T128x128;
+    best = Shape::T128x128;
     double best_cost = 1e300;
+    bool found = false;
     for (const C &c : cands) {
+        if (gcols > 0 && gcols % c.bn != 0) continue;
         const double tiles = (double)((M + c.bm - 1) / c.bm) * (double)((N + c.bn - 1) / c.bn);
         const double rounds = std::ceil(tiles / 256.0);
         const double cost = rounds * c.bm * c.bn * c.w;
         if (cost < best_cost) {
             best_cost = cost;
             best = c.s;
+            found = true;
         }
     }
-    return best;
+    if (!found) best = Shape::T64x64;
+    return found || fits64;
 }
 
-template <typename E, bool ROWS, bool CORR, class Epi>
+template <typename E, bool ROWS, bool CORR, bool GROUPED = false, class Epi>
 hipError_t gemm_dispatch(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N, int64_t K,
                          const Corr<E> &corr, Epi epi, hipStream_t st) {
-    switch (pick_shape(M, N)) {
+    Shape shape;
+    if (!pick_shape(M, N, GROUPED ? corr.gcols : 0, shape)) return hipErrorInvalidValue;
+    switch (shape) {
     case Shape::T256x256:
         // float32 keeps 64-byte slices (128 would spill it)
         if constexpr (sizeof(E) == 4)
-            return gemm_launch<E, 256, 256, 4, 2, 4, 64, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
-        else return gemm_launch<E, 256, 256, 4, 2, 2, 128, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
-    case Shape::T256x160: return gemm_launch<E, 256, 160, 8, 1, 3, 128, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
-    case Shape::T256x128: return gemm_launch<E, 256, 128, 4, 2, 3, 128, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
-    case Shape::T128x128: return gemm_launch<E, 128, 128, 2, 2, 4, 128, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
-    case Shape::T64x64: return gemm_launch<E, 64, 64, 2, 2, 4, 128, ROWS, CORR>(A, lda, B, ldb, M, N, K, corr, epi, st);
+            return gemm_launch<E, 256, 256, 4, 2, 4, 64, ROWS, CORR, GROUPED>(A, lda, B, ldb, M, N, K, corr, epi, st);
+        else return gemm_launch<E, 256, 256, 4, 2, 2, 128, ROWS, CORR, GROUPED>(A, lda, B, ldb, M, N, K, corr, epi, st);
+    case Shape::T256x160:
+        return gemm_launch<E, 256, 160, 8, 1, 3, 128, ROWS, CORR, GROUPED>(A, lda, B, ldb, M, N, K, corr, epi, st);
+    case Shape::T256x128:
+        return gemm_launch<E, 256, 128, 4, 2, 3, 128, ROWS, CORR, GROUPED>(A, lda, B, ldb, M, N, K, corr, epi, st);
+    case Shape::T128x128:
+        return gemm_launch<E, 128, 128, 2, 2, 4, 128, ROWS, CORR, GROUPED>(A, lda, B, ldb, M, N, K, corr, epi, st);
+    case Shape::T64x64:
+        return gemm_launch<E, 64, 64, 2, 2, 4, 128, ROWS, CORR, GROUPED>(A, lda, B, ldb, M, N, K, corr, epi, st);
     }
     return hipErrorInvalidValue;
 }
@@ -506,6 +531,22 @@ hipError_t launch_gemm_store(const E *A, int64_t lda, const E *B, int64_t ldb, i
     return gemm_dispatch<E, true, false>(A, lda, B, ldb, M, N, K, Corr<E>{}, RowStore<E>{D, ldd}, st);
 }
 
+bool gemm_groupable(int64_t M, int64_t N, int gcols) {
+    Shape shape;
+    return gcols > 0 && N % gcols == 0 && pick_shape(M, N, gcols, shape);
+}
+
+template <typename E>
+hipError_t launch_gemm_store_grouped(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N,
+                                     int64_t K, int gcols, int64_t gstride, E *D, int64_t ldd, hipStream_t st) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    if (gcols <= 0 || N % gcols != 0) return hipErrorInvalidValue;
+    Corr<E> g{};
+    g.gcols = gcols;
+    g.gstride = gstride;
+    return gemm_dispatch<E, true, false, true>(A, lda, B, ldb, M, N, K, g, RowStore<E>{D, ldd}, st);
+}
+
 template <typename E>
 hipError_t launch_right(const E *Mp, const E *Wres_t, int64_t rows, int64_t c1, int64_t c2, int kc, float alpha,
                         E *R1t, hipStream_t st) {
@@ -517,18 +558,25 @@ hipError_t launch_right(const E *Mp, const E *Wres_t, int64_t rows, int64_t c1, 
 template <typename E>
 hipError_t launch_output_ex(const E *A, int64_t lda, int64_t K, const E *B, int64_t ldb, int kcol, int kc,
                             const E *R1t, int64_t rstride, int64_t Ntok, int64_t n, int64_t N, const E *bias, E *Y,
-                            int64_t ldy, hipStream_t st) {
+                            int64_t ldy, int gcols, int64_t gstride, hipStream_t st) {
     if (Ntok <= 0) return hipSuccess;
     if (kc > 0 && (n < 1 || kc > 64 || kc % 16 != 0)) return hipErrorInvalidValue;
+    if (gcols < 0 || (gcols > 0 && N % gcols != 0)) return hipErrorInvalidValue;
     const RowStore<E> epi{Y, ldy, bias, N};
-    if (kc == 0) return gemm_dispatch<E, true, false>(A, lda, B, ldb, Ntok, N, K, Corr<E>{}, epi, st);
-    return gemm_dispatch<E, true, true>(A, lda, B, ldb, Ntok, N, K, Corr<E>{R1t, n, kcol, kc, rstride}, epi, st);
+    Corr<E> c{R1t, n, kcol, kc, rstride, gcols, gstride};
+    if (kc == 0) {
+        c.R1t = nullptr;
+        if (gcols > 0) return gemm_dispatch<E, true, false, true>(A, lda, B, ldb, Ntok, N, K, c, epi, st);
+        return gemm_dispatch<E, true, false>(A, lda, B, ldb, Ntok, N, K, c, epi, st);
+    }
+    if (gcols > 0) return gemm_dispatch<E, true, true, true>(A, lda, B, ldb, Ntok, N, K, c, epi, st);
+    return gemm_dispatch<E, true, true>(A, lda, B, ldb, Ntok, N, K, c, epi, st);
 }
 
 template <typename E>
 hipError_t launch_output(const E *T, int64_t ldt, int kw, int kc, const E *Vs, const E *R1t, int64_t Ntok,
                          int64_t n, int64_t c2, const E *bias, E *Y, hipStream_t st) {
-    return launch_output_ex<E>(T, ldt, kw, Vs, kw, kw, kc, R1t, c2 * kc, Ntok, n, c2, bias, Y, c2, st);
+    return launch_output_ex<E>(T, ldt, kw, Vs, kw, kw, kc, R1t, c2 * kc, Ntok, n, c2, bias, Y, c2, 0, 0, st);
 }
 
 template hipError_t launch_gemm_store<bf16>(const bf16 *, int64_t, const bf16 *, int64_t, int64_t, int64_t, int64_t,
@@ -541,10 +589,14 @@ template hipError_t launch_right<float>(const float *, const float *, int64_t, i
                                         hipStream_t);
 template hipError_t launch_output_ex<bf16>(const bf16 *, int64_t, int64_t, const bf16 *, int64_t, int, int,
                                            const bf16 *, int64_t, int64_t, int64_t, int64_t, const bf16 *, bf16 *,
-                                           int64_t, hipStream_t);
+                                           int64_t, int, int64_t, hipStream_t);
 template hipError_t launch_output_ex<float>(const float *, int64_t, int64_t, const float *, int64_t, int, int,
                                             const float *, int64_t, int64_t, int64_t, int64_t, const float *,
-                                            float *, int64_t, hipStream_t);
+                                            float *, int64_t, int, int64_t, hipStream_t);
+template hipError_t launch_gemm_store_grouped<bf16>(const bf16 *, int64_t, const bf16 *, int64_t, int64_t, int64_t,
+                                                    int64_t, int, int64_t, bf16 *, int64_t, hipStream_t);
+template hipError_t launch_gemm_store_grouped<float>(const float *, int64_t, const float *, int64_t, int64_t,
+                                                     int64_t, int64_t, int, int64_t, float *, int64_t, hipStream_t);
 template hipError_t launch_output<bf16>(const bf16 *, int64_t, int, int, const bf16 *, const bf16 *, int64_t,
                                         int64_t, int64_t, const bf16 *, bf16 *, hipStream_t);
 template hipError_t launch_output<float>(const float *, int64_t, int, int, const float *, const float *, int64_t,
