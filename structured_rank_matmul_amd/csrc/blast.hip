@@ -9,6 +9,8 @@
 // for each token row and rank column c the nb values Z_i[c] are mixed by the
 // nb x nb matrix s_..[c] into the nb values H_j[c], so it runs in place over
 // T's first nb * rbp columns, and each thread owns its positions alone.
+// Smix rows are rbp floats, rbp a multiple of 32, so the float4 loads and the
+// LDS image stay aligned.
 #include <hip/hip_runtime.h>
 
 #include "dyra_kernels.h"
@@ -18,27 +20,29 @@ namespace dyra {
 namespace {
 
 constexpr int kMixThreads = 256;
+constexpr int kMixBlocks = 1024;  // four per CU: each walks several rows per thread
 
-// Each thread holds one 16-byte chunk (VEC rank columns) of every block for
-// one row, and keeps that chunk's couplings in registers while it walks rows.
+// Each thread owns one 16-byte chunk (VEC rank columns) of every block for a
+// row and walks rows.  The couplings sit in LDS, loaded once per workgroup
+// (held in registers instead, they cost every thread its own 512-byte read
+// from L2 and three quarters of the register file).
 template <typename E, int NB>
 __global__ __launch_bounds__(kMixThreads) void blast_mix_kernel(E *__restrict__ T, int64_t ldt, int64_t N,
                                                                 int rbp, const float *__restrict__ Smix) {
     constexpr int VEC = 16 / (int)sizeof(E);
-    const int cpr = rbp / VEC;                // chunks per row and block
-    const int rows_per_iter = kMixThreads / cpr;
+    extern __shared__ __align__(16) float ss[];  // [NB][NB][rbp]
     const int t = (int)threadIdx.x;
+    for (int e = 4 * t; e < NB * NB * rbp; e += 4 * kMixThreads)
+        *reinterpret_cast<f32x4 *>(ss + e) = *reinterpret_cast<const f32x4 *>(Smix + e);
+    __syncthreads();
+    const int cpr = rbp / VEC;  // chunks per row and block
+    const int rows_per_iter = kMixThreads / cpr;
     if (t >= rows_per_iter * cpr) return;
-    const int chunk = t % cpr, c0 = chunk * VEC;
-    float s[NB][NB][VEC];
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) s[i][j][v] = Smix[((int64_t)i * NB + j) * rbp + c0 + v];
+    const int c0 = (t % cpr) * VEC;
     const int64_t step = (int64_t)gridDim.x * rows_per_iter;
     for (int64_t row = (int64_t)blockIdx.x * rows_per_iter + t / cpr; row < N; row += step) {
+        // keeps the coupling reads in the loop: hoisted, they take the registers back
+        asm volatile("" ::: "memory");
         E *base = T + row * ldt + c0;
         u32x4 raw[NB];
 #pragma unroll
@@ -52,15 +56,21 @@ __global__ __launch_bounds__(kMixThreads) void blast_mix_kernel(E *__restrict__ 
         }
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
+            float h[VEC] = {};
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const float *sij = ss + (i * NB + j) * rbp + c0;
+#pragma unroll
+                for (int v4 = 0; v4 < VEC; v4 += 4) {
+                    const f32x4 sv = *reinterpret_cast<const f32x4 *>(sij + v4);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) h[v4 + v] = fmaf(z[i][v4 + v], sv[v], h[v4 + v]);
+                }
+            }
             u32x4 out;
             E *o = reinterpret_cast<E *>(&out);
 #pragma unroll
-            for (int v = 0; v < VEC; ++v) {
-                float h = 0.f;
-#pragma unroll
-                for (int i = 0; i < NB; ++i) h = fmaf(z[i][v], s[i][j][v], h);
-                o[v] = to_elem<E>(h);
-            }
+            for (int v = 0; v < VEC; ++v) o[v] = to_elem<E>(h[v]);
             *reinterpret_cast<u32x4 *>(base + (int64_t)j * rbp) = out;
         }
     }
@@ -71,8 +81,18 @@ hipError_t mix_launch(E *T, int64_t ldt, int64_t N, int rbp, const float *Smix, 
     constexpr int VEC = 16 / (int)sizeof(E);
     const int rows_per_iter = kMixThreads / (rbp / VEC);
     const int64_t want = (N + rows_per_iter - 1) / rows_per_iter;
-    const unsigned grid = (unsigned)(want < 2048 ? want : 2048);
-    hipLaunchKernelGGL((blast_mix_kernel<E, NB>), dim3(grid), dim3(kMixThreads), 0, st, T, ldt, N, rbp, Smix);
+    const unsigned grid = (unsigned)(want < kMixBlocks ? want : kMixBlocks);
+    const size_t smem = sizeof(float) * NB * NB * (size_t)rbp;
+    auto kfn = blast_mix_kernel<E, NB>;
+    static bool attr = false;
+    if (!attr) {
+        // up to 128 KB at four blocks and rank 2048
+        const hipError_t e = hipFuncSetAttribute((const void *)kfn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)(sizeof(float) * NB * NB * 2048));
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    hipLaunchKernelGGL(kfn, dim3(grid), dim3(kMixThreads), smem, st, T, ldt, N, rbp, Smix);
     return hipGetLastError();
 }
 
