@@ -95,6 +95,11 @@ def dyra_flops(spec, B, n):
     return sum(fl[st] for st in (DUAL_STAGES if dual_form(spec, n) else PRIMAL_STAGES))
 
 
+def rel_err(a, b) -> float:
+    """||a - b||_F / ||b||_F in float64 (the relative Frobenius error of the metric)."""
+    return float(np.linalg.norm(np.asarray(a, np.float64) - b) / np.linalg.norm(b))
+
+
 def time_loop(fn, steps, warmup, stream, per_step=False):
     """Mean seconds per step over `steps` timed steps (events on `stream`);
     with per_step, also the list of single-step durations."""
@@ -150,12 +155,51 @@ def cpu_baseline(workload, plans_orc, X_host, budget_s):
                       f"layers, float64 numpy, {t_total:.1f} s"}
 
 
+def oracle_leg(w, layers, blast, blast_legs, parity, args):
+    """The CPU leg: the oracle's Offline Preparation per layer, its Inference
+    on the sampled instances compared with the library's outputs (filled into
+    the parity and BLAST records), then the timed CPU baseline."""
+    import oracle as orc
+    n = w.n
+    plans = [orc.offline_preparation(L["W"].astype(np.float64), L["spec"].r, L["spec"].k, 0.0) for L in layers]
+    if not args.no_parity and parity:
+        sample = parity["sample_instances"]
+        rows = np.concatenate([np.arange(b * n, (b + 1) * n) for b in sample])
+        worst, worst_gap = 0.0, None
+
+        def compare(rec, y, Xs, W, op):
+            nonlocal worst, worst_gap
+            ref = orc.inference(Xs, len(sample), n, op)
+            exact = Xs @ W.astype(np.float64)
+            err, e_gpu, e_orc = rel_err(y, ref), rel_err(y, exact), rel_err(ref, exact)
+            rec.update({"rel_fro_vs_oracle": float(f"{err:.3e}"), "e_dyra_oracle": round(e_orc, 5),
+                        "e_weight_only": round(rel_err(orc.weight_only(Xs, op), exact), 5)})
+            worst = max(worst, err)
+            # where the method is exact (one token with lambda = 0: the
+            # correction reaches X W) the relative gap is undefined; parity
+            # against the oracle is the measure there
+            if e_orc > 1e-9:
+                gap = abs(e_gpu - e_orc) / e_orc
+                worst_gap = gap if worst_gap is None else max(worst_gap, gap)
+
+        for L, op in zip(layers, plans):
+            compare(parity[L["spec"].name], L["y_rows"], L["X"].exact[rows], L["W"], op)
+        for G in blast_legs:
+            if "y_rows" not in G:
+                continue
+            bw = G["bw"]
+            op = orc.offline_preparation_blast(bw.W, bw.U, bw.S, bw.V, bw.nb, G["spec"].k, 0.0)
+            compare(blast["layers"][G["spec"].name], G["y_rows"], G["X"].exact[rows], bw.W, op)
+        parity["worst_rel_fro"] = float(f"{worst:.3e}")
+        parity["worst_own_error_gap"] = None if worst_gap is None else float(f"{worst_gap:.3e}")
+    return cpu_baseline(w, plans, [L["X"].exact for L in layers], args.cpu_budget)
+
+
 def blast_record(w, layers, args, stream, reps, t_dense, log):
     """DyRA with a BLAST W_hat: per-layer plans on BLAST-structured stand-in
     weights, the whole-step time, the per-stage times, the mix kernel's
     bandwidth, and parity and error on sampled instances."""
     import torch
-    import oracle as orc
     from structured_rank_matmul_amd import dyra, synth
     B, n, N = w.B, w.n, w.B * w.n
     nb = args.blast_blocks
@@ -196,22 +240,15 @@ def blast_record(w, layers, args, stream, reps, t_dense, log):
         mix_t += per["blast_mix"]
         lrec = {"rank": spec.r, "k": spec.k, "stage_us": {k_: round(v * 1e6, 2) for k_, v in per.items()}}
         if not args.no_parity:
-            bw = G["bw"]
-            op = orc.offline_preparation_blast(bw.W, bw.U, bw.S, bw.V, nb, spec.k, 0.0)
             Xs = G["X"].exact[rows]
-            ref = orc.inference(Xs, len(sample), n, op)
-            y = G["y"].float().cpu().numpy().astype(np.float64)[rows]
-            exact = Xs @ bw.W.astype(np.float64)
-            e_gpu, e_orc = orc.rel_fro(y, exact), orc.rel_fro(ref, exact)
-            lrec.update({"rel_fro_vs_oracle": float(f"{orc.rel_fro(y, ref):.3e}"), "e_dyra": round(e_gpu, 5),
-                         "e_dyra_oracle": round(e_orc, 5),
-                         "e_weight_only": round(orc.rel_fro(orc.weight_only(Xs, op), exact), 5)})
+            G["y_rows"] = G["y"].float().cpu().numpy().astype(np.float64)[rows]
+            lrec["e_dyra"] = round(rel_err(G["y_rows"], Xs @ G["bw"].W.astype(np.float64)), 5)
         rec["layers"][spec.name] = lrec
         log(f"BLAST {spec.name}: " + "  ".join(f"{k_} {v * 1e6:.1f}us" for k_, v in per.items()))
         G["plan"].close()
     rec["blast_mix_gbps"] = round(mix_bytes / mix_t / 1e9, 1)
     rec["sample_instances"] = sample
-    return rec
+    return rec, legs
 
 
 def main():
@@ -244,7 +281,6 @@ def main():
     import torch
     import torch.nn.functional as F
 
-    import oracle as orc
     from structured_rank_matmul_amd import costs, dyra, synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -362,34 +398,17 @@ def main():
                 "mfma_frac": round(dom_fl / t_dom / peak, 4),
                 "hbm_frac": round(dom_by / t_dom / PEAK_HBM, 4)}
 
-    # ---- parity on sampled instances
+    # ---- the metric's error on sampled instances: ||Y - X W|| / ||X W|| with
+    # the exact product in float64 (the oracle comparison is made in the CPU
+    # leg below)
     parity = {}
     if not args.no_parity:
         sample = [0, B // 2, B - 1]
-        worst, worst_gap = 0.0, None
+        rows = np.concatenate([np.arange(b * n, (b + 1) * n) for b in sample])
         for L in layers:
-            spec = L["spec"]
-            op = orc.offline_preparation(L["W"].astype(np.float64), spec.r, spec.k, 0.0)
-            L["orc"] = op
-            rows = np.concatenate([np.arange(b * n, (b + 1) * n) for b in sample])
-            Xs = L["X"].exact[rows]
-            ref = orc.inference(Xs, len(sample), n, op)
-            y = L["y"].float().cpu().numpy().astype(np.float64)[rows]
-            exact = Xs @ L["W"].astype(np.float64)
-            err = orc.rel_fro(y, ref)
-            e_gpu, e_orc = orc.rel_fro(y, exact), orc.rel_fro(ref, exact)
-            # where the method is exact (e.g. one token with lambda = 0: the
-            # correction reaches X W) the relative gap is undefined; parity
-            # against the oracle is the measure there
-            gap = abs(e_gpu - e_orc) / e_orc if e_orc > 1e-9 else None
-            parity[spec.name] = {"rel_fro_vs_oracle": float(f"{err:.3e}"), "e_dyra": round(e_gpu, 5),
-                                 "e_dyra_oracle": round(e_orc, 5),
-                                 "e_weight_only": round(orc.rel_fro(orc.weight_only(Xs, op), exact), 5)}
-            worst = max(worst, err)
-            if gap is not None:
-                worst_gap = gap if worst_gap is None else max(worst_gap, gap)
-        parity["worst_rel_fro"] = float(f"{worst:.3e}")
-        parity["worst_own_error_gap"] = None if worst_gap is None else float(f"{worst_gap:.3e}")
+            L["y_rows"] = L["y"].float().cpu().numpy().astype(np.float64)[rows]
+            exact = L["X"].exact[rows] @ L["W"].astype(np.float64)
+            parity[L["spec"].name] = {"e_dyra": round(rel_err(L["y_rows"], exact), 5)}
         parity["sample_instances"] = sample
 
     # ---- FLOPs-matched static baseline (§2.3 FLOPs-Matched Comparison,
@@ -414,8 +433,8 @@ def main():
                             stream)
             Xs = L["X"].exact[rows]
             exact = Xs @ L["W"].astype(np.float64)
-            e_s = orc.rel_fro(ys.float().cpu().numpy().astype(np.float64)[rows], exact)
-            e_d = orc.rel_fro(L["y"].float().cpu().numpy().astype(np.float64)[rows], exact)
+            e_s = rel_err(ys.float().cpu().numpy().astype(np.float64)[rows], exact)
+            e_d = rel_err(L["y"].float().cpu().numpy().astype(np.float64)[rows], exact)
             matched[spec.name] = {"static_rank": s, "e_dyra": round(e_d, 5), "e_static": round(e_s, 5),
                                   "t_dyra_us": round(t_d * 1e6, 2), "t_static_us": round(t_s * 1e6, 2),
                                   "flops_dyra": costs.dyra_flops(n, spec.c1, spec.c2, spec.r, spec.k) * B,
@@ -443,7 +462,7 @@ def main():
                 ws_h = L["ws"] if hs == 2 else dyra.alloc_workspace(plan_h, B, n)
                 yh = torch.empty_like(L["y"])
                 t_h = time_loop(lambda: dyra.dyra_forward(L["xd"], B, n, plan_h, yh, ws_h, stream), reps, 3, stream)
-                e_h = orc.rel_fro(yh.float().cpu().numpy().astype(np.float64)[rows], exact)
+                e_h = rel_err(yh.float().cpu().numpy().astype(np.float64)[rows], exact)
                 rec[f"t={hs / 2:g}"] = {"half_steps": hs, "e": round(e_h, 5), "t_us": round(t_h * 1e6, 2)}
                 if hs != 2:
                     plan_h.close()
@@ -469,7 +488,7 @@ def main():
                 ws_h = dyra.alloc_workspace(plan_h, B, n)
                 yh = torch.empty_like(L["y"])
                 t_h = time_loop(lambda: dyra.dyra_forward(L["xd"], B, n, plan_h, yh, ws_h, stream), reps, 3, stream)
-                e_h = orc.rel_fro(yh.float().cpu().numpy().astype(np.float64)[rows], exact)
+                e_h = rel_err(yh.float().cpu().numpy().astype(np.float64)[rows], exact)
                 rec[f"ns_iters={it}"] = {"e": round(e_h, 5), "t_us": round(t_h * 1e6, 2)}
                 plan_h.close()
             ns[spec.name] = rec
@@ -482,16 +501,17 @@ def main():
     # FLOPs match the low-rank path's, plus the mix), on a BLAST-structured
     # stand-in weight of each layer; step time, stages and error on the same
     # sampled instances
-    blast = None
+    blast, blast_legs = None, []
     if not args.no_blast and not dual:
-        blast = blast_record(w, layers, args, stream, reps, t_dense, log)
+        blast, blast_legs = blast_record(w, layers, args, stream, reps, t_dense, log)
 
+    # ---- the CPU leg, the one place this script runs the oracle: its float64
+    # result on the sampled instances set beside the library's (parity, the
+    # oracle's own error, the static part alone), and its throughput on the
+    # host cores
     cpu = None
     if not args.no_cpu_baseline:
-        plans_orc = [L.get("orc") or orc.offline_preparation(L["W"].astype(np.float64), L["spec"].r,
-                                                             L["spec"].k, 0.0) for L in layers]
-        X_host = [L["X"].exact for L in layers]
-        cpu = cpu_baseline(w, plans_orc, X_host, args.cpu_budget)
+        cpu = oracle_leg(w, layers, blast, blast_legs, parity, args)
 
     flops = sum(dyra_flops(L["spec"], B, n) for L in layers)
     dense_flops = sum(2.0 * N * L["spec"].c1 * L["spec"].c2 for L in layers)
