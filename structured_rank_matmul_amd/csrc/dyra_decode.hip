@@ -71,8 +71,9 @@ constexpr int kUnrollRes = 4;  // the same for each of the two W_res register se
 template <typename F> __device__ __forceinline__ F keep_if(bool ok, const F &f) { return ok ? f : F{}; }
 
 // partial[s][row][col] = sum over the s-th split of c1 of X[row][k] Aext[col][k].
-// Grid (K1/32 column blocks, splits, row blocks of 64).  The 16-deep steps of a
-// split are dealt round-robin to the four wavefronts, then reduced in LDS.
+// Grid (K1/32 column blocks, splits, row blocks of 64).  Each of the four
+// wavefronts takes a contiguous quarter of the split (its batched loads then
+// cover whole 128-byte lines of each row), and the quarters meet in LDS.
 template <typename E, bool TWO>
 __global__ __launch_bounds__(NT) void decode_project_kernel(const E *__restrict__ X, const E *__restrict__ Aext,
                                                             int64_t N, int64_t c1, int K1, int splits,
@@ -94,13 +95,17 @@ __global__ __launch_bounds__(NT) void decode_project_kernel(const E *__restrict_
     const E *pa0 = X + (a_ok ? ra : row0) * c1 + lk;
     const E *pa1 = X + (b_ok ? rb : row0) * c1 + lk;
     typedef typename Frag<E>::type F;
-    // kUnroll steps' loads are requested before their MFMAs
-    for (int64_t k0 = kbeg + 16 * wave; k0 < kbeg + ks; k0 += 64 * kUnroll) {
+    // kUnroll steps' loads are requested before their MFMAs; each wavefront
+    // streams its own contiguous quarter of the split
+    const int64_t q4 = ((ks + 63) / 64) * 16;
+    const int64_t wb = kbeg + (wave * q4 < ks ? wave * q4 : ks);
+    const int64_t we = kbeg + ((wave + 1) * q4 < ks ? (wave + 1) * q4 : ks);
+    for (int64_t k0 = wb; k0 < we; k0 += 16 * kUnroll) {
         F fb[kUnroll], fa0[kUnroll], fa1[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int64_t k = k0 + 64 * u;
-            const bool kin = k < kbeg + ks;
+            const int64_t k = k0 + 16 * u;
+            const bool kin = k < we;
             const int64_t kk = kin ? k : kbeg;
             fb[u] = keep_if(kin && col_ok, ld_frag(pb + kk));
             fa0[u] = keep_if(kin && a_ok, ld_frag(pa0 + kk));
@@ -221,8 +226,10 @@ __global__ __launch_bounds__(NT) void decode_coef_kernel(const float *__restrict
 
 // Y[rows][col0..col0+32) = T_s V_s^T + bias + alpha blockdiag(C_b) (X W_res)
 // (§2.4's fused output with bias and correction weight alpha).  Grid (c2/32,
-// row blocks of whole instances).  The 16-deep steps of both contractions are
-// dealt round-robin to the four wavefronts and reduced in LDS.
+// row blocks of whole instances).  Each wavefront takes a contiguous quarter of
+// both contractions (measured 11-15 % faster per decode step than dealing the
+// 16-deep steps round-robin, whose loads touch 32 bytes of 32 lines each), and
+// the quarters are reduced in LDS.
 template <typename E, bool TWO>
 __global__ __launch_bounds__(NT) void decode_output_kernel(const E *__restrict__ X, const float *__restrict__ T,
                                                            const float *__restrict__ coef,
@@ -253,11 +260,15 @@ __global__ __launch_bounds__(NT) void decode_output_kernel(const E *__restrict__
         // batch's data is waited for only there.
         constexpr int U = kUnrollRes;
         const E *pb = Wres_t + colc * c1 + lk, *pa0 = X + rac * c1 + lk, *pa1 = X + rbc * c1 + lk;
+        // each wavefront streams its own contiguous quarter of c1
+        const int64_t q4 = ((c1 + 63) / 64) * 16;
+        const int64_t kb = wave * q4 < c1 ? wave * q4 : c1;
+        const int64_t ke = (wave + 1) * q4 < c1 ? (wave + 1) * q4 : c1;
         auto load = [&](int64_t k0, F (&fb)[U], F (&fa0)[U], F (&fa1)[U]) __attribute__((always_inline)) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t k = k0 + 64 * u;
-                const int64_t kk = k < c1 ? k : 0;
+                const int64_t k = k0 + 16 * u;
+                const int64_t kk = k < ke ? k : 0;
                 fb[u] = ld_frag(pb + kk);
                 fa0[u] = ld_frag(pa0 + kk);
                 if constexpr (TWO) fa1[u] = ld_frag(pa1 + kk);
@@ -267,18 +278,18 @@ __global__ __launch_bounds__(NT) void decode_output_kernel(const E *__restrict__
                        __attribute__((always_inline)) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const bool kin = k0 + 64 * u < c1;
+                const bool kin = k0 + 16 * u < ke;
                 const F b = keep_if(kin && col_ok, fb[u]);
                 z0 = mma16(z0, keep_if(a_ok, fa0[u]), b);
                 if constexpr (TWO) z1 = mma16(z1, keep_if(b_ok, fa1[u]), b);
             }
         };
         F ab[U], a0[U], a1[U], bb[U], b0[U], b1[U];
-        constexpr int64_t BS = 64 * U;  // K advance of one batch
-        int64_t k0 = 16 * wave;
+        constexpr int64_t BS = 16 * U;  // K advance of one batch
+        int64_t k0 = kb;
         load(k0, ab, a0, a1);
         __builtin_amdgcn_sched_barrier(0);
-        for (; k0 < c1; k0 += 2 * BS) {
+        for (; k0 < ke; k0 += 2 * BS) {
             load(k0 + BS, bb, b0, b1);
             mma(k0, ab, a0, a1);
             __builtin_amdgcn_sched_barrier(0);
@@ -290,12 +301,14 @@ __global__ __launch_bounds__(NT) void decode_output_kernel(const E *__restrict__
     {
         const E *pb = Vs + colc * kw + lk;
         const float *pa0 = T + rac * K1 + lk, *pa1 = T + rbc * K1 + lk;
-        for (int k0 = 16 * wave; k0 < kw; k0 += 64 * kUnroll) {
+        const int q4 = ((kw + 63) / 64) * 16;
+        const int vb = wave * q4 < kw ? wave * q4 : kw, ve = (wave + 1) * q4 < kw ? (wave + 1) * q4 : kw;
+        for (int k0 = vb; k0 < ve; k0 += 16 * kUnroll) {
             F fb[kUnroll], fa0[kUnroll], fa1[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                const int k = k0 + 64 * u;
-                const bool kin = k < kw;
+                const int k = k0 + 16 * u;
+                const bool kin = k < ve;
                 const int kk = kin ? k : 0;
                 fb[u] = keep_if(kin && col_ok, ld_frag(pb + kk));
                 fa0[u] = keep_if(kin && a_ok, frag_from_f32(pa0 + kk, E{}));
