@@ -24,6 +24,7 @@ CASES = [
     (2, 201, 288, 192, 3, 20, 32),    # three blocks, 96 x 64 each
     (4, 33, 128, 320, 1, 48, 16),     # one block: a diagonal-coupled low-rank product
     (6, 80, 512, 256, 4, 100, 64),    # k = 64 (four correction slices)
+    (3, 90, 384, 256, 4, 64, 16),     # grouped block-row product with K = 96: a short last slice
 ]
 
 
