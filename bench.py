@@ -349,6 +349,23 @@ def main():
     log(f"t_dyra {t_dyra * 1e6:.1f} us  dense nn {t_dense_nn * 1e6:.1f} us  nt {t_dense_nt * 1e6:.1f} us  "
         f"dense_ref {t_dense_ref * 1e6:.1f} us")
 
+    # ---- achievable peaks on this GPU, for context beside the published ones:
+    # a streaming copy (reads and writes 1 GiB) and a large hipBLASLt bf16 GEMM
+    copy_n = (1 << 30) // 2
+    src = torch.ones(copy_n, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = time_loop(lambda: dst.copy_(src), 10, 3, stream)
+    del src, dst
+    ga = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    gb = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    gc = torch.empty_like(ga)
+    t_gemm = time_loop(lambda: torch.matmul(ga, gb, out=gc), 10, 3, stream)
+    del ga, gb, gc
+    achievable = {"copy_gbs": round(2.0 * copy_n * 2 / t_copy / 1e9, 1),
+                  "gemm_bf16_tflops": round(2.0 * 8192 ** 3 / t_gemm / 1e12, 1),
+                  "copy": "torch copy_ of 1 GiB bf16 (read + write)", "gemm": "torch.matmul 8192^3 bf16"}
+    log(f"achievable: copy {achievable['copy_gbs']} GB/s, bf16 GEMM {achievable['gemm_bf16_tflops']} TFLOP/s")
+
     # ---- per-kernel durations with events on the launch stream
     reps = max(5, args.steps // 5)
     stage_time, stage_fl = {}, {}
@@ -396,7 +413,10 @@ def main():
                 "algorithmic_bytes_per_launch": round(dom_by / launches, 0),
                 "algorithmic_flops_per_launch": round(dom_fl / launches, 0),
                 "mfma_frac": round(dom_fl / t_dom / peak, 4),
-                "hbm_frac": round(dom_by / t_dom / PEAK_HBM, 4)}
+                "hbm_frac": round(dom_by / t_dom / PEAK_HBM, 4),
+                "frac_of_achievable": round(achieved / (achievable["copy_gbs"] if bound == "hbm"
+                                                        else achievable["gemm_bf16_tflops"]), 4)
+                if w.dtype == "bf16" or bound == "hbm" else None}
 
     # ---- the metric's error on sampled instances: ||Y - X W|| / ||X W|| with
     # the exact product in float64 (the oracle comparison is made in the CPU
@@ -544,6 +564,7 @@ def main():
         "newton_schulz": ns,
         "blast": blast,
         "roofline": roofline,
+        "achievable_peaks": achievable,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
