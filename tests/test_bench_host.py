@@ -61,3 +61,31 @@ def test_cpu_baseline_cycles_to_budget():
     assert r["sample"].startswith("8.00 passes over the 2 instances (80 tokens)")
     r = bench.cpu_baseline(w, [plan], [X], budget_s=0.0)
     assert r["sample"].startswith("1 of 2 instances (5 tokens)")
+
+
+def test_oracle_leg_fills_parity_and_baseline():
+    # library outputs equal to the oracle's on the sampled rows: parity 0, the
+    # own-error gap 0, and the oracle's error and the static part's filled in
+    import types
+
+    import numpy as np
+
+    import oracle as orc
+    spec = synth.LayerSpec("t", 64, 96, r=8, k=4, p=0.7, kaiming=False, x_kind="gaussian")
+    w = types.SimpleNamespace(B=3, n=10, layers=[spec])
+    W = synth.random_weight(64, 96, 5)
+    X = synth.random_matrix(30, 64, 6, "f32")
+    sample = [0, 1, 2]
+    rows = np.arange(30)
+    op = orc.offline_preparation(W.astype(np.float64), 8, 4, 0.0)
+    y_rows = orc.inference(X.exact[rows], 3, 10, op)
+    layers = [dict(spec=spec, W=W, X=X, y_rows=y_rows)]
+    parity = {"t": {"e_dyra": 0.0}, "sample_instances": sample}
+    args = types.SimpleNamespace(no_parity=False, cpu_budget=0.0)
+    cpu = bench.oracle_leg(w, layers, None, [], parity, args)
+    assert parity["t"]["rel_fro_vs_oracle"] == 0.0
+    assert parity["worst_rel_fro"] == 0.0 and parity["worst_own_error_gap"] == 0.0
+    exact = X.exact @ W.astype(np.float64)
+    assert abs(parity["t"]["e_dyra_oracle"] - bench.rel_err(y_rows, exact)) < 1e-5
+    assert parity["t"]["e_weight_only"] >= parity["t"]["e_dyra_oracle"]
+    assert cpu["kind"] == "oracle" and cpu["value"] > 0
