@@ -186,7 +186,8 @@ dyra_status dyra_plan_info(const dyra_plan *plan, int64_t *c1, int64_t *c2, int3
  * failure flag per instance, the left pass output [X A_s | L1] (L1 later
  * replaced by Q = L1 C^-T, C C^T = L1^T L1 + lambda I), M' = Q^T X and R1 per
  * instance (for float32 also Q^T), or the dual form's buffers when n <= 16 or
- * n < k.
+ * n < k.  For a BLAST plan the left pass output is [H_1 .. H_nb | L1], the
+ * block-column inputs of the static product, and there is no dual form.
  */
 size_t dyra_workspace_bytes(const dyra_plan *plan, int64_t B, int64_t n);
 
@@ -210,7 +211,9 @@ size_t dyra_workspace_bytes(const dyra_plan *plan, int64_t B, int64_t n);
  * Cholesky pivot at or below the working precision (lambda = 0 with a
  * numerically rank-deficient L1) sets that instance's failure flag, read back
  * by dyra_forward_status(); its rows then hold the static product X A_s V_s^T
- * alone.  Every call rewrites every flag.
+ * alone.  Every call rewrites every flag.  A BLAST plan (dyra_prepare_blast)
+ * always takes the k x k Cholesky form and returns DYRA_ERR_SHAPE for n < k
+ * with lambda = 0; its static product is X W_hat for the BLAST W_hat.
  */
 dyra_status dyra_forward(const void *X, int64_t B, int64_t n, const dyra_plan *plan, void *Y,
                          void *workspace, size_t workspace_bytes, void *stream);
