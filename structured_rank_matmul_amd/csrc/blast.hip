@@ -3,9 +3,9 @@
 //
 // With W_hat's block (i, j) = U_i diag(s_ij) V_j^T, the static output of block
 // column j is sum_i X_i U_i diag(s_ij) V_j^T.  The forward computes it in
-// three steps: Z_i = X_i U_i (one GEMM per block row), H_j = sum_i Z_i
-// diag(s_ij) (this kernel), Y_j = H_j V_j^T (one GEMM per block column, with
-// the correction slices).  This kernel is elementwise across the rank index:
+// three steps: Z_i = X_i U_i (one grouped GEMM launch over the block rows),
+// H_j = sum_i Z_i diag(s_ij) (this kernel), Y_j = H_j V_j^T (one grouped
+// launch over the block columns, with the correction slices).  This kernel is elementwise across the rank index:
 // for each token row and rank column c the nb values Z_i[c] are mixed by the
 // nb x nb matrix s_..[c] into the nb values H_j[c], so it runs in place over
 // T's first nb * rbp columns, and each thread owns its positions alone.
