@@ -148,25 +148,44 @@ __global__ __launch_bounds__(NT) void decode_coef_kernel(const float *__restrict
     const int tid = threadIdx.x;
     const int64_t b = blockIdx.x;
     const int64_t r0 = b * n;
-    for (int64_t e = tid; e < n * K1; e += NT) {
-        const int64_t i = e / K1, c = e - (e / K1) * K1;
-        // every split's value requested before the first add (one load latency)
-        float v[kMaxSplits];
+    // every split's value of kEB elements per thread requested before the
+    // first add (one load latency per batch; past the end, element 0 and
+    // split 0 are reread and dropped)
+    constexpr int kEB = 4;
+    const int64_t total = n * K1;
+    for (int64_t e0 = tid; e0 < total; e0 += (int64_t)NT * kEB) {
+        float v[kEB][kMaxSplits];
 #pragma unroll
-        for (int q = 0; q < kMaxSplits; ++q) v[q] = q < splits ? partial[((int64_t)q * N + r0 + i) * K1 + c] : 0.f;
-        float s = 0.f;
+        for (int j = 0; j < kEB; ++j) {
+            const int64_t e = e0 + (int64_t)j * NT < total ? e0 + (int64_t)j * NT : 0;
+            const int64_t i = e / K1, c = e - i * K1;
 #pragma unroll
-        for (int q = 0; q < kMaxSplits; ++q) s += v[q];
-        T[(r0 + i) * K1 + c] = s;
-        if (c >= kw) Ls[i][c - kw] = s;
+            for (int q = 0; q < kMaxSplits; ++q)
+                v[j][q] = partial[((int64_t)(q < splits ? q : 0) * N + r0 + i) * K1 + c];
+        }
+#pragma unroll
+        for (int j = 0; j < kEB; ++j) {
+            const int64_t e = e0 + (int64_t)j * NT;
+            if (e >= total) continue;
+            const int64_t i = e / K1, c = e - i * K1;
+            float s = 0.f;
+#pragma unroll
+            for (int q = 0; q < kMaxSplits; ++q) s += q < splits ? v[j][q] : 0.f;
+            T[(r0 + i) * K1 + c] = s;
+            if (c >= kw) Ls[i][c - kw] = s;
+        }
     }
     __syncthreads();
     const int nn = (int)n;
-    for (int e = tid; e < nn * nn; e += NT) {
+    // one Gram element per wavefront at a time: lanes over the correction
+    // columns (k_real <= 64), then a butterfly sum
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int e = wave; e < nn * nn; e += NT / 64) {
         const int i = e / nn, j = e - (e / nn) * nn;
-        double s = 0.0;
-        for (int c = 0; c < k_real; ++c) s += (double)Ls[i][c] * (double)Ls[j][c];
-        K[i][j] = s;
+        double s = lane < k_real ? (double)Ls[i][lane] * (double)Ls[j][lane] : 0.0;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+        if (lane == 0) K[i][j] = s;
     }
     __syncthreads();
     if (tid == 0) {
