@@ -125,3 +125,23 @@ def test_factor_shapes_validated():
         orc.blast_matrix(U, np.zeros((2, 2, 3)), V, 2)       # coupling rank mismatch
     with pytest.raises(ValueError):
         orc.blast_matrix(U, np.zeros((2, 2, 2)), np.zeros((12, 3)), 2)
+
+
+def test_blast_generator_is_seeded_and_shaped():
+    a = synth.random_blast_weight(64, 96, 4, 8, 3)
+    b = synth.random_blast_weight(64, 96, 4, 8, 3)
+    c = synth.random_blast_weight(64, 96, 4, 8, 4)
+    for x, y in ((a.W, b.W), (a.U, b.U), (a.S, b.S), (a.V, b.V)):
+        assert np.array_equal(x, y)
+    assert not np.array_equal(a.W, c.W)
+    assert a.W.shape == (64, 96) and a.U.shape == (64, 8) and a.V.shape == (96, 8) and a.S.shape == (4, 4, 8)
+    assert all(m.dtype == np.float32 for m in (a.W, a.U, a.S, a.V))
+    # the workload stand-ins: one per layer, distinct across layers and block counts
+    w = synth.WORKLOADS["vitb_fc1"]
+    spec = w.layers[0]
+    b4 = synth.make_blast_weight(w, spec, 4, 16)
+    b2 = synth.make_blast_weight(w, spec, 2, 16)
+    assert b4.W.shape == (spec.c1, spec.c2) and b4.nb == 4 and b2.nb == 2
+    assert not np.array_equal(b4.U, b2.U)
+    with pytest.raises(ValueError):
+        synth.random_blast_weight(60, 96, 4, 8, 1)   # 4 does not divide 60
