@@ -144,4 +144,4 @@ def test_blast_generator_is_seeded_and_shaped():
     assert b4.W.shape == (spec.c1, spec.c2) and b4.nb == 4 and b2.nb == 2
     assert not np.array_equal(b4.U, b2.U)
     with pytest.raises(ValueError):
-        synth.random_blast_weight(60, 96, 4, 8, 1)   # 4 does not divide 60
+        synth.random_blast_weight(62, 96, 4, 8, 1)   # 4 does not divide 62
