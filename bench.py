@@ -36,7 +36,7 @@ def stage_flops(spec, B, n):
     return {
         # one pass over X gives X A_s and L1 = X P_L
         "left": 2.0 * N * c1 * (r + k),
-        # G = L1^T L1 and Q = L1 C^-T per instance
+            # G = L1^T L1 and Q = L1 C^-T per instance
         "gram_q": 2.0 * N * k * k + 1.0 * N * k * k,
         "mprime": 2.0 * N * k * c1,
         "right": 2.0 * B * k * c1 * c2,
@@ -50,13 +50,34 @@ def stage_flops(spec, B, n):
 
 
 def stage_bytes(spec, B, n, es):
-    """Algorithmic HBM bytes of each kernel for one layer call (every operand
-    read once, every result written once; es = element size)."""
+    """Algorithmic HBM bytes of each kernel for one layer call.  The layer's
+    algorithmic bytes are X, Y and the plan's factors ([A_s | P_L], V_s,
+    W_res), each moved once in the element size es; each is counted at the
+    kernel that must move it.  The intermediates (T = [X A_s | L1], Q, M', R1)
+    and a second read of X are practical extra traffic, reported by
+    stage_operand_bytes and the counters, not here."""
+    N = B * n
+    c1, c2, r, k = spec.c1, spec.c2, spec.r, spec.k
+    return {
+        "left": es * (N * c1 + (r + k) * c1),
+        "gram_q": 0,
+        "mprime": 0,
+        "right": es * (c1 * c2),
+        "output": es * (c2 * r + N * c2),
+        "decode_project": es * (N * c1 + (r + k) * c1),
+        "decode_coef": 0,
+        "decode_output": es * (c2 * r + c1 * c2 + N * c2),
+    }
+
+
+def stage_operand_bytes(spec, B, n, es):
+    """Bytes each kernel reads and writes at the least, intermediates
+    included (every operand read once, every result written once)."""
     N = B * n
     c1, c2, r, k = spec.c1, spec.c2, spec.r, spec.k
     return {
         "left": es * (N * c1 + (r + k) * c1 + N * (r + k)),
-        "gram_q": es * (2 * N * k),
+        "gram_q": es * (3 * N * k),
         "mprime": es * (N * c1 + N * k + B * k * c1),
         "right": es * (B * k * c1 + c1 * c2 + B * k * c2),
         "output": es * (N * (r + k) + c2 * r + B * k * c2 + N * c2),
@@ -75,7 +96,7 @@ def dual_form(spec, n):
 # kernel behind each stage of the primal path (for the roofline record)
 STAGE_KERNEL = {
     "left": "gemm_kernel (T = X [A_s | P_L])",
-    "gram_q": "cholq_kernel",
+    "gram_q": "gram_chol_kernel + q_apply_kernel",
     "mprime": "mprime_tr_kernel",
     "right": "gemm_kernel (R1 = M' W_res, R1t store)",
     "output": "gemm_kernel with correction slices (Y = T_s V_s^T + Q R1_b)",
@@ -146,11 +167,29 @@ def cpu_baseline(workload, plans_orc, X_host, budget_s):
         if t_total >= budget_s:
             break
     tokens = done * n
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+    except Exception:  # pragma: no cover
+        pass
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     if done <= workload.B:
         what = f"{done} of {workload.B} instances"
     else:
         what = f"{done / workload.B:.2f} passes over the {workload.B} instances"
     return {"value": tokens / t_total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model, "blas": blas, "numpy": np.__version__,
             "sample": f"{what} ({tokens} tokens) through all {len(workload.layers)} "
                       f"layers, float64 numpy, {t_total:.1f} s"}
 
@@ -388,13 +427,16 @@ def main():
             stage_fl[nm] = stage_fl.get(nm, 0.0) + fl.get(nm, 0.0)
         L["stages"] = per
         log(f"{L['spec'].name}: " + "  ".join(f"{k} {v * 1e6:.1f}us" for k, v in per.items()))
-    # ---- roofline of the dominant kernel: algorithmic FLOPs and bytes per
-    # launch against MFMA and HBM peaks; the larger ideal time is the bound
+    # ---- roofline of the dominant kernel: its algorithmic FLOPs and bytes
+    # per launch (the layer's X, Y and factors counted at the kernel that must
+    # move them) against the MFMA and HBM peaks; the larger ideal time is the
+    # bound.  The bytes it moves including intermediates are reported beside.
     dom = max(stage_time, key=stage_time.get)
     es = 2 if w.dtype == "bf16" else 4
     launches = len(layers)
     dom_fl = sum(stage_flops(L["spec"], B, n)[dom] for L in layers)
     dom_by = sum(stage_bytes(L["spec"], B, n, es)[dom] for L in layers)
+    dom_op = sum(stage_operand_bytes(L["spec"], B, n, es)[dom] for L in layers)
     peak = PEAK_BF16 if w.dtype == "bf16" else PEAK_FP32
     t_dom = stage_time[dom]
     if dom_by / PEAK_HBM > dom_fl / peak:
@@ -412,11 +454,20 @@ def main():
                 "avg_launch_us": round(t_dom / launches * 1e6, 2),
                 "algorithmic_bytes_per_launch": round(dom_by / launches, 0),
                 "algorithmic_flops_per_launch": round(dom_fl / launches, 0),
+                "operand_bytes_per_launch": round(dom_op / launches, 0),
                 "mfma_frac": round(dom_fl / t_dom / peak, 4),
                 "hbm_frac": round(dom_by / t_dom / PEAK_HBM, 4),
                 "frac_of_achievable": round(achieved / (achievable["copy_gbs"] if bound == "hbm"
                                                         else achievable["gemm_bf16_tflops"]), 4)
                 if w.dtype == "bf16" or bound == "hbm" else None}
+    # every stage on the same accounting (summed over the step's launches)
+    stage_roofline = {}
+    for nm, t in stage_time.items():
+        fl = sum(stage_flops(L["spec"], B, n).get(nm, 0.0) for L in layers)
+        by = sum(stage_bytes(L["spec"], B, n, es).get(nm, 0.0) for L in layers)
+        b_ = "hbm" if by / PEAK_HBM > fl / peak else "mfma"
+        stage_roofline[nm] = {"bound": b_, "us_per_step": round(t * 1e6, 2),
+                              "frac": round((by / PEAK_HBM if b_ == "hbm" else fl / peak) / t, 4)}
 
     # ---- the metric's error on sampled instances: ||Y - X W|| / ||X W|| with
     # the exact product in float64 (the oracle comparison is made in the CPU
@@ -564,6 +615,7 @@ def main():
         "newton_schulz": ns,
         "blast": blast,
         "roofline": roofline,
+        "stage_roofline": stage_roofline,
         "achievable_peaks": achievable,
         "cpu_baseline": cpu,
     }

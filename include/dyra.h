@@ -211,7 +211,12 @@ size_t dyra_workspace_bytes(const dyra_plan *plan, int64_t B, int64_t n);
  * Cholesky pivot at or below the working precision (lambda = 0 with a
  * numerically rank-deficient L1) sets that instance's failure flag, read back
  * by dyra_forward_status(); its rows then hold the static product X A_s V_s^T
- * alone.  Every call rewrites every flag.  A BLAST plan (dyra_prepare_blast)
+ * alone.  Every call that forms a correction rewrites every flag; the
+ * weight-only path (k = 0) writes none, and dyra_forward_status reports no
+ * failure for it.  The kernels' one-time host set-up (LDS limits, resident
+ * workgroups per CU) is done by the preparation calls on the plan's device,
+ * so a forward call on a prepared device makes no HIP call besides its kernel
+ * launches and can be captured into a graph.  A BLAST plan (dyra_prepare_blast)
  * always takes the k x k Cholesky form and returns DYRA_ERR_SHAPE for n < k
  * with lambda = 0; its static product is X W_hat for the BLAST W_hat.
  */
@@ -237,7 +242,8 @@ dyra_status dyra_forward_ex(const void *X, int64_t B, int64_t n, const dyra_plan
  * Number of instances whose SPD solve broke down in the last
  * dyra_forward(X, B, n, plan, ...) that used this workspace.  Copies the B
  * flags from the workspace on `stream` and synchronises it; *failures
- * receives the count.
+ * receives the count.  For the weight-only path (k = 0) it is 0 without a
+ * copy.
  */
 dyra_status dyra_forward_status(const dyra_plan *plan, int64_t B, int64_t n, const void *workspace,
                                 void *stream, int32_t *failures);
@@ -247,7 +253,8 @@ dyra_status dyra_forward_status(const dyra_plan *plan, int64_t B, int64_t n, con
  * timing point.  X device [N][c1], Wt device [c2][c1] (W transposed, i.e. the
  * nn.Linear weight layout), Y device [N][c2], all in `dtype`, row-major,
  * 16-byte aligned; float32 accumulation.  c1 and c2 multiples of 32.
- * Asynchronous on `stream`.
+ * Asynchronous on `stream`.  The first call on a device where no plan was
+ * prepared also does the GEMM kernels' one-time host set-up.
  */
 dyra_status dyra_dense_ref(const void *X, const void *Wt, int64_t N, int64_t c1, int64_t c2,
                            dyra_dtype dtype, void *Y, void *stream);

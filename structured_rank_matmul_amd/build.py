@@ -4,6 +4,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
@@ -34,17 +35,19 @@ def _run(cmd):
 def build(verbose: bool = False) -> str:
     """Compiles every source and links libdyra.so; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
-    objs = []
-    for src in CXX_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
-        _run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
-        objs.append(obj)
-    for src in HIP_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
-        out = _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
-        if verbose and out.strip():
-            print(out)
-        objs.append(obj)
+    jobs = [(["g++", *CXX_FLAGS], src) for src in CXX_SOURCES] + [([HIPCC, *HIP_FLAGS], src) for src in HIP_SOURCES]
+    objs = [os.path.join(BUILD, src + ".o") for _, src in jobs]
+
+    def compile_one(job):
+        (cc, src), obj = job
+        return _run([*cc, "-c", os.path.join(CSRC, src), "-o", obj])
+
+    # the sources compile independently: one compiler process per source
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        for out in pool.map(compile_one, zip(jobs, objs)):
+            if verbose and out.strip():
+                print(out)
     tmp = OUT + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-lgomp"])
     os.replace(tmp, OUT)

@@ -5,13 +5,16 @@
 // column j is sum_i X_i U_i diag(s_ij) V_j^T.  The forward computes it in
 // three steps: Z_i = X_i U_i (one grouped GEMM launch over the block rows),
 // H_j = sum_i Z_i diag(s_ij) (this kernel), Y_j = H_j V_j^T (one grouped
-// launch over the block columns, with the correction slices).  This kernel is elementwise across the rank index:
-// for each token row and rank column c the nb values Z_i[c] are mixed by the
+// launch over the block columns, with the correction slices).  This kernel is
+// elementwise across the rank index: for each token row and rank column c the nb values Z_i[c] are mixed by the
 // nb x nb matrix s_..[c] into the nb values H_j[c], so it runs in place over
 // T's first nb * rbp columns, and each thread owns its positions alone.
 // Smix rows are rbp floats, rbp a multiple of 32, so the float4 loads and the
 // LDS image stay aligned.
 #include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <mutex>
 
 #include "dyra_kernels.h"
 #include "mfma_tile.h"
@@ -76,6 +79,25 @@ __global__ __launch_bounds__(kMixThreads) void blast_mix_kernel(E *__restrict__ 
     }
 }
 
+// One-time set-up of a mix instantiation on the current device (its dynamic
+// LDS limit: up to 128 KB at four blocks and rank 2048), under a lock.
+template <typename E, int NB> hipError_t mix_setup() {
+    static std::mutex mu;
+    static std::atomic<uint64_t> done{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev < 64 ? (uint64_t{1} << dev) : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    std::lock_guard<std::mutex> lock(mu);
+    if (bit && (done.load(std::memory_order_relaxed) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute((const void *)blast_mix_kernel<E, NB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)(sizeof(float) * NB * NB * 2048));
+    if (e != hipSuccess) return e;
+    done.fetch_or(bit, std::memory_order_release);
+    return hipSuccess;
+}
+
 template <typename E, int NB>
 hipError_t mix_launch(E *T, int64_t ldt, int64_t N, int rbp, const float *Smix, hipStream_t st) {
     constexpr int VEC = 16 / (int)sizeof(E);
@@ -83,16 +105,9 @@ hipError_t mix_launch(E *T, int64_t ldt, int64_t N, int rbp, const float *Smix, 
     const int64_t want = (N + rows_per_iter - 1) / rows_per_iter;
     const unsigned grid = (unsigned)(want < kMixBlocks ? want : kMixBlocks);
     const size_t smem = sizeof(float) * NB * NB * (size_t)rbp;
-    auto kfn = blast_mix_kernel<E, NB>;
-    static bool attr = false;
-    if (!attr) {
-        // up to 128 KB at four blocks and rank 2048
-        const hipError_t e = hipFuncSetAttribute((const void *)kfn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)(sizeof(float) * NB * NB * 2048));
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
-    hipLaunchKernelGGL(kfn, dim3(grid), dim3(kMixThreads), smem, st, T, ldt, N, rbp, Smix);
+    const hipError_t e = mix_setup<E, NB>();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((blast_mix_kernel<E, NB>), dim3(grid), dim3(kMixThreads), smem, st, T, ldt, N, rbp, Smix);
     return hipGetLastError();
 }
 
@@ -113,6 +128,16 @@ hipError_t launch_blast_mix(E *T, int64_t ldt, int64_t N, int nb, int rbp, const
     return hipErrorInvalidValue;
 }
 
+template <typename E> hipError_t blast_prepare() {
+    hipError_t e;
+    if ((e = mix_setup<E, 1>()) != hipSuccess) return e;
+    if ((e = mix_setup<E, 2>()) != hipSuccess) return e;
+    if ((e = mix_setup<E, 3>()) != hipSuccess) return e;
+    return mix_setup<E, 4>();
+}
+
+template hipError_t blast_prepare<bf16>();
+template hipError_t blast_prepare<float>();
 template hipError_t launch_blast_mix<bf16>(bf16 *, int64_t, int64_t, int, int, const float *, hipStream_t);
 template hipError_t launch_blast_mix<float>(float *, int64_t, int64_t, int, int, const float *, hipStream_t);
 

@@ -87,6 +87,7 @@ Path path_for(const dyra_plan *p, int64_t n) {
 //   T      [N][kw + kc]          X A_s next to L1 (then Q) for every token
 //   Qt     [B][kc][npad]         Q_b^T, token-contiguous, npad = n rounded up to 32
 //                                (float32 only; bf16 reads Q_b from T)
+//   Ct     float32 [B][kc][kc]   Cholesky factor of G_b by columns (bf16 only)
 //   Mp     [B * kc][c1]          M'_b = Q_b^T X_b stacked over instances
 //   R1t    [B][c2][kc]           R1_b transposed
 //   with further ALS steps (half_steps > 2, als.hip):
@@ -99,7 +100,7 @@ Path path_for(const dyra_plan *p, int64_t n) {
 //   F      float32 [B][kc][kc]   G^-1/2 per instance
 //   dual   decode workspace      (n <= 16 or n < k only)
 struct Layout {
-    size_t flags, T, Qt, Mp, R1t, C, R1row, Sp, H, Kp, F, dual, total;
+    size_t flags, T, Qt, Ct, Mp, R1t, C, R1row, Sp, H, Kp, F, dual, total;
     int64_t npad;
 };
 
@@ -118,6 +119,8 @@ Layout workspace_layout(const dyra_plan *p, int64_t B, int64_t n) {
         L.npad = round_up(n, 32);
         L.Qt = off;
         if (p->dtype == DYRA_F32) off += align_up(es * B * p->kc * L.npad);
+        L.Ct = off;
+        if (p->dtype == DYRA_BF16 && p->ns_iters == 0) off += align_up(sizeof(float) * (size_t)B * p->kc * p->kc);
         L.Mp = off;
         off += align_up(es * B * p->kc * p->c1);
         L.R1t = off;
@@ -167,6 +170,16 @@ dyra_status upload_rounded(const std::vector<double> &src, dyra_dtype dtype, voi
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 dyra_status hip_status(hipError_t e) { return e == hipSuccess ? DYRA_OK : DYRA_ERR_HIP; }
+
+// The kernels' one-time host set-up on the current device, done while
+// preparing a plan so that forward calls only enqueue work.
+dyra_status prepare_launches(dyra_dtype dtype) {
+    if (dtype == DYRA_BF16)
+        return hip_status(dyra::gemm_prepare<bf16>()) == DYRA_OK ? hip_status(dyra::blast_prepare<bf16>())
+                                                                 : DYRA_ERR_HIP;
+    return hip_status(dyra::gemm_prepare<float>()) == DYRA_OK ? hip_status(dyra::blast_prepare<float>())
+                                                              : DYRA_ERR_HIP;
+}
 
 dyra_status check_device(int device) {
     int cur = -1;
@@ -271,7 +284,7 @@ dyra_status run_forward(const E *X, int64_t B, int64_t n, const dyra_plan *p, co
                         return t;
                 } else {
                     if ((t = hip_status(dyra::launch_gram_q<E>(T, ldt, p->kw, B, n, L.npad, p->k, p->kc, p->lambda,
-                                                               Qt, flags, Cf, st))) != DYRA_OK)
+                                                               Qt, (float *)(ws + L.Ct), flags, Cf, st))) != DYRA_OK)
                         return t;
                     if ((t = mark()) != DYRA_OK) return t;
                 }
@@ -453,6 +466,7 @@ dyra_status dyra_prepare_ex(const float *W, int64_t c1, int64_t c2, int32_t r, i
     if ((s = upload(A, &p->Aext)) == DYRA_OK && (s = upload(V, &p->Vs)) == DYRA_OK)
         s = upload(Rt, &p->Wres_t);
     if (s == DYRA_OK && p->half_steps > 2) s = upload(f.W_res, &p->Wres);
+    if (s == DYRA_OK) s = prepare_launches(dtype);
     if (prev >= 0) (void)hipSetDevice(prev);
     if (s != DYRA_OK) {
         dyra_plan_destroy(p);
@@ -529,6 +543,7 @@ dyra_status dyra_prepare_blast(const float *W, int64_t c1, int64_t c2, int32_t n
         else if (hipMemcpy(p->Smix, Sm.data(), Sm.size() * sizeof(float), hipMemcpyHostToDevice) != hipSuccess)
             s = DYRA_ERR_HIP;
     }
+    if (s == DYRA_OK) s = prepare_launches(dtype);
     if (prev >= 0) (void)hipSetDevice(prev);
     if (s != DYRA_OK) {
         dyra_plan_destroy(p);
@@ -599,7 +614,8 @@ dyra_status dyra_forward_status(const dyra_plan *plan, int64_t B, int64_t n, con
                                 int32_t *failures) {
     if (!plan || !workspace || !failures || B < 0 || n < 1) return DYRA_ERR_ARG;
     *failures = 0;
-    if (B == 0) return DYRA_OK;
+    // the weight-only path solves nothing and writes no flag
+    if (B == 0 || path_for(plan, n) == Path::Static) return DYRA_OK;
     const Layout L = workspace_layout(plan, B, n);
     std::vector<int32_t> flags((size_t)B);
     hipStream_t st = (hipStream_t)stream;

@@ -9,6 +9,13 @@ namespace dyra {
 
 typedef __bf16 bf16;
 
+// One-time host set-up (dynamic LDS limits, resident workgroups per CU) of
+// every GEMM instantiation on the current device, so that later launches only
+// enqueue.  Launches that find their instantiation not set up do it first.
+template <typename E> hipError_t gemm_prepare();
+// The same for the BLAST mix kernels.
+template <typename E> hipError_t blast_prepare();
+
 // D[M][N] (leading dim ldd) = A[M][K] B[N][K]^T, K a multiple of 32.
 template <typename E>
 hipError_t launch_gemm_store(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N, int64_t K,
@@ -22,13 +29,15 @@ hipError_t launch_right(const E *Mp, const E *Wres_t, int64_t rows, int64_t c1, 
 // With C C^T = L1_b^T L1_b + lambda I: Q_b = L1_b C^-T replaces L1_b in place
 // (columns [off, off + kc) of T's rows b*n .. b*n + n - 1, leading dimension
 // ldt).  float32 also writes Qt[b] = Q_b^T ([kc][npad], token-contiguous, zero
-// for tokens n..npad-1); bf16 leaves Qt untouched.  flags[b] = 1 if a pivot
-// broke down (then Q_b = 0).  kc in {16, 32, 48, 64}.  Cout, if not null,
-// receives the Cholesky factor C_b ([B][kc][kc] float64, lower, identity on
-// the padding) for the L updates of further ALS steps.
+// for tokens n..npad-1); bf16 leaves Qt untouched and keeps C_b, column by
+// column, in Ct ([B][kc][kc] float32 workspace) between its two kernels.
+// flags[b] = 1 if a pivot broke down (then Q_b = 0).  kc in {16, 32, 48,
+// 64}.  Cout, if not null, receives the Cholesky factor C_b ([B][kc][kc]
+// float64, lower, identity on the padding) for the L updates of further ALS
+// steps.
 template <typename E>
 hipError_t launch_gram_q(E *T, int64_t ldt, int64_t off, int64_t B, int64_t n, int64_t npad, int kc_real, int kc,
-                         float lambda, E *Qt, int *flags, double *Cout, hipStream_t st);
+                         float lambda, E *Qt, float *Ct, int *flags, double *Cout, hipStream_t st);
 
 // Mp[b*kc + i][:] = (Q_b^T X_b)[i][:]: bf16 reads Q_b from T (as left by
 // launch_gram_q), float32 from Qt.

@@ -28,7 +28,9 @@
 #include "dyra_kernels.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "mfma_tile.h"
@@ -439,24 +441,49 @@ template <typename E, int BM, int BN, int NS, int SB, bool ROWS> constexpr size_
                : stage_bytes<BM, BN, NS, SB>();
 }
 
+// One-time host set-up of a kernel instantiation on the current device: its
+// dynamic LDS limit and the number of workgroups resident per CU (the
+// persistent grid's size).  Done once per device under a lock, normally from
+// the preparation calls (gemm_prepare), so that a forward call only launches.
+struct LaunchSetup {
+    std::mutex mu;
+    std::atomic<uint64_t> done{0};  // bit d: device d is set up
+    std::atomic<int> per_cu{0};     // the same on every gfx950 device
+};
+
+template <class K>
+hipError_t ensure_setup(LaunchSetup &ls, K kfn, int threads, size_t smem) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev < 64 ? (uint64_t{1} << dev) : 0;
+    if (bit && (ls.done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    std::lock_guard<std::mutex> lock(ls.mu);
+    if (bit && (ls.done.load(std::memory_order_relaxed) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute((const void *)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    int occ = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kfn, threads, smem);
+    if (e != hipSuccess) return e;
+    ls.per_cu.store(occ > 0 ? occ : 1, std::memory_order_relaxed);
+    ls.done.fetch_or(bit, std::memory_order_release);
+    return hipSuccess;
+}
+
+// setup_only: run the one-time set-up of this instantiation and launch nothing.
 template <typename E, int BM, int BN, int WM, int WN, int NS, int SB, bool ROWS, bool CORR, bool GROUPED,
           class Epi>
 hipError_t gemm_launch(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N, int64_t K,
-                       const Corr<E> &corr, Epi epi, hipStream_t st) {
+                       const Corr<E> &corr, Epi epi, hipStream_t st, bool setup_only = false) {
     static_assert(gemm_smem<E, BM, BN, NS, SB, ROWS>() <= kLdsBytes, "LDS");
-    if (K % 16 != 0) return hipErrorInvalidValue;
-    if (GROUPED && corr.gcols <= 0) return hipErrorInvalidValue;
     auto kfn = gemm_kernel<E, BM, BN, WM, WN, NS, SB, ROWS, CORR, Epi, GROUPED>;
     constexpr size_t smem = gemm_smem<E, BM, BN, NS, SB, ROWS>();
-    static int per_cu = 0;  // resident workgroups per CU
-    if (per_cu == 0) {
-        hipError_t e = hipFuncSetAttribute((const void *)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (e != hipSuccess) return e;
-        int occ = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kfn, 64 * WM * WN, smem);
-        if (e != hipSuccess) return e;
-        per_cu = occ > 0 ? occ : 1;
-    }
+    static LaunchSetup ls;
+    hipError_t e = ensure_setup(ls, kfn, 64 * WM * WN, smem);
+    if (e != hipSuccess || setup_only) return e;
+    if (K % 16 != 0) return hipErrorInvalidValue;
+    if (GROUPED && corr.gcols <= 0) return hipErrorInvalidValue;
+    const int per_cu = ls.per_cu.load(std::memory_order_relaxed);
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
     const int ntiles = tiles_m * tiles_n;
     const int per_xcd = (ntiles + 7) / 8;
@@ -499,30 +526,61 @@ bool pick_shape(int64_t M, int64_t N, int gcols, Shape &best) {
     return found || fits64;
 }
 
+template <typename E, bool ROWS, bool CORR, bool GROUPED, class Epi>
+hipError_t launch_shape(Shape shape, const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N,
+                        int64_t K, const Corr<E> &corr, Epi epi, hipStream_t st, bool setup_only) {
+    switch (shape) {
+    case Shape::T256x256:
+        // float32 keeps 64-byte slices (128 would spill it)
+        if constexpr (sizeof(E) == 4)
+            return gemm_launch<E, 256, 256, 4, 2, 4, 64, ROWS, CORR, GROUPED>(A, lda, B, ldb, M, N, K, corr, epi, st,
+                                                                              setup_only);
+        else return gemm_launch<E, 256, 256, 4, 2, 2, 128, ROWS, CORR, GROUPED>(A, lda, B, ldb, M, N, K, corr, epi, st,
+                                                                               setup_only);
+    case Shape::T256x160:
+        return gemm_launch<E, 256, 160, 8, 1, 3, 128, ROWS, CORR, GROUPED>(A, lda, B, ldb, M, N, K, corr, epi, st,
+                                                                           setup_only);
+    case Shape::T256x128:
+        return gemm_launch<E, 256, 128, 4, 2, 3, 128, ROWS, CORR, GROUPED>(A, lda, B, ldb, M, N, K, corr, epi, st,
+                                                                           setup_only);
+    case Shape::T128x128:
+        return gemm_launch<E, 128, 128, 2, 2, 4, 128, ROWS, CORR, GROUPED>(A, lda, B, ldb, M, N, K, corr, epi, st,
+                                                                           setup_only);
+    case Shape::T64x64:
+        return gemm_launch<E, 64, 64, 2, 2, 4, 128, ROWS, CORR, GROUPED>(A, lda, B, ldb, M, N, K, corr, epi, st,
+                                                                         setup_only);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <typename E, bool ROWS, bool CORR, bool GROUPED = false, class Epi>
 hipError_t gemm_dispatch(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N, int64_t K,
                          const Corr<E> &corr, Epi epi, hipStream_t st) {
     Shape shape;
     if (!pick_shape(M, N, GROUPED ? corr.gcols : 0, shape)) return hipErrorInvalidValue;
-    switch (shape) {
-    case Shape::T256x256:
-        // float32 keeps 64-byte slices (128 would spill it)
-        if constexpr (sizeof(E) == 4)
-            return gemm_launch<E, 256, 256, 4, 2, 4, 64, ROWS, CORR, GROUPED>(A, lda, B, ldb, M, N, K, corr, epi, st);
-        else return gemm_launch<E, 256, 256, 4, 2, 2, 128, ROWS, CORR, GROUPED>(A, lda, B, ldb, M, N, K, corr, epi, st);
-    case Shape::T256x160:
-        return gemm_launch<E, 256, 160, 8, 1, 3, 128, ROWS, CORR, GROUPED>(A, lda, B, ldb, M, N, K, corr, epi, st);
-    case Shape::T256x128:
-        return gemm_launch<E, 256, 128, 4, 2, 3, 128, ROWS, CORR, GROUPED>(A, lda, B, ldb, M, N, K, corr, epi, st);
-    case Shape::T128x128:
-        return gemm_launch<E, 128, 128, 2, 2, 4, 128, ROWS, CORR, GROUPED>(A, lda, B, ldb, M, N, K, corr, epi, st);
-    case Shape::T64x64:
-        return gemm_launch<E, 64, 64, 2, 2, 4, 128, ROWS, CORR, GROUPED>(A, lda, B, ldb, M, N, K, corr, epi, st);
+    return launch_shape<E, ROWS, CORR, GROUPED>(shape, A, lda, B, ldb, M, N, K, corr, epi, st, false);
+}
+
+// The one-time set-up of every tile shape of one kernel family.
+template <typename E, bool ROWS, bool CORR, bool GROUPED, class Epi> hipError_t setup_family() {
+    for (Shape sh : {Shape::T256x256, Shape::T256x160, Shape::T256x128, Shape::T128x128, Shape::T64x64}) {
+        const hipError_t e = launch_shape<E, ROWS, CORR, GROUPED>(sh, nullptr, 0, nullptr, 0, 0, 0, 0, Corr<E>{},
+                                                                  Epi{}, nullptr, true);
+        if (e != hipSuccess) return e;
     }
-    return hipErrorInvalidValue;
+    return hipSuccess;
 }
 
 }  // namespace
+
+template <typename E> hipError_t gemm_prepare() {
+    hipError_t e;
+    if ((e = setup_family<E, true, false, false, RowStore<E>>()) != hipSuccess) return e;   // left pass, dense
+    if ((e = setup_family<E, true, false, true, RowStore<E>>()) != hipSuccess) return e;    // grouped (BLAST)
+    if ((e = setup_family<E, false, false, false, R1tStore<E>>()) != hipSuccess) return e;  // right factor
+    if ((e = setup_family<E, true, true, false, RowStore<E>>()) != hipSuccess) return e;    // output
+    return setup_family<E, true, true, true, RowStore<E>>();                                // BLAST output
+}
 
 template <typename E>
 hipError_t launch_gemm_store(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N, int64_t K,
@@ -579,6 +637,8 @@ hipError_t launch_output(const E *T, int64_t ldt, int kw, int kc, const E *Vs, c
     return launch_output_ex<E>(T, ldt, kw, Vs, kw, kw, kc, R1t, c2 * kc, Ntok, n, c2, bias, Y, c2, 0, 0, st);
 }
 
+template hipError_t gemm_prepare<bf16>();
+template hipError_t gemm_prepare<float>();
 template hipError_t launch_gemm_store<bf16>(const bf16 *, int64_t, const bf16 *, int64_t, int64_t, int64_t, int64_t,
                                             bf16 *, int64_t, hipStream_t);
 template hipError_t launch_gemm_store<float>(const float *, int64_t, const float *, int64_t, int64_t, int64_t,

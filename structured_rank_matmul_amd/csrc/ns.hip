@@ -15,7 +15,7 @@
 // mat_product).
 //
 //   ns_factor  workgroup per instance: G by MFMA over the instance's tokens
-//              (chunks of 256, transposed through LDS as in cholq_kernel),
+//              (chunks of 256, transposed through LDS as in gram_chol_kernel),
 //              then the iteration on 64 x 64 float32 matrices held in LDS,
 //              one 32 x 32 block of every product per wavefront
 //              (v_mfma_f32_32x32x2_f32).  Correction indices past the real

@@ -15,14 +15,14 @@
 // L1_b lives in columns [off, off + kc) of the rows b*n .. b*n + n - 1 of the
 // row-major pass output T (leading dimension ldt) and Q_b overwrites it there.
 //
-//   cholq (bf16)  workgroup (token block of 256, instance b): G by MFMA over
-//            all n tokens of b (the block's own tokens are loaded once, into
-//            registers, and serve both G and the elimination), then every
-//            wavefront factors G with one matrix row per lane and, in the same
-//            elimination steps, turns its 64 token rows of L1_b into rows of
-//            Q_b: factoring [G; L1_b] leaves L1_b C^-T in the lower block.  The
-//            pivot row's entries reach all lanes through v_readlane, so the
-//            factorisation has no barrier and no LDS traffic.
+//   gram_chol (bf16)  workgroup per instance b: G by MFMA over all n tokens
+//            of b, then its Cholesky factor C in one wavefront with one matrix
+//            row per lane (the pivot row reaches all lanes through
+//            v_readlane: no barrier, no LDS traffic), stored column by column.
+//   q_apply (bf16)  workgroup per (64 tokens, instance b): Q_b = L1_b C^-T in
+//            place by forward substitution, each token row over a quad of
+//            lanes, C staged in LDS.  G is complete before any row of T is
+//            rewritten: the two are separate launches.
 //   gram_q (float32)  one workgroup per instance, all in float64: G, a
 //            right-looking Cholesky and the inverse C^-1 with 16 matrix entries
 //            per thread, then q_t = C^-1 l_t per token, written both in place
@@ -41,11 +41,6 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int TK = 32;  // tokens per slice of the token contraction (mprime)
-
-// Optional per-phase timestamps for profiling builds (empty in the library).
-#ifndef DYRA_PHASE_MARK
-#define DYRA_PHASE_MARK(i)
-#endif
 
 // Transposes a [TK tokens][kc] slice of a row-major [tokens][kc] matrix into
 // LDS dst[feature][token] (row stride ST); tokens at or beyond `tokens` read 0.
@@ -72,69 +67,95 @@ __device__ __forceinline__ void load_transposed(const E *src, int64_t ld, int64_
 }
 
 // ---------------------------------------------------------------- bf16 path
+// Lane-per-row Cholesky step K of a matrix held one row per lane (g of lane
+// i = row i): the pivot row's entries reach every lane through v_readlane in
+// batches of 8.  After all steps g[0..i] of lane i is row i of the lower
+// factor C (G = C C^T); entries past the diagonal are left over.
+template <int KC, int K, int M0>
+__device__ __forceinline__ void chol_batch(float (&g)[KC], float a) {
+    constexpr int CNT = (KC - M0) < 8 ? (KC - M0) : 8;
+    float sv[CNT];
+#pragma unroll
+    for (int u = 0; u < CNT; ++u) sv[u] = bcast(g[M0 + u], K);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < CNT; ++u) g[M0 + u] = fmaf(-a, sv[u], g[M0 + u]);
+#pragma unroll
+    for (int u = 0; u < CNT; ++u) asm volatile("" : "+v"(g[M0 + u]));
+    if constexpr (M0 + 8 < KC) chol_batch<KC, K, M0 + 8>(g, a);
+}
+
+template <int KC, int K>
+__device__ __forceinline__ void chol_step(float (&g)[KC], int kc_real, float th, bool &fail) {
+    if constexpr (K < KC) {
+        float pk = bcast(g[K], K);
+        const bool bad = K < kc_real && !(pk > th);  // padding pivots are 1
+        fail = fail || bad;
+        pk = bad ? 1.f : pk;
+        const float a = g[K] * __builtin_amdgcn_rcpf(pk);  // G[i][K] / G[K][K]
+        g[K] = g[K] * __builtin_amdgcn_rsqf(pk);           // C[i][K]
+        if constexpr (K + 1 < KC) chol_batch<KC, K, K + 1>(g, a);
+        chol_step<KC, K + 1>(g, kc_real, th, fail);
+    }
+}
+
+// Per instance b (one workgroup): G = L1_b^T L1_b + lambda I over all n tokens
+// on MFMA, then its Cholesky factor C in one wavefront (lane-per-row), stored
+// column by column as Ct[b][m][i] = C[i][m] (i > m), Ct[b][m][m] = 1 / C[m][m]
+// and zero above, which is the order the forward substitution of
+// q_apply_kernel reads it in.  The kernel only reads T: Q is formed by a later
+// launch, so no workgroup sees rows another one rewrites.
+//
+// Token chunks of 256 rows are loaded one per thread, written transposed to
+// LDS ([feature][token]) and multiplied there; the next chunk's loads are in
+// flight during the current chunk's MFMAs.
 template <int KC>
-__global__ __launch_bounds__(NT) void cholq_kernel(bf16 *__restrict__ T, int64_t ldt, int64_t off, int64_t n,
-                                                   int kc_real, float lambda, int *__restrict__ flags,
-                                                   double *__restrict__ Cout) {
+__global__ __launch_bounds__(NT) void gram_chol_kernel(const bf16 *__restrict__ T, int64_t ldt, int64_t off,
+                                                       int64_t n, int kc_real, float lambda, float *__restrict__ Ct,
+                                                       int *__restrict__ flags, double *__restrict__ Cout) {
+    static_assert(KC % 16 == 0 && KC <= 64, "correction rank");
     constexpr int GS = 68;        // row stride (floats) of G in LDS
-    constexpr int TT = NT;        // tokens per Gram chunk = tokens per workgroup
+    constexpr int TT = NT;        // tokens per chunk, one per thread
     constexpr int ST = TT + 8;    // row stride (bf16) of the transposed chunk [feature][token]
     constexpr int NBLK = (KC + 31) / 32;
     constexpr int NV = KC / 8;    // 16-byte vectors per token row
-    __shared__ __align__(16) bf16 Lt[64 * ST];
+    __shared__ __align__(16) bf16 Lt[32 * NBLK * ST];
     __shared__ __align__(16) float Gs[64 * GS];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 31, lk = (lane >> 5) * 8;
-    const int64_t b = blockIdx.y;
-    bf16 *const Tb = T + b * n * ldt + off;  // token t of instance b: Tb + t * ldt
-    DYRA_PHASE_MARK(0);
+    const int64_t b = blockIdx.x;
+    const bf16 *const Tb = T + b * n * ldt + off;  // token t of instance b: Tb + t * ldt
 
-    // this thread's token row of L1_b, requested first so that its latency
-    // overlaps the set-up (tokens past n read as zero)
-    const int64_t tbase = (int64_t)blockIdx.x * TT;
-    const int64_t t = tbase + tid;
-    const bool tin = t < n;
-    uint4 lraw[NV];
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        const uint4 x = *reinterpret_cast<const uint4 *>(Tb + (tin ? t * ldt : 0) + 8 * v);
-        lraw[v] = tin ? x : make_uint4(0, 0, 0, 0);
-    }
     // features KC .. 32 NBLK - 1 of the transposed chunk are MFMA padding
     if (KC % 32 != 0) {
         for (int e = tid; e < (32 * NBLK - KC) * ST; e += NT) Lt[KC * ST + e] = bf16(0.f);
     }
-
-    // ---- G = L1_b^T L1_b over all n tokens, 32x32 blocks on MFMA; the
-    // workgroup's own chunk comes from lraw, others (n > TT) are loaded
+    // a chunk's token rows, requested unconditionally (rows past n reread
+    // row n - 1 and are zeroed when staged)
+    auto load = [&](int64_t c0, u32x4 (&v)[NV]) __attribute__((always_inline)) {
+        const int64_t t = c0 + tid < n ? c0 + tid : n - 1;
+#pragma unroll
+        for (int q = 0; q < NV; ++q) v[q] = *reinterpret_cast<const u32x4 *>(Tb + t * ldt + 8 * q);
+    };
     const int wm = wave >> 1, wn = wave & 1;
     const bool gact = wm < NBLK && wn < NBLK;
     f32x16 acc = f32x16{};
     const int64_t nch = (n + TT - 1) / TT;
+    u32x4 v[NV];
+    load(0, v);
     for (int64_t ch = 0; ch < nch; ++ch) {
-        const int64_t c0 = ch * TT;
-        uint4 v[NV];
-        if (c0 == tbase) {
-#pragma unroll
-            for (int q = 0; q < NV; ++q) v[q] = lraw[q];
-        } else {
-            const bool ok = c0 + tid < n;
-#pragma unroll
-            for (int q = 0; q < NV; ++q) {
-                const uint4 x = *reinterpret_cast<const uint4 *>(Tb + (ok ? (c0 + tid) * ldt : 0) + 8 * q);
-                v[q] = ok ? x : make_uint4(0, 0, 0, 0);
-            }
-        }
+        const bool in = ch * TT + tid < n;
         __syncthreads();  // the previous chunk's MFMA reads are done
 #pragma unroll
         for (int q = 0; q < NV; ++q) {
-            union { uint4 u; bf16 e[8]; } w;
+            union { u32x4 u; bf16 e[8]; } w;
             w.u = v[q];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) Lt[(8 * q + e) * ST + tid] = w.e[e];
+            for (int e = 0; e < 8; ++e) Lt[(8 * q + e) * ST + tid] = in ? w.e[e] : bf16(0.f);
         }
         __syncthreads();
+        if (ch + 1 < nch) load((ch + 1) * TT, v);
         if (gact) {
 #pragma unroll 4
             for (int kk = 0; kk < TT; kk += 16)
@@ -146,7 +167,7 @@ __global__ __launch_bounds__(NT) void cholq_kernel(bf16 *__restrict__ T, int64_t
         for (int q = 0; q < 16; ++q) Gs[(wm * 32 + acc_row(lane, q)) * GS + wn * 32 + lr] = acc[q];
     }
     __syncthreads();
-    DYRA_PHASE_MARK(1);
+    if (wave != 0) return;
 
     // ---- lane i holds row i of G + lambda I (identity rows past kc_real)
     const int i = lane;
@@ -169,39 +190,122 @@ __global__ __launch_bounds__(NT) void cholq_kernel(bf16 *__restrict__ T, int64_t
     for (int o = 32; o > 0; o >>= 1) dmax = fmaxf(dmax, __shfl_xor(dmax, o));
     const float th = lambda > 0.f ? 0.f : (float)KC * 1.2e-7f * dmax;
     bool fail = !(dmax > 0.f);
-    float l[KC];
-#pragma unroll
-    for (int q = 0; q < NV; ++q) {
-        union { uint4 u; bf16 e[8]; } w;
-        w.u = lraw[q];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) l[8 * q + e] = (float)w.e[e];
-    }
-    DYRA_PHASE_MARK(2);
+    chol_step<KC, 0>(g, kc_real, th, fail);
 
-    // ---- elimination: step k takes pivot row k (lane k) to all lanes
-    elim_step<KC, 0>(g, l, kc_real, th, fail);
-    DYRA_PHASE_MARK(3);
-
-    // ---- Q_b rows in place of L1_b
-    if (tin) {
+    // ---- C column by column (coalesced over lanes), reciprocal diagonal
+    float *Cb = Ct + b * KC * KC;
+    if (i < KC) {
 #pragma unroll
-        for (int m = 0; m < KC; m += 8) {
-            union { uint4 u; bf16 e[8]; } w;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) w.e[q] = fail ? bf16(0.f) : (bf16)l[m + q];
-            *reinterpret_cast<uint4 *>(Tb + t * ldt + m) = w.u;
+        for (int m = 0; m < KC; ++m) {
+            const float c = m < i ? g[m] : (m == i ? __builtin_amdgcn_rcpf(g[m]) : 0.f);
+            Cb[m * KC + i] = fail ? 0.f : c;
         }
     }
-    if (blockIdx.x == 0 && tid == 0) flags[b] = fail ? 1 : 0;
-    // the Cholesky factor itself (lane i holds row i of C in g[0..i]) for the
-    // L updates of further ALS steps
-    if (Cout && blockIdx.x == 0 && wave == 0 && i < KC) {
+    if (i == 0) flags[b] = fail ? 1 : 0;
+    // the factor itself (lane i holds row i of C in g[0..i]) for the L updates
+    // of further ALS steps
+    if (Cout && i < KC) {
         double *Cr = Cout + ((int64_t)b * KC + i) * KC;
 #pragma unroll
         for (int m = 0; m < KC; ++m) Cr[m] = m <= i ? (double)g[m] : 0.0;
     }
-    DYRA_PHASE_MARK(4);
+}
+
+// Broadcast within groups of G lanes (G = 1, 2 or 4) of lane q of the group,
+// by DPP quad_perm (one VALU instruction, no LDS).  q is a constant once the
+// caller's loop is unrolled, so the switch folds away.
+template <int G> __device__ __forceinline__ float group_bcast(float v, int q) {
+    if constexpr (G == 1) {
+        return v;
+    } else {
+        int ctrl;
+        if constexpr (G == 4) ctrl = q * 0x55;                                          // [q, q, q, q]
+        else ctrl = q | (q << 2) | ((2 + q) << 4) | ((2 + q) << 6);                    // [q, q, 2+q, 2+q]
+        const int iv = __float_as_int(v);
+        int r;
+        switch (ctrl) {
+#define DYRA_DPP(C) case C: r = __builtin_amdgcn_mov_dpp(iv, C, 0xf, 0xf, false); break;
+            DYRA_DPP(0x00) DYRA_DPP(0x55) DYRA_DPP(0xaa) DYRA_DPP(0xff) DYRA_DPP(0xa0) DYRA_DPP(0xf5)
+#undef DYRA_DPP
+        default: r = iv;
+        }
+        return __int_as_float(r);
+    }
+}
+
+// Lanes per token row in q_apply_kernel: each lane's share must be whole
+// 16-byte vectors.
+template <int KC> constexpr int q_lanes() { return KC % 32 == 0 ? 4 : (KC % 16 == 0 ? 2 : 1); }
+
+// Q_b = L1_b C^-T in place.  Each token row is spread over a group of G lanes
+// (G = q_lanes), lane p of the group holding columns [p PW, (p+1) PW).  The
+// forward substitution C q^T = l^T is taken column by column: step K scales
+// q_K by 1 / C[K][K] in the lane that owns it, broadcasts it over the group
+// (DPP), and every lane subtracts q_K C[m][K] from its columns m.  The factor,
+// the same for every token, is staged in LDS once per workgroup with the
+// diagonal and everything above it zero (the reciprocal diagonal kept apart),
+// so the updates need no masking; each 16-byte read is at G addresses per
+// wavefront.  64 G threads per workgroup, one token per group; rows of a
+// failed instance become zero.
+template <int KC>
+__global__ __launch_bounds__(64 * q_lanes<KC>()) void q_apply_kernel(bf16 *__restrict__ T, int64_t ldt, int64_t off,
+                                                                     int64_t n, const float *__restrict__ Ct,
+                                                                     const int *__restrict__ flags) {
+    constexpr int G = q_lanes<KC>();
+    constexpr int PW = KC / G;  // columns per lane
+    constexpr int NTH = 64 * G;
+    static_assert(PW % 8 == 0, "columns per lane");
+    __shared__ __align__(16) float Cs[KC * KC];  // Cs[K][m] = C[m][K] for m > K, else 0
+    __shared__ float rd[KC];                      // 1 / C[K][K]
+    const int tid = threadIdx.x;
+    const int p = tid % G;
+    const int64_t b = blockIdx.y;
+    const int64_t t = (int64_t)blockIdx.x * 64 + tid / G;
+    bf16 *const row = T + (b * n + (t < n ? t : n - 1)) * ldt + off + p * PW;
+    float x[PW];
+#pragma unroll
+    for (int q = 0; q < PW / 8; ++q) {
+        union { u32x4 u; bf16 e[8]; } w;
+        w.u = *reinterpret_cast<const u32x4 *>(row + 8 * q);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[8 * q + e] = (float)w.e[e];
+    }
+    const f32x4 *Cb = reinterpret_cast<const f32x4 *>(Ct + b * KC * KC);
+    for (int e = tid; e < KC * KC / 4; e += NTH) {
+        f32x4 v = Cb[e];
+        const int K = (4 * e) / KC, m0 = (4 * e) % KC;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (m0 + u == K) rd[K] = v[u];
+            if (m0 + u <= K) v[u] = 0.f;
+        }
+        reinterpret_cast<f32x4 *>(Cs)[e] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int K = 0; K < KC; ++K) {
+        const int PK = K / PW, U = K % PW;
+        const float sc = x[U] * rd[K];
+        x[U] = p == PK ? sc : x[U];
+        const float qk = group_bcast<G>(x[U], PK);
+        const float *cr = &Cs[K * KC + p * PW];
+#pragma unroll
+        for (int v0 = 0; v0 < PW; v0 += 4) {
+            const f32x4 c = *reinterpret_cast<const f32x4 *>(cr + v0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[v0 + u] = fmaf(-qk, c[u], x[v0 + u]);
+        }
+    }
+    const bool dead = flags[b] != 0;
+    if (t < n) {
+#pragma unroll
+        for (int q = 0; q < PW / 8; ++q) {
+            union { u32x4 u; bf16 e[8]; } w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w.e[e] = dead ? bf16(0.f) : (bf16)x[8 * q + e];
+            *reinterpret_cast<u32x4 *>(row + 8 * q) = w.u;
+        }
+    }
 }
 
 // ------------------------------------------------------------- float32 path
@@ -591,15 +695,22 @@ __global__ __launch_bounds__(NT) void mprime_tr_kernel(const bf16 *__restrict__ 
 }  // namespace
 
 template <>
-hipError_t launch_gram_q<bf16>(bf16 *T, int64_t ldt, int64_t off, int64_t B, int64_t n, int64_t npad, int kc_real,
-                               int kc, float lambda, bf16 *, int *flags, double *Cout, hipStream_t st) {
+hipError_t launch_gram_q<bf16>(bf16 *T, int64_t ldt, int64_t off, int64_t B, int64_t n, int64_t, int kc_real,
+                               int kc, float lambda, bf16 *, float *Ct, int *flags, double *Cout, hipStream_t st) {
     if (B <= 0) return hipSuccess;
-    const dim3 grid((unsigned)((npad + NT - 1) / NT), (unsigned)B);
+    const dim3 g1((unsigned)B), g2((unsigned)((n + 63) / 64), (unsigned)B);
     switch (kc) {
-    case 16: hipLaunchKernelGGL(cholq_kernel<16>, grid, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda, flags, Cout); break;
-    case 32: hipLaunchKernelGGL(cholq_kernel<32>, grid, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda, flags, Cout); break;
-    case 48: hipLaunchKernelGGL(cholq_kernel<48>, grid, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda, flags, Cout); break;
-    case 64: hipLaunchKernelGGL(cholq_kernel<64>, grid, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda, flags, Cout); break;
+#define DYRA_GQ(KC)                                                                                                  \
+    case KC:                                                                                                         \
+        hipLaunchKernelGGL(gram_chol_kernel<KC>, g1, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda, Ct, flags,     \
+                           Cout);                                                                                    \
+        hipLaunchKernelGGL(q_apply_kernel<KC>, g2, dim3(64 * q_lanes<KC>()), 0, st, T, ldt, off, n, Ct, flags);      \
+        break;
+        DYRA_GQ(16)
+        DYRA_GQ(32)
+        DYRA_GQ(48)
+        DYRA_GQ(64)
+#undef DYRA_GQ
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -607,7 +718,7 @@ hipError_t launch_gram_q<bf16>(bf16 *T, int64_t ldt, int64_t off, int64_t B, int
 
 template <>
 hipError_t launch_gram_q<float>(float *T, int64_t ldt, int64_t off, int64_t B, int64_t n, int64_t npad, int kc_real,
-                                int kc, float lambda, float *Qt, int *flags, double *Cout, hipStream_t st) {
+                                int kc, float lambda, float *Qt, float *, int *flags, double *Cout, hipStream_t st) {
     if (B <= 0) return hipSuccess;
     if (kc < 1 || kc > 64) return hipErrorInvalidValue;
     hipLaunchKernelGGL(gram_q_f32_kernel, dim3((unsigned)B), dim3(NT), 0, st, T, ldt, off, n, npad, kc_real, kc,

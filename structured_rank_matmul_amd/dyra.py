@@ -255,6 +255,15 @@ def alloc_workspace(plan: Plan, B: int, n: int):
     return torch.empty(nbytes, dtype=torch.uint8, device=f"cuda:{plan.device}")
 
 
+def _on_stream(t, stream) -> None:
+    """A tensor allocated here on the current stream but used by work enqueued
+    on another one: tell the caching allocator, so that its memory is not
+    handed out again before that stream's work has finished."""
+    import torch
+    if stream is not None and stream != torch.cuda.current_stream(t.device):
+        t.record_stream(stream)
+
+
 def dyra_forward(X, B: int, n: int, plan: Plan, Y=None, workspace=None, stream=None):
     """Algorithm 1 Inference for B instances of n tokens: X [B*n, c1] -> Y [B*n, c2] (device tensors)."""
     import torch
@@ -264,8 +273,10 @@ def dyra_forward(X, B: int, n: int, plan: Plan, Y=None, workspace=None, stream=N
         raise ValueError(f"X shape {tuple(X.shape)} != ({B * n}, {plan.c1})")
     if Y is None:
         Y = torch.empty((B * n, plan.c2), dtype=X.dtype, device=X.device)
+        _on_stream(Y, stream)
     if workspace is None:
         workspace = alloc_workspace(plan, B, n)
+        _on_stream(workspace, stream)
     st = load().dyra_forward(_dev_ptr(X), int(B), int(n), ctypes.c_void_p(plan.handle), _dev_ptr(Y),
                              _dev_ptr(workspace), workspace.numel() * workspace.element_size(),
                              _stream_ptr(stream))
@@ -285,8 +296,10 @@ def dyra_forward_ex(X, B: int, n: int, plan: Plan, bias=None, alpha: float = 1.0
         raise ValueError(f"bias must be [{plan.c2}] in {X.dtype}")
     if Y is None:
         Y = torch.empty((B * n, plan.c2), dtype=X.dtype, device=X.device)
+        _on_stream(Y, stream)
     if workspace is None:
         workspace = alloc_workspace(plan, B, n)
+        _on_stream(workspace, stream)
     st = load().dyra_forward_ex(_dev_ptr(X), int(B), int(n), ctypes.c_void_p(plan.handle),
                                 _dev_ptr(bias) if bias is not None else None, float(alpha), _dev_ptr(Y),
                                 _dev_ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -341,6 +354,7 @@ def dyra_dense_ref(X, Wt, Y=None, stream=None):
         raise ValueError("Wt must be [c2, c1] in X's dtype")
     if Y is None:
         Y = torch.empty((N, c2), dtype=X.dtype, device=X.device)
+        _on_stream(Y, stream)
     st = load().dyra_dense_ref(_dev_ptr(X), _dev_ptr(Wt), N, c1, c2, _dtype_code(X.dtype), _dev_ptr(Y),
                                _stream_ptr(stream))
     _check(st, "dyra_dense_ref")

@@ -89,3 +89,21 @@ def test_oracle_leg_fills_parity_and_baseline():
     assert abs(parity["t"]["e_dyra_oracle"] - bench.rel_err(y_rows, exact)) < 1e-5
     assert parity["t"]["e_weight_only"] >= parity["t"]["e_dyra_oracle"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0
+
+
+@pytest.mark.parametrize("wname", ["vitl_block", "whisper_mlp", "llama_prefill", "llama_decode_m16"])
+def test_algorithmic_bytes_count_each_layer_array_once(wname):
+    # over the stages of one layer call, the algorithmic bytes are X, Y and
+    # the plan's factors ([A_s | P_L], V_s, W_res), each exactly once; the
+    # intermediates appear only in the operand bytes
+    w = synth.workload(wname)
+    for spec in w.layers:
+        es = 2
+        N = w.B * w.n
+        stages = bench.DUAL_STAGES if bench.dual_form(spec, w.n) else bench.PRIMAL_STAGES
+        by = bench.stage_bytes(spec, w.B, w.n, es)
+        total = sum(by[s] for s in stages)
+        c1, c2, r, k = spec.c1, spec.c2, spec.r, spec.k
+        assert total == es * (N * c1 + N * c2 + (r + k) * c1 + c2 * r + c1 * c2)
+        op = bench.stage_operand_bytes(spec, w.B, w.n, es)
+        assert all(op[s] >= by[s] for s in stages)

@@ -7,7 +7,7 @@ import pytest
 import oracle as orc
 from structured_rank_matmul_amd import dyra, synth
 
-from gpu_util import OWN_ERR_TOL, TOL, own_error_gap, rel, to_device, to_host
+from gpu_util import OWN_ERR_TOL, TOL, check_parity, own_error_gap, rel, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -39,10 +39,10 @@ def test_newton_schulz_matches_oracle(case):
     ref = orc.inference(X.exact, B, n, op, ns_iters=iters)
     chol = orc.inference(X.exact, B, n, op)
     exact = X.exact @ W.astype(np.float64)
-    err, gap = rel(y, ref), own_error_gap(y, ref, exact)
+    err, _, _ = check_parity(y, ref, n, dtype, f"ns {case}")
+    gap = own_error_gap(y, ref, exact)
     print(f"ns case {case}: parity {err:.3e}  own-error gap {gap:.3e}  "
           f"oracle NS vs Cholesky {rel(ref, chol):.2e}", flush=True)
-    assert err <= TOL[dtype]
     assert gap <= OWN_ERR_TOL
     plan.close()
 
@@ -66,8 +66,9 @@ def test_newton_schulz_on_a_vitl_layer_equals_cholesky_path():
     op = orc.offline_preparation(W.astype(np.float64), spec.r, spec.k, 0.0)
     ref = orc.inference(X.exact[rows], len(sample), w.n, op, ns_iters=24)
     print(f"vitl qkv NS 24: parity {rel(y_ns[rows], ref):.3e}  NS vs Cholesky path {rel(y_ns, y_ch):.3e}", flush=True)
-    assert rel(y_ns[rows], ref) <= TOL["bf16"]
-    assert rel(y_ns, y_ch) <= TOL["bf16"]
+    check_parity(y_ns[rows], ref, w.n, "bf16", "vitl qkv NS 24")
+    # the two solves agree on every instance, each on its own
+    check_parity(y_ns, y_ch, w.n, "bf16", "vitl qkv NS 24 vs Cholesky")
     plan_ns.close()
     plan_ch.close()
 
@@ -85,8 +86,11 @@ def test_newton_schulz_zero_instance_is_flagged_and_arguments_checked():
     y = to_host(Y)
     torch.cuda.synchronize()
     assert np.all(y[n:2 * n] == 0)
-    ref = orc.inference(X.exact[:n], 1, n, orc.offline_preparation(W.astype(np.float64), r, k, 0.0), ns_iters=20)
-    assert rel(y[:n], ref) <= TOL["bf16"]
+    # the oracle's iteration is undefined for G = 0 (it divides by ||G||):
+    # the other two instances are held to it, each on its own
+    keep = np.r_[0:n, 2 * n:3 * n]
+    ref = orc.inference(X.exact[keep], 2, n, orc.offline_preparation(W.astype(np.float64), r, k, 0.0), ns_iters=20)
+    check_parity(y[keep], ref, n, "bf16", "ns zero instance")
     plan.close()
     for kw in (dict(ns_iters=65), dict(ns_iters=-1), dict(ns_iters=10, als_half_steps=3)):
         with pytest.raises(dyra.DyraError) as e:

@@ -1,9 +1,11 @@
 """Parity of the HIP path (through the C ABI) with the float64 CPU oracle.
 
 Bar: relative Frobenius error <= 1e-2 (bf16) / 1e-5 (fp32) against the
-oracle's output, and the approximation's own error ||XW - Y||/||XW|| within 1%
-(relative) of the oracle's.  Small shapes span several tiles with ragged
-tails; the workload shapes run at full size.
+oracle's output, for the whole output and for every instance on its own,
+every token row within ROW_MULT times that (gpu_util.check_parity), and the
+approximation's own error ||XW - Y||/||XW|| within 1% (relative) of the
+oracle's.  Small shapes span several tiles with ragged tails; the workload
+shapes run at full size, on every instance or on sampled ones.
 """
 import numpy as np
 import pytest
@@ -11,7 +13,7 @@ import pytest
 import oracle as orc
 from structured_rank_matmul_amd import dyra, synth
 
-from gpu_util import OWN_ERR_TOL, TOL, own_error_gap, rel, to_device, to_host, weight_to_device
+from gpu_util import OWN_ERR_TOL, TOL, check_parity, own_error_gap, rel, to_device, to_host, weight_to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -34,8 +36,7 @@ def run_case(W, X, B, n, r, k, lam, dtype, check_own=True):
     y = to_host(Y)
     op = oracle_plan(W, r, k, lam)
     ref = orc.inference(X.exact, B, n, op)
-    err = rel(y, ref)
-    assert err <= TOL[dtype], f"parity {err:.3e} > {TOL[dtype]}"
+    err, _, _ = check_parity(y, ref, n, dtype, f"B={B} n={n} r={r} k={k} lambda={lam} {dtype}")
     if check_own:
         exact = X.exact @ W.astype(np.float64)
         gap = own_error_gap(y, ref, exact)
@@ -56,7 +57,7 @@ def test_dense_ref_matches_exact(dtype, N, c1, c2):
     Y = dyra.dyra_dense_ref(to_device(X), Wt)
     torch.cuda.synchronize()
     ref = X.exact @ W_exact
-    assert rel(to_host(Y), ref) <= TOL[dtype]
+    check_parity(to_host(Y), ref, N, dtype, f"dense {N}x{c1}x{c2}")
     # agrees with the vendor GEMM to output rounding
     Yt = to_device(X).float() @ Wt.float().T
     assert rel(to_host(Y), to_host(Yt)) <= (5e-3 if dtype == "bf16" else 1e-6)
@@ -173,8 +174,8 @@ def test_failed_solve_is_flagged():
     assert dyra.dyra_forward_status(plan, B, n, ws) == 2
     y = to_host(Y)
     assert np.all(y[n:2 * n] == 0) and np.all(y[3 * n:] == 0)
-    ref = orc.inference(X.exact[:n], 1, n, oracle_plan(W, r, k, 0.0))
-    assert rel(y[:n], ref) <= TOL["bf16"]
+    ref = orc.inference(X.exact, B, n, oracle_plan(W, r, k, 0.0))
+    check_parity(y, ref, n, "bf16", "zero instances")
     torch.cuda.synchronize()
 
 
@@ -207,13 +208,13 @@ def _workload_case(wname, lname, sample=None):
     rows = np.concatenate([np.arange(b * w.n, (b + 1) * w.n) for b in idx])
     Xs = X.exact[rows]
     ref = orc.inference(Xs, len(idx), w.n, op)
-    err = rel(y[rows], ref)
+    err, worst_inst, worst_row = check_parity(y[rows], ref, w.n, w.dtype, f"{wname}/{lname}")
     exact = Xs @ W.astype(np.float64)
     gap = own_error_gap(y[rows], ref, exact)
     e_w = rel(orc.weight_only(Xs, op), exact)
-    print(f"{wname}/{lname}: parity {err:.3e}  own-error gap {gap:.3e}  "
-          f"e_dyra {rel(ref, exact):.4f}  e_weight_only {e_w:.4f}", flush=True)
-    assert err <= TOL[w.dtype]
+    print(f"{wname}/{lname}: parity {err:.3e} (worst instance {worst_inst:.3e}, worst row {worst_row:.3e}) over "
+          f"{len(idx)} instances  own-error gap {gap:.3e}  e_dyra {rel(ref, exact):.4f}  e_weight_only {e_w:.4f}",
+          flush=True)
     assert gap <= OWN_ERR_TOL
     plan.close()
 
@@ -233,4 +234,16 @@ def test_workload_vitl_block(layer):
 
 @pytest.mark.parametrize("layer", ["fc1", "fc2"])
 def test_workload_whisper_mlp(layer):
-    _workload_case("whisper_mlp", layer, sample=[0, 7, 15])
+    """Every instance: each spans six 256-token blocks."""
+    _workload_case("whisper_mlp", layer)
+
+
+def test_many_long_instances():
+    """96 instances of 2048 tokens: the per-instance statistics span eight
+    256-token blocks per instance and the launches far more workgroups than
+    are resident at once, so an instance's Gram matrix must be complete before
+    any of its rows is rewritten.  Every instance is checked on its own."""
+    B, n, c1, c2, r, k = 96, 2048, 512, 512, 128, 64
+    W = synth.random_weight(c1, c2, 71, p=0.6)
+    X = synth.random_matrix(B * n, c1, 72, "bf16")
+    run_case(W, X, B, n, r, k, 0.0, "bf16")

@@ -8,7 +8,7 @@ import pytest
 import oracle as orc
 from structured_rank_matmul_amd import costs, dyra, synth
 
-from gpu_util import OWN_ERR_TOL, TOL, own_error_gap, rel, to_device, to_host
+from gpu_util import OWN_ERR_TOL, check_parity, own_error_gap, rel, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -33,9 +33,9 @@ def test_flops_matched_static_matches_oracle(wname, lname, sample):
     ref = orc.weight_only(Xs, op)
     y = to_host(Y)[rows]
     exact = Xs @ W.astype(np.float64)
-    err, gap = rel(y, ref), own_error_gap(y, ref, exact)
+    err, _, _ = check_parity(y, ref, w.n, w.dtype, f"{wname}/{lname} static rank {s}")
+    gap = own_error_gap(y, ref, exact)
     print(f"{wname}/{lname}: FLOPs-matched static rank {s}: parity {err:.3e}  own-error gap {gap:.3e}  "
           f"e_static {rel(ref, exact):.4f}", flush=True)
-    assert err <= TOL[w.dtype]
     assert gap <= OWN_ERR_TOL
     plan.close()

@@ -12,7 +12,7 @@ import pytest
 import oracle as orc
 from structured_rank_matmul_amd import dyra, synth
 
-from gpu_util import TOL, rel, to_device, to_host
+from gpu_util import check_parity, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -37,8 +37,8 @@ def test_forward_is_repeatable_and_stream_safe():
     # both inputs meet the oracle bar, so the comparison below is against
     # correct results
     op = orc.offline_preparation(W.astype(np.float64), R, K, 0.0)
-    assert rel(to_host(ya0), orc.inference(Xa.exact, B, N_TOK, op)) <= TOL["bf16"]
-    assert rel(to_host(yb0), orc.inference(Xb.exact, B, N_TOK, op)) <= TOL["bf16"]
+    check_parity(to_host(ya0), orc.inference(Xa.exact, B, N_TOK, op), N_TOK, "bf16", "stream a")
+    check_parity(to_host(yb0), orc.inference(Xb.exact, B, N_TOK, op), N_TOK, "bf16", "stream b")
 
     # two default-priority streams, separate workspaces and outputs, several
     # forwards each in flight at once
@@ -54,4 +54,15 @@ def test_forward_is_repeatable_and_stream_safe():
     torch.cuda.synchronize()
     assert torch.equal(ya, ya0)
     assert torch.equal(yb, yb0)
+
+    # a side stream with the output and workspace allocated by the binding:
+    # they are marked as used on that stream, so the allocator does not hand
+    # their memory to the next allocation before the stream is done with it
+    s1.wait_stream(cur)
+    outs = [dyra.dyra_forward(xa, B, N_TOK, plan, stream=s1) for _ in range(3)]
+    filler = [torch.full_like(ya0, 7.0) for _ in range(3)]  # allocations on the current stream meanwhile
+    torch.cuda.synchronize()
+    for y in outs:
+        assert torch.equal(y, ya0)
+    del filler
     plan.close()

@@ -521,3 +521,19 @@ def test_newton_schulz_converges_to_the_cholesky_solution():
     G = L1.T @ L1
     lam, V = np.linalg.eigh(G)
     np.testing.assert_allclose(orc.newton_schulz_inv_sqrt(G, 40), (V / np.sqrt(lam)) @ V.T, rtol=1e-9, atol=1e-12)
+
+
+def test_rel_fro_hand_values():
+    """The metric's relative Frobenius error, ||A - B||_F / ||B||_F, against
+    values worked by hand: the reference is the second argument (swapping the
+    two changes the value), the norm runs over every entry of the matrix (not a
+    row or column), and it is a ratio of norms, not of squared norms."""
+    A = np.array([[3.0, 4.0], [0.0, 1.0]])
+    B = np.array([[3.0, 4.0], [0.0, 0.0]])
+    assert orc.rel_fro(A, B) == pytest.approx(1.0 / 5.0, rel=1e-15)          # ||(0,0,0,1)|| / ||(3,4,0,0)||
+    assert orc.rel_fro(B, A) == pytest.approx(1.0 / np.sqrt(26.0), rel=1e-15)
+    C = np.array([[1.0, 2.0], [2.0, 4.0]])
+    D = np.array([[1.0, 0.0], [0.0, 2.0]])
+    # ||(0,2,2,2)|| / ||(1,0,0,2)|| = sqrt(12) / sqrt(5)
+    assert orc.rel_fro(C, D) == pytest.approx(np.sqrt(12.0 / 5.0), rel=1e-15)
+    assert orc.rel_fro(D, D) == 0.0
