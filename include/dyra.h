@@ -43,7 +43,8 @@ typedef enum {
     DYRA_ERR_HIP = 6,        /* a HIP runtime call or kernel launch failed */
     DYRA_ERR_NOMEM = 7,      /* host or device allocation failed */
     DYRA_ERR_WORKSPACE = 8,  /* workspace missing or smaller than dyra_workspace_bytes() */
-    DYRA_ERR_NODEVICE = 9    /* no HIP device, or the plan lives on another device */
+    DYRA_ERR_NODEVICE = 9,   /* no HIP device, or the plan lives on another device */
+    DYRA_ERR_SCRATCH = 10    /* dyra_forward_noalloc: the call needs more than its built-in scratch */
 } dyra_status;
 
 typedef enum {
@@ -237,6 +238,29 @@ dyra_status dyra_forward(const void *X, int64_t B, int64_t n, const dyra_plan *p
  */
 dyra_status dyra_forward_ex(const void *X, int64_t B, int64_t n, const dyra_plan *plan, const void *bias,
                             float alpha, void *Y, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * dyra_forward for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and result as dyra_forward, with the
+ * workspace taken from a scratch array built into the library, one per GPU,
+ * of dyra_noalloc_scratch_bytes() (128 MiB) and held until the process ends.
+ * No allocation or free of any kind is made.
+ *
+ * X, Y, plan, stream, B, n as for dyra_forward.  Returns DYRA_ERR_SCRATCH when
+ * dyra_workspace_bytes(plan, B, n) exceeds the scratch (nothing is enqueued),
+ * DYRA_ERR_NODEVICE if no plan was prepared on the plan's device in this
+ * process.  Every call on one GPU shares that GPU's scratch: calls that
+ * overlap in time on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  The scratch keeps the last call's contents; no
+ * kernel reads it before writing it.  dyra_forward_status does not see this
+ * call's failure flags.
+ */
+dyra_status dyra_forward_noalloc(const void *X, int64_t B, int64_t n, const dyra_plan *plan, void *Y,
+                                 void *stream);
+
+/* Size in bytes of dyra_forward_noalloc's per-GPU scratch. */
+size_t dyra_noalloc_scratch_bytes(void);
 
 /*
  * Number of instances whose SPD solve broke down in the last

@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -37,9 +38,37 @@ struct dyra_plan {
     void *Smix;       // float32 [nb][nb][rbp]: the couplings s_ij
 };
 
+// Device-side scratch of dyra_forward_noalloc: one copy per GPU, held until
+// the process ends.  In host code this name is only a stand-in for the symbol;
+// the device address comes from hipGetSymbolAddress (scratch_ptr below).
+constexpr size_t kNoallocScratchBytes = size_t{128} << 20;
+__device__ __align__(256) static char scratch[kNoallocScratchBytes];
+
 namespace {
 
 using dyra::bf16;
+
+// Per-device address of `scratch`, looked up once per device with that device
+// current (each GPU holds its own copy of the array at its own address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+dyra_status scratch_setup(int device) {
+    if (device < 0 || device >= kMaxDevices) return DYRA_ERR_NODEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[device]) return DYRA_OK;
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return DYRA_ERR_HIP;
+    g_scratch_ptr[device] = ptr;
+    return DYRA_OK;
+}
+
+void *scratch_ptr(int device) {
+    if (device < 0 || device >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    return g_scratch_ptr[device];
+}
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxCorrection = 64;
@@ -173,7 +202,9 @@ dyra_status hip_status(hipError_t e) { return e == hipSuccess ? DYRA_OK : DYRA_E
 
 // The kernels' one-time host set-up on the current device, done while
 // preparing a plan so that forward calls only enqueue work.
-dyra_status prepare_launches(dyra_dtype dtype) {
+dyra_status prepare_launches(dyra_dtype dtype, int device) {
+    const dyra_status s = scratch_setup(device);
+    if (s != DYRA_OK) return s;
     if (dtype == DYRA_BF16)
         return hip_status(dyra::gemm_prepare<bf16>()) == DYRA_OK ? hip_status(dyra::blast_prepare<bf16>())
                                                                  : DYRA_ERR_HIP;
@@ -400,6 +431,7 @@ const char *dyra_status_str(dyra_status s) {
     case DYRA_ERR_NOMEM: return "out of memory";
     case DYRA_ERR_WORKSPACE: return "workspace missing or too small";
     case DYRA_ERR_NODEVICE: return "no device or wrong device";
+    case DYRA_ERR_SCRATCH: return "call needs more than the built-in scratch of dyra_forward_noalloc";
     }
     return "unknown status";
 }
@@ -466,7 +498,7 @@ dyra_status dyra_prepare_ex(const float *W, int64_t c1, int64_t c2, int32_t r, i
     if ((s = upload(A, &p->Aext)) == DYRA_OK && (s = upload(V, &p->Vs)) == DYRA_OK)
         s = upload(Rt, &p->Wres_t);
     if (s == DYRA_OK && p->half_steps > 2) s = upload(f.W_res, &p->Wres);
-    if (s == DYRA_OK) s = prepare_launches(dtype);
+    if (s == DYRA_OK) s = prepare_launches(dtype, device);
     if (prev >= 0) (void)hipSetDevice(prev);
     if (s != DYRA_OK) {
         dyra_plan_destroy(p);
@@ -543,7 +575,7 @@ dyra_status dyra_prepare_blast(const float *W, int64_t c1, int64_t c2, int32_t n
         else if (hipMemcpy(p->Smix, Sm.data(), Sm.size() * sizeof(float), hipMemcpyHostToDevice) != hipSuccess)
             s = DYRA_ERR_HIP;
     }
-    if (s == DYRA_OK) s = prepare_launches(dtype);
+    if (s == DYRA_OK) s = prepare_launches(dtype, device);
     if (prev >= 0) (void)hipSetDevice(prev);
     if (s != DYRA_OK) {
         dyra_plan_destroy(p);
@@ -603,6 +635,20 @@ dyra_status dyra_forward_timed(const void *X, int64_t B, int64_t n, const dyra_p
     return forward_impl(X, B, n, plan, nullptr, 1.f, Y, workspace, workspace_bytes, stream, events, n_events,
                         n_recorded);
 }
+
+dyra_status dyra_forward_noalloc(const void *X, int64_t B, int64_t n, const dyra_plan *plan, void *Y,
+                                 void *stream) {
+    if (!plan) return DYRA_ERR_ARG;
+    if (B < 0 || n < 1) return DYRA_ERR_SHAPE;
+    if (B == 0) return DYRA_OK;
+    const size_t need = dyra_workspace_bytes(plan, B, n);
+    if (need > kNoallocScratchBytes) return DYRA_ERR_SCRATCH;
+    void *ws = scratch_ptr(plan->device);
+    if (!ws) return DYRA_ERR_NODEVICE;
+    return forward_impl(X, B, n, plan, nullptr, 1.f, Y, ws, kNoallocScratchBytes, stream, nullptr, 0, nullptr);
+}
+
+size_t dyra_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
 
 const char *dyra_stage_name(const dyra_plan *plan, int64_t n, int32_t i) {
     if (!plan || n < 1 || i < 0) return nullptr;

@@ -27,6 +27,7 @@ EXPORTED = (
     "dyra_plan_info",
     "dyra_workspace_bytes", "dyra_forward", "dyra_forward_ex", "dyra_forward_status", "dyra_dense_ref",
     "dyra_forward_timed", "dyra_stage_name", "dyra_prepare_blast", "dyra_factorize_blast_host",
+    "dyra_forward_noalloc", "dyra_noalloc_scratch_bytes",
 )
 
 
@@ -82,6 +83,10 @@ def load() -> ctypes.CDLL:
     L.dyra_forward_timed.argtypes = [vp, i64, i64, vp, vp, vp, ctypes.c_size_t, vp, ctypes.POINTER(vp), i32,
                                      ctypes.POINTER(i32)]
     L.dyra_forward_timed.restype = ctypes.c_int
+    L.dyra_forward_noalloc.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.dyra_forward_noalloc.restype = ctypes.c_int
+    L.dyra_noalloc_scratch_bytes.argtypes = []
+    L.dyra_noalloc_scratch_bytes.restype = ctypes.c_size_t
     L.dyra_stage_name.argtypes = [vp, i64, i32]
     L.dyra_stage_name.restype = ctypes.c_char_p
     _lib = L
@@ -306,6 +311,24 @@ def dyra_forward_ex(X, B: int, n: int, plan: Plan, bias=None, alpha: float = 1.0
                                 _stream_ptr(stream))
     _check(st, "dyra_forward_ex")
     return Y
+
+
+def dyra_forward_noalloc(X, B: int, n: int, plan: Plan, Y, stream=None):
+    """dyra_forward with the library's built-in per-GPU scratch as workspace
+    (the caller passes X and Y; nothing is allocated).  Calls overlapping on
+    one GPU race on that scratch."""
+    if X.dtype != plan.torch_dtype or Y.dtype != plan.torch_dtype:
+        raise ValueError(f"X and Y must be {plan.torch_dtype}")
+    if tuple(X.shape) != (B * n, plan.c1) or tuple(Y.shape) != (B * n, plan.c2):
+        raise ValueError(f"X must be ({B * n}, {plan.c1}) and Y ({B * n}, {plan.c2})")
+    st = load().dyra_forward_noalloc(_dev_ptr(X), int(B), int(n), ctypes.c_void_p(plan.handle), _dev_ptr(Y),
+                                     _stream_ptr(stream))
+    _check(st, "dyra_forward_noalloc")
+    return Y
+
+
+def dyra_noalloc_scratch_bytes() -> int:
+    return int(load().dyra_noalloc_scratch_bytes())
 
 
 def dyra_forward_status(plan: Plan, B: int, n: int, workspace, stream=None) -> int:

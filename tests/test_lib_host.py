@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(0, 10):
+    for s in range(0, 11):
         assert dyra.status_str(s) not in ("", "unknown status")
     assert dyra.status_str(1234) == "unknown status"
 
@@ -74,6 +74,9 @@ def test_forward_and_dense_ref_reject_bad_arguments():
     fails = ctypes.c_int32()
     assert L.dyra_forward_status(None, 1, 1, 16, None, ctypes.byref(fails)) == 1
     assert L.dyra_stage_name(None, 1, 0) is None
+    # the allocation-free forward: null plan, bad shape; its scratch size
+    assert L.dyra_forward_noalloc(16, 1, 4, None, 16, None) == 1
+    assert L.dyra_noalloc_scratch_bytes() == 128 << 20
 
 
 def test_factorize_rejects_non_finite_weight():
