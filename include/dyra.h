@@ -90,7 +90,8 @@ dyra_status dyra_factorize_host(const float *W, int64_t c1, int64_t c2, int32_t 
  *
  * W, c1, c2, r, k, lambda as for dyra_factorize_host.  c1 and c2 must be
  * multiples of 32 (DYRA_ERR_SHAPE otherwise).  r and k may be any values with
- * r + k <= min(c1, c2); k = 0 gives the weight-only product X A_s V_s^T, and
+ * r + k <= min(c1, c2) and k <= 256 (k <= 64 for DYRA_F32; DYRA_ERR_SHAPE
+ * otherwise); k = 0 gives the weight-only product X A_s V_s^T, and
  * r = min(c1, c2), k = 0 the exact product up to rounding.
  * On success *plan_out owns device memory until dyra_plan_destroy.
  */
@@ -122,9 +123,10 @@ dyra_status dyra_prepare(const float *W, int64_t c1, int64_t c2, int32_t r, int3
  *                 gets no correction.  The dual form does not use it.
  *
  * A plan with als_half_steps > 2 also holds W_res untransposed ([c1][c2]) and
- * needs a larger workspace; dyra_forward runs the extra steps for instances of
- * n > 16 tokens with n >= k and returns DYRA_ERR_SHAPE for the dual form
- * (n <= 16 or n < k), which carries one ALS step only.
+ * needs a larger workspace; dyra_forward runs the extra steps for instances
+ * on the primal path (n > 16 tokens with n >= k, or n < k with lambda > 0) and
+ * returns DYRA_ERR_SHAPE for the dual form, which carries one ALS step only.
+ * als_half_steps > 2 and ns_iters > 0 take k <= 64 (DYRA_ERR_SHAPE above).
  */
 dyra_status dyra_prepare_ex(const float *W, int64_t c1, int64_t c2, int32_t r, int32_t k, float lambda,
                             dyra_dtype dtype, int device, const float *R0, int32_t als_half_steps,
@@ -157,7 +159,8 @@ dyra_status dyra_factorize_blast_host(const float *W, int64_t c1, int64_t c2, in
  * nb  1..4 blocks per side; c1 and c2 multiples of 32 * nb.
  * rb  BLAST rank >= 1; padded to 32 it must fit 256 16-byte chunks (rb <= 2048
  *     for bf16, 1024 for float32).
- * k   correction rank 0..64, k <= min(c1, c2); lambda >= 0 and finite.
+ * k   correction rank 0..256 (0..64 for DYRA_F32), k <= min(c1, c2); lambda >= 0
+ *     and finite.
  *
  * W_res = W - W_hat, R0 = the top-k right singular vectors of W_res
  * (Appendix D) and P_L (Eq. 7) are formed on the host in float64.  The
@@ -204,11 +207,15 @@ size_t dyra_workspace_bytes(const dyra_plan *plan, int64_t B, int64_t n);
  * All pointers 16-byte aligned.  B >= 0, n >= 1 (B = 0 is a no-op).
  *
  * Asynchronous: enqueues kernels on `stream` and returns; no allocation, no
- * host synchronisation.  For n > 16 and n >= k the per-instance right factor
- * comes from a Cholesky factorisation of L1^T L1 + lambda I (§2.4); for
- * n <= 16 or n < k the same product L1 R1 is formed in its n x n dual
- * (push-through) form L1 L1^T (L1 L1^T + lambda I_n)^-1 X W_res, which is also
- * defined at lambda = 0 and better conditioned when n is close to k.  A
+ * host synchronisation.  For n > 16 and n >= k (or n < k with lambda > 0) the
+ * per-instance right factor comes from a Cholesky factorisation of
+ * L1^T L1 + lambda I (§2.4); for n <= 16, and for 16 < n < k with lambda = 0,
+ * the same product L1 R1 is formed in its n x n dual (push-through) form
+ * L1 L1^T (L1 L1^T + lambda I_n)^-1 X W_res, which is also defined at
+ * lambda = 0 (the projector onto the range of L1, by an eigen-decomposition
+ * for n <= 16 and a Cholesky factorisation with diagonal pivoting for
+ * 16 < n <= 64) and better conditioned when n is close to k.  lambda = 0 with
+ * 64 < n < k returns DYRA_ERR_SHAPE.  A
  * Cholesky pivot at or below the working precision (lambda = 0 with a
  * numerically rank-deficient L1) sets that instance's failure flag, read back
  * by dyra_forward_status(); its rows then hold the static product X A_s V_s^T

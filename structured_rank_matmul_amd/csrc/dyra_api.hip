@@ -71,8 +71,12 @@ void *scratch_ptr(int device) {
 }
 
 constexpr size_t kAlign = 256;
-constexpr int kMaxCorrection = 64;
-constexpr int kMaxDualTokens = 16;
+constexpr int kMaxCorrection = 256;
+// The float32 path's SPD solve, further ALS steps and the Newton-Schulz solve
+// are built for correction ranks up to 64.
+constexpr int kMaxCorrectionSmall = 64;
+constexpr int kMaxDualTokens = 16;       // every instance this short takes the dual form
+constexpr int kMaxWideDualTokens = 64;   // the dual form for n < k at lambda = 0
 constexpr int kMaxHalfSteps = 8;
 constexpr int kMaxNsIters = 64;
 constexpr int kMaxBlastBlocks = 4;
@@ -101,14 +105,19 @@ uint16_t bf16_bits(double x) {
 
 enum class Path { Primal, Dual, Static };
 
-// Instances with at most kMaxDualTokens tokens (and any with fewer tokens than
-// the correction rank) take the n x n dual form: its eigen-decomposition stays
-// accurate where the k x k normal equations of the primal form would be
-// ill-conditioned (n close to k).
+// Instances with at most kMaxDualTokens tokens take the n x n dual form: its
+// eigen-decomposition stays accurate where the k x k normal equations of the
+// primal form would be ill-conditioned (n close to k).  Longer instances with
+// fewer tokens than the correction rank take the primal form when lambda > 0
+// (the ridge keeps L1^T L1 + lambda I positive definite) and the dual form,
+// with a rank-revealing factorisation, at lambda = 0 (up to
+// kMaxWideDualTokens tokens).
 Path path_for(const dyra_plan *p, int64_t n) {
     if (p->kc == 0) return Path::Static;
     if (p->nb > 0) return Path::Primal;  // BLAST plans have no dual form
-    return (n < p->k || n <= kMaxDualTokens) ? Path::Dual : Path::Primal;
+    if (n <= kMaxDualTokens) return Path::Dual;
+    if (n < p->k) return p->lambda > 0.f ? Path::Primal : Path::Dual;
+    return Path::Primal;
 }
 
 // Workspace of one forward call (offsets in bytes, each 256-byte aligned):
@@ -117,6 +126,8 @@ Path path_for(const dyra_plan *p, int64_t n) {
 //   Qt     [B][kc][npad]         Q_b^T, token-contiguous, npad = n rounded up to 32
 //                                (float32 only; bf16 reads Q_b from T)
 //   Ct     float32 [B][kc][kc]   Cholesky factor of G_b by columns (bf16 only)
+//   Gw     float32 [B][kp][kp]   G_b while it is factored, kp = kc rounded up to 32
+//                                (bf16 with kc above 128 only; smaller G stay in LDS)
 //   Mp     [B * kc][c1]          M'_b = Q_b^T X_b stacked over instances
 //   R1t    [B][c2][kc]           R1_b transposed
 //   with further ALS steps (half_steps > 2, als.hip):
@@ -129,7 +140,7 @@ Path path_for(const dyra_plan *p, int64_t n) {
 //   F      float32 [B][kc][kc]   G^-1/2 per instance
 //   dual   decode workspace      (n <= 16 or n < k only)
 struct Layout {
-    size_t flags, T, Qt, Ct, Mp, R1t, C, R1row, Sp, H, Kp, F, dual, total;
+    size_t flags, T, Qt, Ct, Gw, Mp, R1t, C, R1row, Sp, H, Kp, F, dual, total;
     int64_t npad;
 };
 
@@ -150,6 +161,9 @@ Layout workspace_layout(const dyra_plan *p, int64_t B, int64_t n) {
         if (p->dtype == DYRA_F32) off += align_up(es * B * p->kc * L.npad);
         L.Ct = off;
         if (p->dtype == DYRA_BF16 && p->ns_iters == 0) off += align_up(sizeof(float) * (size_t)B * p->kc * p->kc);
+        L.Gw = off;
+        if (p->dtype == DYRA_BF16 && p->ns_iters == 0)
+            off += align_up(sizeof(float) * (size_t)B * dyra::gram_workspace_floats(p->kc));
         L.Mp = off;
         off += align_up(es * B * p->kc * p->c1);
         L.R1t = off;
@@ -315,7 +329,8 @@ dyra_status run_forward(const E *X, int64_t B, int64_t n, const dyra_plan *p, co
                         return t;
                 } else {
                     if ((t = hip_status(dyra::launch_gram_q<E>(T, ldt, p->kw, B, n, L.npad, p->k, p->kc, p->lambda,
-                                                               Qt, (float *)(ws + L.Ct), flags, Cf, st))) != DYRA_OK)
+                                                               Qt, (float *)(ws + L.Ct), (float *)(ws + L.Gw), flags,
+                                                               Cf, st))) != DYRA_OK)
                         return t;
                     if ((t = mark()) != DYRA_OK) return t;
                 }
@@ -396,7 +411,7 @@ dyra_status forward_impl(const void *X, int64_t B, int64_t n, const dyra_plan *p
     if (!aligned16(X) || !aligned16(Y)) return DYRA_ERR_ALIGN;
     if (B > INT32_MAX / std::max<int64_t>(n, 1)) return DYRA_ERR_SHAPE;
     const Path path = path_for(p, n);
-    if (path == Path::Dual && n > kMaxDualTokens) return DYRA_ERR_SHAPE;  // n < k with k > 16 tokens
+    if (path == Path::Dual && n > kMaxWideDualTokens) return DYRA_ERR_SHAPE;  // n < k, lambda = 0, n > 64
     if (path == Path::Dual && p->half_steps > 2) return DYRA_ERR_SHAPE;   // one ALS step only in the dual form
     // BLAST plans solve the k x k system in every case: it is singular for
     // fewer tokens than k without a ridge term
@@ -455,6 +470,7 @@ dyra_status dyra_prepare_ex(const float *W, int64_t c1, int64_t c2, int32_t r, i
     if (!(lambda >= 0.f) || !std::isfinite(lambda)) return DYRA_ERR_ARG;
     if (c1 % 32 != 0 || c2 % 32 != 0) return DYRA_ERR_SHAPE;
     if (k > kMaxCorrection) return DYRA_ERR_SHAPE;
+    if (k > kMaxCorrectionSmall && (dtype == DYRA_F32 || als_half_steps > 2 || ns_iters > 0)) return DYRA_ERR_SHAPE;
     const int32_t kw = r > 0 ? (int32_t)round_up(r, 32) : 0;
     const int32_t kc = k > 0 ? (int32_t)round_up(k, 16) : 0;
     int ndev = 0;
@@ -520,6 +536,7 @@ dyra_status dyra_prepare_blast(const float *W, int64_t c1, int64_t c2, int32_t n
     if (nb > kMaxBlastBlocks) return DYRA_ERR_SHAPE;
     if (c1 % (32 * (int64_t)nb) != 0 || c2 % (32 * (int64_t)nb) != 0) return DYRA_ERR_SHAPE;
     if (k > kMaxCorrection) return DYRA_ERR_SHAPE;
+    if (k > kMaxCorrectionSmall && dtype == DYRA_F32) return DYRA_ERR_SHAPE;
     const int32_t rbp = (int32_t)round_up(rb, 32);
     if ((int64_t)rbp * (int64_t)elem_size(dtype) > 16 * 256) return DYRA_ERR_SHAPE;  // the mix kernel's row chunks
     const int32_t kc = k > 0 ? (int32_t)round_up(k, 16) : 0;

@@ -20,7 +20,7 @@ constexpr int NT = 256;
 constexpr int kRowBlock = 64;  // rows (tokens) per workgroup, two 32-row MFMA blocks
 
 constexpr int kMaxSplits = 4;  // split-K parts of the projection (16 measured slower overall)
-constexpr int kMaxCorr = 64;    // largest padded correction rank
+constexpr int kMaxCorr = 256;   // largest padded correction rank
 
 int decode_splits(int64_t c1) {
     int s = 1;
@@ -178,11 +178,12 @@ __global__ __launch_bounds__(NT) void decode_coef_kernel(const float *__restrict
     __syncthreads();
     const int nn = (int)n;
     // one Gram element per wavefront at a time: lanes over the correction
-    // columns (k_real <= 64), then a butterfly sum
+    // columns (k_real <= 256, in passes of 64), then a butterfly sum
     const int lane = tid & 63, wave = tid >> 6;
     for (int e = wave; e < nn * nn; e += NT / 64) {
         const int i = e / nn, j = e - (e / nn) * nn;
-        double s = lane < k_real ? (double)Ls[i][lane] * (double)Ls[j][lane] : 0.0;
+        double s = 0.0;
+        for (int c = lane; c < k_real; c += 64) s += (double)Ls[i][c] * (double)Ls[j][c];
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
         if (lane == 0) K[i][j] = s;
@@ -241,6 +242,148 @@ __global__ __launch_bounds__(NT) void decode_coef_kernel(const float *__restrict
             }
         flags[b] = 0;
     }
+}
+
+// One workgroup per instance for 16 < n <= 64 tokens with lambda = 0 (fewer
+// tokens than the correction rank): T rows = sum of the split partials, and
+// C_b = the orthogonal projector onto range(L1_b), the lambda -> 0 limit of
+// L1 L1^T (L1 L1^T + lambda I)^-1.  K = L1_b L1_b^T is formed in float64 from
+// the float32 L1 values and factored by a Cholesky with diagonal pivoting,
+// which stops at the first remaining diagonal at or below n * 1e-12 times the
+// largest diagonal of K: the factor's columns then span range(K) = range(L1_b)
+// and their count is its numerical rank.  Full rank (the generic case, L1_b
+// has independent rows) gives C_b = I exactly; a deficient rank gives
+// C_b = F (F^T F)^-1 F^T for the factor's columns F (Gauss-Jordan inverse of
+// the small SPD F^T F, float64).
+constexpr int kWideTokens = 64;
+
+template <typename E>
+__global__ __launch_bounds__(NT) void decode_coef_wide_kernel(const float *__restrict__ partial, int64_t N,
+                                                              int64_t n, int K1, int kw, int k_real, int splits,
+                                                              float *__restrict__ T, float *__restrict__ coef,
+                                                              int *__restrict__ flags) {
+    constexpr int KS = kMaxCorr + 1;
+    constexpr int MS = kWideTokens + 1;
+    // the L1 rows (float32) while K is formed, afterwards the product W = F M^-1
+    __shared__ __align__(16) char buf[kWideTokens * KS * sizeof(float)];
+    __shared__ double Km[kWideTokens][MS];  // K, then F^T F and its inverse
+    __shared__ double Fm[kWideTokens][MS];  // pivoted factor, one column per accepted step
+    __shared__ int done[kWideTokens];
+    __shared__ int sh_p, sh_rank;
+    __shared__ double sh_d, sh_tol;
+    float(*Ls)[KS] = reinterpret_cast<float(*)[KS]>(buf);
+    double(*Wm)[MS] = reinterpret_cast<double(*)[MS]>(buf);
+    const int tid = threadIdx.x;
+    const int64_t b = blockIdx.x;
+    const int64_t r0 = b * n;
+    const int nn = (int)n;
+    // ---- T rows and L1 (split partials summed)
+    const int64_t total = n * K1;
+    for (int64_t e = tid; e < total; e += NT) {
+        const int64_t i = e / K1, c = e - i * K1;
+        float s = 0.f;
+        for (int q = 0; q < splits; ++q) s += partial[((int64_t)q * N + r0 + i) * K1 + c];
+        T[(r0 + i) * K1 + c] = s;
+        if (c >= kw) Ls[i][c - kw] = s;
+    }
+    if (tid < kWideTokens) done[tid] = 0;
+    __syncthreads();
+    // ---- K = L1 L1^T, float64 (lower triangle computed, mirrored)
+    for (int e = tid; e < nn * nn; e += NT) {
+        const int i = e / nn, j = e - i * nn;
+        if (j > i) continue;
+        double s = 0.0;
+        for (int c = 0; c < k_real; ++c) s += (double)Ls[i][c] * (double)Ls[j][c];
+        Km[i][j] = s;
+        Km[j][i] = s;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double d = 0.0;
+        for (int i = 0; i < nn; ++i) d = fmax(d, Km[i][i]);
+        sh_tol = (double)nn * 1e-12 * d;
+        sh_rank = 0;
+    }
+    __syncthreads();
+    // ---- Cholesky with diagonal pivoting, right-looking
+    for (int s = 0; s < nn; ++s) {
+        if (tid == 0) {
+            int p = -1;
+            double d = sh_tol;
+            for (int i = 0; i < nn; ++i)
+                if (!done[i] && Km[i][i] > d) {
+                    d = Km[i][i];
+                    p = i;
+                }
+            sh_p = p;
+            sh_d = d;
+        }
+        __syncthreads();
+        const int p = sh_p;
+        if (p < 0) break;
+        const double sq = sqrt(sh_d), rs = 1.0 / sq;
+        if (tid < nn) Fm[tid][s] = done[tid] ? 0.0 : (tid == p ? sq : Km[tid][p] * rs);
+        __syncthreads();
+        for (int e = tid; e < nn * nn; e += NT) {
+            const int i = e / nn, j = e - i * nn;
+            Km[i][j] -= Fm[i][s] * Fm[j][s];
+        }
+        if (tid == 0) {
+            done[p] = 1;
+            sh_rank = s + 1;
+        }
+        __syncthreads();
+    }
+    const int rank = sh_rank;
+    float *Cb = coef + b * n * n;
+    if (rank == nn || rank == 0) {
+        // independent token rows: the projector is the identity; no rows: zero
+        for (int e = tid; e < nn * nn; e += NT) Cb[e] = (rank == nn && e / nn == e % nn) ? 1.f : 0.f;
+    } else {
+        // M = F^T F (rank x rank), then its inverse in place (Gauss-Jordan,
+        // SPD: no pivoting), W = F M^-1, C_b = W F^T
+        for (int e = tid; e < rank * rank; e += NT) {
+            const int a = e / rank, c = e - a * rank;
+            double s = 0.0;
+            for (int i = 0; i < nn; ++i) s += Fm[i][a] * Fm[i][c];
+            Km[a][c] = s;
+        }
+        __syncthreads();
+        for (int q = 0; q < rank; ++q) {
+            const double piv = Km[q][q];
+            __syncthreads();
+            // row q scaled, then every other row cleared in column q
+            if (tid < rank) Km[q][tid] = (tid == q ? 1.0 : Km[q][tid]) / piv;
+            __syncthreads();
+            for (int e = tid; e < rank * rank; e += NT) {
+                const int i = e / rank, j = e - i * rank;
+                if (i == q) continue;
+                const double f = Km[i][q];
+                // column q of the other rows becomes -f / piv (the inverse's column)
+                Wm[i][j] = j == q ? -f * Km[q][q] : Km[i][j] - f * Km[q][j];
+            }
+            __syncthreads();
+            for (int e = tid; e < rank * rank; e += NT) {
+                const int i = e / rank, j = e - i * rank;
+                if (i != q) Km[i][j] = Wm[i][j];
+            }
+            __syncthreads();
+        }
+        for (int e = tid; e < nn * rank; e += NT) {
+            const int i = e / rank, c = e - i * rank;
+            double s = 0.0;
+            for (int a = 0; a < rank; ++a) s += Fm[i][a] * Km[a][c];
+            Wm[i][c] = s;
+        }
+        __syncthreads();
+        for (int e = tid; e < nn * nn; e += NT) {
+            const int i = e / nn, j = e - i * nn;
+            double s = 0.0;
+            for (int a = 0; a < rank; ++a) s += Wm[i][a] * Fm[j][a];
+            Cb[e] = (float)s;
+        }
+    }
+    if (tid == 0) flags[b] = 0;
 }
 
 // Y[rows][col0..col0+32) = T_s V_s^T + bias + alpha blockdiag(C_b) (X W_res)
@@ -405,6 +548,13 @@ template <typename E> hipError_t launch_decode_project(const DecodeArgs<E> &a, h
 template <typename E> hipError_t launch_decode_coef(const DecodeArgs<E> &a, hipStream_t st) {
     const DualLayout L = dual_layout(a.B, a.n, a.c1, a.kw, a.kc);
     const int64_t N = a.B * a.n;
+    if (a.n > 16) {
+        if (a.n > kWideTokens || a.lambda != 0.f || a.kc > kMaxCorr) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((decode_coef_wide_kernel<E>), dim3((unsigned)a.B), dim3(NT), 0, st,
+                           (const float *)(a.ws + L.partial), N, a.n, a.kw + a.kc, a.kw, a.k_real, L.splits,
+                           (float *)(a.ws + L.T), (float *)(a.ws + L.coef), a.flags);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((decode_coef_kernel<E>), dim3((unsigned)a.B), dim3(NT), 0, st,
                        (const float *)(a.ws + L.partial), N, a.n, a.kw + a.kc, a.kw, a.k_real, L.splits, a.lambda,
                        (float *)(a.ws + L.T), (float *)(a.ws + L.coef), a.flags);

@@ -28,16 +28,20 @@ hipError_t launch_right(const E *Mp, const E *Wres_t, int64_t rows, int64_t c1, 
 
 // With C C^T = L1_b^T L1_b + lambda I: Q_b = L1_b C^-T replaces L1_b in place
 // (columns [off, off + kc) of T's rows b*n .. b*n + n - 1, leading dimension
-// ldt).  float32 also writes Qt[b] = Q_b^T ([kc][npad], token-contiguous, zero
-// for tokens n..npad-1); bf16 leaves Qt untouched and keeps C_b, column by
-// column, in Ct ([B][kc][kc] float32 workspace) between its two kernels.
-// flags[b] = 1 if a pivot broke down (then Q_b = 0).  kc in {16, 32, 48,
-// 64}.  Cout, if not null, receives the Cholesky factor C_b ([B][kc][kc]
-// float64, lower, identity on the padding) for the L updates of further ALS
-// steps.
+// ldt).  float32 (kc <= 64) also writes Qt[b] = Q_b^T ([kc][npad],
+// token-contiguous, zero for tokens n..npad-1); bf16 (kc <= 256) leaves Qt
+// untouched and keeps C_b, column by column, in Ct ([B][kc][kc] float32
+// workspace) between its two kernels, and, for kc above 128, G_b in Gw
+// ([B] x gram_workspace_floats(kc) float32 workspace).  flags[b] = 1 if a
+// pivot broke down (then Q_b = 0).  kc a multiple of 16.  Cout, if not null,
+// receives the Cholesky factor C_b ([B][kc][kc] float64, lower, identity on
+// the padding) for the L updates of further ALS steps.
 template <typename E>
 hipError_t launch_gram_q(E *T, int64_t ldt, int64_t off, int64_t B, int64_t n, int64_t npad, int kc_real, int kc,
-                         float lambda, E *Qt, float *Ct, int *flags, double *Cout, hipStream_t st);
+                         float lambda, E *Qt, float *Ct, float *Gw, int *flags, double *Cout, hipStream_t st);
+// Floats of the per-instance Gram buffer launch_gram_q<bf16> needs (0 if G
+// stays in LDS).
+size_t gram_workspace_floats(int kc);
 
 // Mp[b*kc + i][:] = (Q_b^T X_b)[i][:]: bf16 reads Q_b from T (as left by
 // launch_gram_q), float32 from Qt.

@@ -618,7 +618,7 @@ hipError_t launch_output_ex(const E *A, int64_t lda, int64_t K, const E *B, int6
                             const E *R1t, int64_t rstride, int64_t Ntok, int64_t n, int64_t N, const E *bias, E *Y,
                             int64_t ldy, int gcols, int64_t gstride, hipStream_t st) {
     if (Ntok <= 0) return hipSuccess;
-    if (kc > 0 && (n < 1 || kc > 64 || kc % 16 != 0)) return hipErrorInvalidValue;
+    if (kc > 0 && (n < 1 || kc > 256 || kc % 16 != 0)) return hipErrorInvalidValue;
     if (gcols < 0 || (gcols > 0 && N % gcols != 0)) return hipErrorInvalidValue;
     const RowStore<E> epi{Y, ldy, bias, N};
     Corr<E> c{R1t, n, kcol, kc, rstride, gcols, gstride};

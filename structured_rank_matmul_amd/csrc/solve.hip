@@ -32,6 +32,8 @@
 //   mprime (float32)  the same product from Q_b^T stored token-contiguous.
 #include "dyra_kernels.h"
 
+#include <utility>
+
 #include "elim.h"
 #include "mfma_tile.h"
 
@@ -99,116 +101,214 @@ __device__ __forceinline__ void chol_step(float (&g)[KC], int kc_real, float th,
     }
 }
 
-// Per instance b (one workgroup): G = L1_b^T L1_b + lambda I over all n tokens
-// on MFMA, then its Cholesky factor C in one wavefront (lane-per-row), stored
-// column by column as Ct[b][m][i] = C[i][m] (i > m), Ct[b][m][m] = 1 / C[m][m]
-// and zero above, which is the order the forward substitution of
-// q_apply_kernel reads it in.  The kernel only reads T: Q is formed by a later
-// launch, so no workgroup sees rows another one rewrites.
-//
-// Token chunks of 256 rows are loaded one per thread, written transposed to
-// LDS ([feature][token]) and multiplied there; the next chunk's loads are in
-// flight during the current chunk's MFMAs.
+// Sizes of gram_chol_kernel for a padded correction rank KC (a multiple of 16,
+// at most 256): G is factored as a KP x KP matrix (KC rounded up to whole
+// 32-wide panels, identity on the padding), held in LDS up to KP = 128 and in
+// the workspace (L2) above; token chunks of TT rows are staged per pass.
+template <int KC> constexpr int gram_kp() { return (KC + 31) / 32 * 32; }
+template <int KC> constexpr bool gram_g_in_lds() { return gram_kp<KC>() <= 128; }
+template <int KC> constexpr int gram_tokens() { return gram_kp<KC>() <= 64 ? 256 : (gram_kp<KC>() <= 128 ? 128 : 64); }
+
+// Per instance b (one workgroup of four wavefronts):
+//  1. G = L1_b^T L1_b + lambda I over all n tokens: token chunks are loaded,
+//     written transposed to LDS ([feature][token]) and multiplied on MFMA, the
+//     lower 32 x 32 blocks of G dealt round-robin to the wavefronts; the next
+//     chunk's loads are in flight during the current chunk's MFMAs.
+//  2. Its Cholesky factor C by 32-wide panels (right-looking, blocked): each
+//     wavefront eliminates [G_pp; 64 rows of G below the panel] with one row
+//     per lane (elim_step: the pivot rows reach every lane through
+//     v_readlane, each wavefront factoring the 32 x 32 diagonal block for
+//     itself), which leaves the panel's rows of C; the trailing matrix then
+//     loses C_below C_below^T, formed on float32 MFMA from the panel staged in
+//     LDS.
+// C is stored column by column, Ct[b][m][i] = C[i][m] (i > m), Ct[b][m][m] =
+// 1 / C[m][m], zero above: the order q_apply_kernel reads it in.  The kernel
+// only reads T; Q is formed by a later launch, so no workgroup sees rows
+// another one rewrites.
 template <int KC>
 __global__ __launch_bounds__(NT) void gram_chol_kernel(const bf16 *__restrict__ T, int64_t ldt, int64_t off,
                                                        int64_t n, int kc_real, float lambda, float *__restrict__ Ct,
-                                                       int *__restrict__ flags, double *__restrict__ Cout) {
-    static_assert(KC % 16 == 0 && KC <= 64, "correction rank");
-    constexpr int GS = 68;        // row stride (floats) of G in LDS
-    constexpr int TT = NT;        // tokens per chunk, one per thread
-    constexpr int ST = TT + 8;    // row stride (bf16) of the transposed chunk [feature][token]
-    constexpr int NBLK = (KC + 31) / 32;
-    constexpr int NV = KC / 8;    // 16-byte vectors per token row
-    __shared__ __align__(16) bf16 Lt[32 * NBLK * ST];
-    __shared__ __align__(16) float Gs[64 * GS];
+                                                       float *__restrict__ Gw, int *__restrict__ flags,
+                                                       double *__restrict__ Cout) {
+    static_assert(KC % 16 == 0 && KC >= 16 && KC <= 256, "correction rank");
+    constexpr int KP = gram_kp<KC>();
+    constexpr int NBB = KP / 32;                  // 32-blocks per side
+    constexpr int NLOW = NBB * (NBB + 1) / 2;     // lower blocks of G
+    constexpr int NQ = (NLOW + 3) / 4;            // G blocks per wavefront
+    constexpr int TT = gram_tokens<KC>();         // tokens per chunk
+    constexpr int ST = TT + 8;                    // row stride (bf16) of the transposed chunk
+    constexpr int VPR = KC / 8;                   // 16-byte vectors per token row
+    constexpr int TOT = TT * VPR;                 // vectors per chunk
+    constexpr int NL = (TOT + NT - 1) / NT;       // vectors per thread
+    constexpr bool GLDS = gram_g_in_lds<KC>();
+    constexpr int GS = GLDS ? KP + 4 : KP;        // row stride (floats) of G
+    constexpr int CBS = 36;                       // row stride (floats) of the staged panel
+    __shared__ __align__(16) bf16 Lt[KP * ST];
+    __shared__ __align__(16) float Gsh[GLDS ? KP * GS : 4];
+    __shared__ __align__(16) float Cb[(KP > 32 ? KP - 32 : 1) * CBS];
+    __shared__ float sh_dmax;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 31, lk = (lane >> 5) * 8;
     const int64_t b = blockIdx.x;
     const bf16 *const Tb = T + b * n * ldt + off;  // token t of instance b: Tb + t * ldt
+    float *const G = GLDS ? Gsh : Gw + b * KP * KP;
+    auto blk = [](int q, int &bi, int &bj) {  // q-th lower block, row by row
+        bi = 0;
+        while ((bi + 1) * (bi + 2) / 2 <= q) ++bi;
+        bj = q - bi * (bi + 1) / 2;
+    };
 
-    // features KC .. 32 NBLK - 1 of the transposed chunk are MFMA padding
-    if (KC % 32 != 0) {
-        for (int e = tid; e < (32 * NBLK - KC) * ST; e += NT) Lt[KC * ST + e] = bf16(0.f);
+    // features KC .. KP - 1 of the transposed chunk are MFMA padding
+    if (KC != KP) {
+        for (int e = tid; e < (KP - KC) * ST; e += NT) Lt[KC * ST + e] = bf16(0.f);
     }
     // a chunk's token rows, requested unconditionally (rows past n reread
     // row n - 1 and are zeroed when staged)
-    auto load = [&](int64_t c0, u32x4 (&v)[NV]) __attribute__((always_inline)) {
-        const int64_t t = c0 + tid < n ? c0 + tid : n - 1;
+    auto load = [&](int64_t c0, u32x4 (&v)[NL]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < NV; ++q) v[q] = *reinterpret_cast<const u32x4 *>(Tb + t * ldt + 8 * q);
+        for (int q = 0; q < NL; ++q) {
+            const int e = q * NT + tid < TOT ? q * NT + tid : 0;
+            const int tok = e % TT, vec = e / TT;
+            const int64_t t = c0 + tok < n ? c0 + tok : n - 1;
+            v[q] = *reinterpret_cast<const u32x4 *>(Tb + t * ldt + 8 * vec);
+        }
     };
-    const int wm = wave >> 1, wn = wave & 1;
-    const bool gact = wm < NBLK && wn < NBLK;
-    f32x16 acc = f32x16{};
+    f32x16 acc[NQ];
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) acc[s] = f32x16{};
     const int64_t nch = (n + TT - 1) / TT;
-    u32x4 v[NV];
+    u32x4 v[NL];
     load(0, v);
     for (int64_t ch = 0; ch < nch; ++ch) {
-        const bool in = ch * TT + tid < n;
         __syncthreads();  // the previous chunk's MFMA reads are done
 #pragma unroll
-        for (int q = 0; q < NV; ++q) {
-            union { u32x4 u; bf16 e[8]; } w;
-            w.u = v[q];
+        for (int q = 0; q < NL; ++q) {
+            const int e = q * NT + tid;
+            if (TOT % NT == 0 || e < TOT) {
+                const int tok = e % TT, vec = e / TT;
+                const bool in = ch * TT + tok < n;
+                union { u32x4 u; bf16 h[8]; } w;
+                w.u = v[q];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) Lt[(8 * q + e) * ST + tid] = in ? w.e[e] : bf16(0.f);
+                for (int j = 0; j < 8; ++j) Lt[(8 * vec + j) * ST + tok] = in ? w.h[j] : bf16(0.f);
+            }
         }
         __syncthreads();
         if (ch + 1 < nch) load((ch + 1) * TT, v);
-        if (gact) {
+#pragma unroll
+        for (int s = 0; s < NQ; ++s) {
+            const int q = wave + 4 * s;
+            if (q < NLOW) {
+                int bi, bj;
+                blk(q, bi, bj);
+                const bf16 *pa = Lt + (bi * 32 + lr) * ST + lk, *pb = Lt + (bj * 32 + lr) * ST + lk;
 #pragma unroll 4
-            for (int kk = 0; kk < TT; kk += 16)
-                acc = mma16(acc, ld_frag(Lt + (wm * 32 + lr) * ST + kk + lk), ld_frag(Lt + (wn * 32 + lr) * ST + kk + lk));
+                for (int kk = 0; kk < TT; kk += 16) acc[s] = mma16(acc[s], ld_frag(pa + kk), ld_frag(pb + kk));
+            }
         }
     }
-    if (gact) {
+    // G + lambda I on the real indices, identity on the padding (lower blocks)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) Gs[(wm * 32 + acc_row(lane, q)) * GS + wn * 32 + lr] = acc[q];
+    for (int s = 0; s < NQ; ++s) {
+        const int q = wave + 4 * s;
+        if (q < NLOW) {
+            int bi, bj;
+            blk(q, bi, bj);
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const int i = bi * 32 + acc_row(lane, t), j = bj * 32 + lr;
+                const bool real = i < kc_real && j < kc_real;
+                G[i * GS + j] = real ? acc[s][t] + (i == j ? lambda : 0.f) : (i == j ? 1.f : 0.f);
+            }
+        }
+    }
+    if (Cout) {  // its upper part stays zero; the panels fill the rest
+        for (int e = tid; e < KC * KC; e += NT) Cout[b * KC * KC + e] = 0.0;
     }
     __syncthreads();
-    if (wave != 0) return;
-
-    // ---- lane i holds row i of G + lambda I (identity rows past kc_real)
-    const int i = lane;
-    float g[KC];
-#pragma unroll
-    for (int m = 0; m < KC; m += 4) {
-        const float4 x = *reinterpret_cast<const float4 *>(&Gs[(i < KC ? i : 0) * GS + m]);
-        g[m] = x.x; g[m + 1] = x.y; g[m + 2] = x.z; g[m + 3] = x.w;
-    }
-    const float diag = i < kc_real ? Gs[i * GS + i] : 0.f;
-#pragma unroll
-    for (int m = 0; m < KC; ++m) {
-        const float e = (i < kc_real && m < kc_real) ? g[m] : 0.f;
-        g[m] = (m == i) ? (i < kc_real ? e + lambda : 1.f) : e;
-    }
     // a pivot at or below the working precision times the largest diagonal
     // marks a numerically singular G (possible only for lambda = 0)
-    float dmax = diag;
+    if (wave == 0) {
+        float d = 0.f;
+        for (int i = lane; i < kc_real; i += 64) d = fmaxf(d, G[i * GS + i]);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) dmax = fmaxf(dmax, __shfl_xor(dmax, o));
+        for (int o = 32; o > 0; o >>= 1) d = fmaxf(d, __shfl_xor(d, o));
+        if (lane == 0) sh_dmax = d;
+    }
+    __syncthreads();
+    const float dmax = sh_dmax;
     const float th = lambda > 0.f ? 0.f : (float)KC * 1.2e-7f * dmax;
     bool fail = !(dmax > 0.f);
-    chol_step<KC, 0>(g, kc_real, th, fail);
+    float *const Cb_ = Ct + b * KC * KC;
 
-    // ---- C column by column (coalesced over lanes), reciprocal diagonal
-    float *Cb = Ct + b * KC * KC;
-    if (i < KC) {
+    for (int p0 = 0; p0 < KP; p0 += 32) {
+        const int below = KP - p0 - 32;             // rows under the panel
+        const bool has_l = 64 * wave < below;
+        if (wave == 0 || has_l) {
+            float g[32], l[32];
+            const int rg = p0 + (lane < 32 ? lane : 0);
+            const int rl = p0 + 32 + 64 * wave + lane;
+            const bool lin = rl < KP;
 #pragma unroll
-        for (int m = 0; m < KC; ++m) {
-            const float c = m < i ? g[m] : (m == i ? __builtin_amdgcn_rcpf(g[m]) : 0.f);
-            Cb[m * KC + i] = fail ? 0.f : c;
+            for (int m = 0; m < 32; m += 4) {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(&G[rg * GS + p0 + m]);
+                const f32x4 y = *reinterpret_cast<const f32x4 *>(&G[(lin ? rl : rg) * GS + p0 + m]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    g[m + u] = lane < 32 ? x[u] : 0.f;
+                    l[m + u] = lin ? y[u] : 0.f;
+                }
+            }
+            bool f = false;
+            if (has_l) elim_step<32, 0>(g, l, kc_real - p0, th, f);
+            else chol_step<32, 0>(g, kc_real - p0, th, f);
+            if (wave == 0) fail = fail || f;
+            // the panel's rows of C: the diagonal block (wavefront 0) and the
+            // rows below it (every wavefront), by columns into Ct
+            if (wave == 0 && lane < 32 && p0 + lane < KC) {
+                const int i = p0 + lane;
+#pragma unroll
+                for (int m = 0; m < 32; ++m) {
+                    if (p0 + m < KC) {
+                        const float c = m < lane ? g[m] : (m == lane ? __builtin_amdgcn_rcpf(g[m]) : 0.f);
+                        Cb_[(p0 + m) * KC + i] = c;
+                        if (Cout && m <= lane) Cout[(b * KC + i) * KC + p0 + m] = (double)g[m];
+                    }
+                }
+            }
+            if (has_l && lin) {
+                if (rl < KC) {
+#pragma unroll
+                    for (int m = 0; m < 32; ++m) {
+                        if (p0 + m < KC) {
+                            Cb_[(p0 + m) * KC + rl] = l[m];
+                            if (Cout) Cout[(b * KC + rl) * KC + p0 + m] = (double)l[m];
+                        }
+                    }
+                }
+#pragma unroll
+                for (int m = 0; m < 32; m += 4)
+                    *reinterpret_cast<f32x4 *>(&Cb[(rl - p0 - 32) * CBS + m]) = f32x4{l[m], l[m + 1], l[m + 2], l[m + 3]};
+            }
         }
-    }
-    if (i == 0) flags[b] = fail ? 1 : 0;
-    // the factor itself (lane i holds row i of C in g[0..i]) for the L updates
-    // of further ALS steps
-    if (Cout && i < KC) {
-        double *Cr = Cout + ((int64_t)b * KC + i) * KC;
+        __syncthreads();
+        // trailing update G_ij -= C_i C_j^T over the lower 32-blocks under the panel
+        const int nbt = below / 32;
+        for (int q = wave; q < nbt * (nbt + 1) / 2; q += 4) {
+            int bi, bj;
+            blk(q, bi, bj);
+            f32x16 a = f32x16{};
 #pragma unroll
-        for (int m = 0; m < KC; ++m) Cr[m] = m <= i ? (double)g[m] : 0.0;
+            for (int k0 = 0; k0 < 32; k0 += 16)
+                a = mma16(a, ld_frag(&Cb[(bi * 32 + lr) * CBS + k0 + lk]), ld_frag(&Cb[(bj * 32 + lr) * CBS + k0 + lk]));
+            float *gb = G + (p0 + 32 + bi * 32) * GS + p0 + 32 + bj * 32;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) gb[acc_row(lane, t) * GS + lr] -= a[t];
+        }
+        __syncthreads();
     }
+    if (tid == 0) flags[b] = fail ? 1 : 0;
 }
 
 // Broadcast within groups of G lanes (G = 1, 2 or 4) of lane q of the group,
@@ -233,77 +333,116 @@ template <int G> __device__ __forceinline__ float group_bcast(float v, int q) {
     }
 }
 
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, each i a
+// compile-time constant.
+template <class F, int... Is>
+__device__ __forceinline__ void unroll_seq_impl(F &&f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F> __device__ __forceinline__ void unroll_seq(F &&f) {
+    unroll_seq_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // Lanes per token row in q_apply_kernel: each lane's share must be whole
 // 16-byte vectors.
-template <int KC> constexpr int q_lanes() { return KC % 32 == 0 ? 4 : (KC % 16 == 0 ? 2 : 1); }
+template <int KC> constexpr int q_lanes() { return KC % 32 == 0 ? 4 : 2; }
+// Rows of the factor staged in LDS at a time: the largest whole fraction of
+// KC that fits in 64 KB.
+template <int KC> constexpr int q_stage_rows() {
+    int d = 1;
+    while (KC % d != 0 || (KC / d) * KC * 4 > 65536) ++d;
+    return KC / d;
+}
 
 // Q_b = L1_b C^-T in place.  Each token row is spread over a group of G lanes
-// (G = q_lanes), lane p of the group holding columns [p PW, (p+1) PW).  The
-// forward substitution C q^T = l^T is taken column by column: step K scales
-// q_K by 1 / C[K][K] in the lane that owns it, broadcasts it over the group
-// (DPP), and every lane subtracts q_K C[m][K] from its columns m.  The factor,
-// the same for every token, is staged in LDS once per workgroup with the
-// diagonal and everything above it zero (the reciprocal diagonal kept apart),
-// so the updates need no masking; each 16-byte read is at G addresses per
-// wavefront.  64 G threads per workgroup, one token per group; rows of a
-// failed instance become zero.
+// (G = q_lanes), by 8-column chunks dealt round-robin: lane p of the group
+// holds chunks p, p + G, p + 2G, ...  The forward substitution C q^T = l^T is
+// taken column by column: step K scales q_K by 1 / C[K][K] in the lane that
+// owns it, broadcasts it over the group (DPP), and every lane subtracts
+// q_K C[m][K] from its columns m > K; with the chunks dealt round-robin the
+// lanes keep equal shares of the shrinking trailing part, and chunks wholly
+// at or left of K are skipped.  The factor, the same for every token, is
+// staged in LDS (in the lanes' column order, the diagonal and everything above
+// it zero, the reciprocal diagonal kept apart), so the updates need no
+// masking.  64 G threads per workgroup, one token per group; rows of a failed
+// instance become zero.
 template <int KC>
 __global__ __launch_bounds__(64 * q_lanes<KC>()) void q_apply_kernel(bf16 *__restrict__ T, int64_t ldt, int64_t off,
                                                                      int64_t n, const float *__restrict__ Ct,
                                                                      const int *__restrict__ flags) {
     constexpr int G = q_lanes<KC>();
-    constexpr int PW = KC / G;  // columns per lane
+    constexpr int PW = KC / G;   // columns per lane
+    constexpr int NU = PW / 8;   // chunks per lane
     constexpr int NTH = 64 * G;
-    static_assert(PW % 8 == 0, "columns per lane");
-    __shared__ __align__(16) float Cs[KC * KC];  // Cs[K][m] = C[m][K] for m > K, else 0
+    constexpr int CH = q_stage_rows<KC>();
+    static_assert(PW % 8 == 0 && KC % CH == 0, "columns per lane");
+    __shared__ __align__(16) float Cs[CH * KC];  // Cs[K][lane-order column] = C[col][K] for col > K, else 0
     __shared__ float rd[KC];                      // 1 / C[K][K]
     const int tid = threadIdx.x;
     const int p = tid % G;
     const int64_t b = blockIdx.y;
     const int64_t t = (int64_t)blockIdx.x * 64 + tid / G;
-    bf16 *const row = T + (b * n + (t < n ? t : n - 1)) * ldt + off + p * PW;
+    bf16 *const row = T + (b * n + (t < n ? t : n - 1)) * ldt + off;
     float x[PW];
 #pragma unroll
-    for (int q = 0; q < PW / 8; ++q) {
-        union { u32x4 u; bf16 e[8]; } w;
-        w.u = *reinterpret_cast<const u32x4 *>(row + 8 * q);
+    for (int u = 0; u < NU; ++u) {
+        union { u32x4 u4; bf16 e[8]; } w;
+        w.u4 = *reinterpret_cast<const u32x4 *>(row + 8 * (p + G * u));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[8 * q + e] = (float)w.e[e];
+        for (int e = 0; e < 8; ++e) x[8 * u + e] = (float)w.e[e];
     }
-    const f32x4 *Cb = reinterpret_cast<const f32x4 *>(Ct + b * KC * KC);
-    for (int e = tid; e < KC * KC / 4; e += NTH) {
-        f32x4 v = Cb[e];
-        const int K = (4 * e) / KC, m0 = (4 * e) % KC;
+    const float *Cb = Ct + b * KC * KC;
+    // one substitution step, K a compile-time constant (x is indexed by it)
+    auto step = [&](auto Kc, const float *cs) __attribute__((always_inline)) {
+        constexpr int K = decltype(Kc)::value;
+        constexpr int cK = K / 8, PK = cK % G, IDX = 8 * (cK / G) + K % 8;
+        const float sc = x[IDX] * rd[K];
+        x[IDX] = p == PK ? sc : x[IDX];
+        const float qk = group_bcast<G>(x[IDX], PK);
+        const float *cr = cs + p * PW;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (m0 + u == K) rd[K] = v[u];
-            if (m0 + u <= K) v[u] = 0.f;
+        for (int u = (K / 8) / G; u < NU; ++u) {
+#pragma unroll
+            for (int j0 = 0; j0 < 8; j0 += 4) {
+                const f32x4 c = *reinterpret_cast<const f32x4 *>(cr + 8 * u + j0);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) x[8 * u + j0 + v] = fmaf(-qk, c[v], x[8 * u + j0 + v]);
+            }
         }
-        reinterpret_cast<f32x4 *>(Cs)[e] = v;
-    }
-    __syncthreads();
+    };
+    // rows [K0, K0 + CH) of the factor: staged in LDS, then their steps
+    auto stage = [&](auto K0c) __attribute__((always_inline)) {
+        constexpr int K0 = decltype(K0c)::value;
+        if constexpr (K0 > 0) __syncthreads();  // the previous rows' reads are done
+        for (int e = tid; e < CH * KC / 4; e += NTH) {
+            const int Kl = (4 * e) / KC, pos = (4 * e) % KC;
+            const int pp = pos / PW, uu = (pos % PW) / 8, jj = pos % 8;
+            const int col = 8 * (pp + G * uu) + jj, K = K0 + Kl;
+            f32x4 v = *reinterpret_cast<const f32x4 *>(Cb + K * KC + col);
 #pragma unroll
-    for (int K = 0; K < KC; ++K) {
-        const int PK = K / PW, U = K % PW;
-        const float sc = x[U] * rd[K];
-        x[U] = p == PK ? sc : x[U];
-        const float qk = group_bcast<G>(x[U], PK);
-        const float *cr = &Cs[K * KC + p * PW];
-#pragma unroll
-        for (int v0 = 0; v0 < PW; v0 += 4) {
-            const f32x4 c = *reinterpret_cast<const f32x4 *>(cr + v0);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) x[v0 + u] = fmaf(-qk, c[u], x[v0 + u]);
+            for (int u = 0; u < 4; ++u) {
+                if (col + u == K) rd[K] = v[u];
+                if (col + u <= K) v[u] = 0.f;
+            }
+            *reinterpret_cast<f32x4 *>(&Cs[Kl * KC + pos]) = v;
         }
-    }
+        __syncthreads();
+        unroll_seq<CH>([&](auto Klc) __attribute__((always_inline)) {
+            constexpr int Kl = decltype(Klc)::value;
+            step(std::integral_constant<int, K0 + Kl>{}, &Cs[Kl * KC]);
+        });
+    };
+    unroll_seq<KC / CH>([&](auto Sc) __attribute__((always_inline)) {
+        stage(std::integral_constant<int, decltype(Sc)::value * CH>{});
+    });
     const bool dead = flags[b] != 0;
     if (t < n) {
 #pragma unroll
-        for (int q = 0; q < PW / 8; ++q) {
-            union { u32x4 u; bf16 e[8]; } w;
+        for (int u = 0; u < NU; ++u) {
+            union { u32x4 u4; bf16 e[8]; } w;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) w.e[e] = dead ? bf16(0.f) : (bf16)x[8 * q + e];
-            *reinterpret_cast<u32x4 *>(row + 8 * q) = w.u;
+            for (int e = 0; e < 8; ++e) w.e[e] = dead ? bf16(0.f) : (bf16)x[8 * u + e];
+            *reinterpret_cast<u32x4 *>(row + 8 * (p + G * u)) = w.u4;
         }
     }
 }
@@ -541,7 +680,7 @@ __device__ __forceinline__ uint2 lds_tr16(const char *p) {
 template <int KC, int CW>
 __global__ __launch_bounds__(NT) void mprime_tr_kernel(const bf16 *__restrict__ X, const bf16 *__restrict__ T,
                                                        int64_t ldt, int64_t off, int64_t n, int64_t c1,
-                                                       bf16 *__restrict__ Mp) {
+                                                       bf16 *__restrict__ Mp, int64_t mp_rows, int mp_row0) {
     // CW features per workgroup, CW / 4 per wavefront
     constexpr int TS = 32;                  // tokens per slice
     constexpr int RB = CW * 2;              // bytes per X row in LDS
@@ -687,7 +826,7 @@ __global__ __launch_bounds__(NT) void mprime_tr_kernel(const bf16 *__restrict__ 
     for (int q = 0; q < KC * CPM / NT; ++q) {
         const int e = q * NT + tid, row = e / CPM, c = e % CPM;
         if (f0 + 8 * c < c1)
-            *reinterpret_cast<u32x4 *>(Mp + (b * KC + row) * c1 + f0 + 8 * c) =
+            *reinterpret_cast<u32x4 *>(Mp + (b * mp_rows + mp_row0 + row) * c1 + f0 + 8 * c) =
                 *reinterpret_cast<const u32x4 *>(ms + row * MS + 8 * c);
     }
 }
@@ -696,29 +835,34 @@ __global__ __launch_bounds__(NT) void mprime_tr_kernel(const bf16 *__restrict__ 
 
 template <>
 hipError_t launch_gram_q<bf16>(bf16 *T, int64_t ldt, int64_t off, int64_t B, int64_t n, int64_t, int kc_real,
-                               int kc, float lambda, bf16 *, float *Ct, int *flags, double *Cout, hipStream_t st) {
+                               int kc, float lambda, bf16 *, float *Ct, float *Gw, int *flags, double *Cout,
+                               hipStream_t st) {
     if (B <= 0) return hipSuccess;
     const dim3 g1((unsigned)B), g2((unsigned)((n + 63) / 64), (unsigned)B);
     switch (kc) {
 #define DYRA_GQ(KC)                                                                                                  \
     case KC:                                                                                                         \
-        hipLaunchKernelGGL(gram_chol_kernel<KC>, g1, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda, Ct, flags,     \
+        hipLaunchKernelGGL(gram_chol_kernel<KC>, g1, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda, Ct, Gw, flags, \
                            Cout);                                                                                    \
         hipLaunchKernelGGL(q_apply_kernel<KC>, g2, dim3(64 * q_lanes<KC>()), 0, st, T, ldt, off, n, Ct, flags);      \
         break;
-        DYRA_GQ(16)
-        DYRA_GQ(32)
-        DYRA_GQ(48)
-        DYRA_GQ(64)
+        DYRA_GQ(16) DYRA_GQ(32) DYRA_GQ(48) DYRA_GQ(64) DYRA_GQ(80) DYRA_GQ(96) DYRA_GQ(112) DYRA_GQ(128)
+        DYRA_GQ(144) DYRA_GQ(160) DYRA_GQ(176) DYRA_GQ(192) DYRA_GQ(208) DYRA_GQ(224) DYRA_GQ(240) DYRA_GQ(256)
 #undef DYRA_GQ
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
+size_t gram_workspace_floats(int kc) {
+    const int kp = (kc + 31) / 32 * 32;
+    return kp > 128 ? (size_t)kp * kp : 0;
+}
+
 template <>
 hipError_t launch_gram_q<float>(float *T, int64_t ldt, int64_t off, int64_t B, int64_t n, int64_t npad, int kc_real,
-                                int kc, float lambda, float *Qt, float *, int *flags, double *Cout, hipStream_t st) {
+                                int kc, float lambda, float *Qt, float *, float *, int *flags, double *Cout,
+                                hipStream_t st) {
     if (B <= 0) return hipSuccess;
     if (kc < 1 || kc > 64) return hipErrorInvalidValue;
     hipLaunchKernelGGL(gram_q_f32_kernel, dim3((unsigned)B), dim3(NT), 0, st, T, ldt, off, n, npad, kc_real, kc,
@@ -730,14 +874,23 @@ template <>
 hipError_t launch_mprime<bf16>(const bf16 *X, const bf16 *T, int64_t ldt, int64_t off, const bf16 *, int64_t B,
                                int64_t n, int64_t, int64_t c1, int kc, bf16 *Mp, hipStream_t st) {
     if (B <= 0) return hipSuccess;
+    if (kc < 16 || kc % 16 != 0) return hipErrorInvalidValue;
     constexpr int CW = kMprimeFeatures;
     const dim3 grid((unsigned)((c1 + CW - 1) / CW), (unsigned)B);
-    switch (kc) {
-    case 16: hipLaunchKernelGGL((mprime_tr_kernel<16, CW>), grid, dim3(NT), 0, st, X, T, ldt, off, n, c1, Mp); break;
-    case 32: hipLaunchKernelGGL((mprime_tr_kernel<32, CW>), grid, dim3(NT), 0, st, X, T, ldt, off, n, c1, Mp); break;
-    case 48: hipLaunchKernelGGL((mprime_tr_kernel<48, CW>), grid, dim3(NT), 0, st, X, T, ldt, off, n, c1, Mp); break;
-    case 64: hipLaunchKernelGGL((mprime_tr_kernel<64, CW>), grid, dim3(NT), 0, st, X, T, ldt, off, n, c1, Mp); break;
-    default: return hipErrorInvalidValue;
+    // correction ranks above 64 in passes of at most 64 rows of M'_b (X_b is
+    // streamed once per pass)
+    for (int r0 = 0; r0 < kc; r0 += 64) {
+        const int w = kc - r0 < 64 ? kc - r0 : 64;
+        switch (w) {
+#define DYRA_MP(KC)                                                                                                   \
+    case KC:                                                                                                          \
+        hipLaunchKernelGGL((mprime_tr_kernel<KC, CW>), grid, dim3(NT), 0, st, X, T, ldt, off + r0, n, c1, Mp,          \
+                           (int64_t)kc, r0);                                                                          \
+        break;
+            DYRA_MP(16) DYRA_MP(32) DYRA_MP(48) DYRA_MP(64)
+#undef DYRA_MP
+        default: return hipErrorInvalidValue;
+        }
     }
     return hipGetLastError();
 }

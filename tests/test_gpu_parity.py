@@ -121,6 +121,58 @@ def test_forward_small(dtype, case):
     run_case(W, X, B, n, r, k, 0.0, dtype)
 
 
+LARGE_K = [
+    # B, n, c1, c2, r, k: correction ranks above 64 (blocked Cholesky,
+    # several 32-wide panels; G in the workspace above 128; M' in passes of 64)
+    (4, 300, 512, 640, 64, 128),
+    (3, 400, 512, 512, 32, 256),
+    (2, 260, 384, 512, 40, 200),    # padded to 208: panels past the real rank
+    (5, 150, 256, 384, 48, 80),     # n < 2k, tiles straddle instances
+]
+
+
+@pytest.mark.parametrize("case", LARGE_K, ids=lambda c: f"B{c[0]}n{c[1]}-{c[2]}x{c[3]}-r{c[4]}k{c[5]}")
+def test_forward_large_correction_rank(case):
+    B, n, c1, c2, r, k = case
+    W = synth.random_weight(c1, c2, 13 + k, p=0.5)
+    X = synth.random_matrix(B * n, c1, 14 + n, "bf16")
+    X = synth.round_activations(X.exact * np.exp(synth.random_matrix(1, c1, 15, "f32").exact), "bf16")
+    run_case(W, X, B, n, r, k, 0.0, "bf16")
+
+
+@pytest.mark.parametrize("k", [128, 192])
+def test_vitl_qkv_large_correction_rank(k):
+    """The ViT-L qkv layer (128 x 201 tokens, 1024 -> 3072, r = 256) with a
+    correction rank of 128 and 192, three instances against the oracle."""
+    import torch
+    w = synth.WORKLOADS["vitl_block"]
+    spec = w.layer("qkv")
+    W, _ = synth.make_weight(w, spec)
+    X = synth.make_activations(w, spec)
+    plan = dyra.dyra_prepare(W, spec.r, k, 0.0, "bf16", 0)
+    Y = dyra.dyra_forward(to_device(X), w.B, w.n, plan)
+    torch.cuda.synchronize()
+    sample = [0, 63, 127]
+    rows = np.concatenate([np.arange(b * w.n, (b + 1) * w.n) for b in sample])
+    Xs = X.exact[rows]
+    op = oracle_plan(W, spec.r, k, 0.0)
+    ref = orc.inference(Xs, len(sample), w.n, op)
+    y = to_host(Y)[rows]
+    err, wi, wr = check_parity(y, ref, w.n, "bf16", f"vitl qkv k={k}")
+    exact = Xs @ W.astype(np.float64)
+    gap = own_error_gap(y, ref, exact)
+    e_orc = rel(ref, exact)
+    print(f"vitl qkv k={k}: parity {err:.3e} (instance {wi:.3e}, row {wr:.3e})  own-error gap {gap:.3e}  "
+          f"e_dyra {e_orc:.4f}", flush=True)
+    # the output's own rounding adds to the approximation error in
+    # quadrature, e_gpu^2 ~ e_orc^2 + err^2, so the 1% bar on the own error
+    # is reachable only where e_orc >= 7 err (k = 192 leaves e_dyra near 0.02,
+    # within 6x of the bf16 rounding of Y: parity is the measure there)
+    if e_orc >= 7 * err:
+        assert gap <= OWN_ERR_TOL
+    plan.close()
+
+
 def test_forward_k_tail_on_large_tiles():
     """32 instances of 201 tokens into 4096 outputs select the 256 x 256
     output tiles with correction slices; r = 96 leaves a short last static
@@ -189,6 +241,55 @@ def test_forward_dual_form(dtype, B, n, lam):
     W = synth.random_weight(c1, c2, 51, p=0.5)
     X = synth.random_matrix(B * n, c1, 52 + B * n, dtype)
     run_case(W, X, B, n, r, k, lam, dtype, check_own=(lam > 0 or n > 1))
+
+
+# ------------------------------------------------------------------ 16 < n < k
+
+@pytest.mark.parametrize("dtype", ["bf16"])
+@pytest.mark.parametrize("B,n,c1,c2,r,k", [(6, 20, 256, 320, 32, 32), (4, 40, 256, 384, 48, 64),
+                                           (3, 63, 256, 256, 32, 64), (2, 50, 512, 512, 64, 128),
+                                           (5, 17, 128, 192, 16, 48)])
+def test_forward_fewer_tokens_than_rank_no_ridge(dtype, B, n, c1, c2, r, k):
+    """lambda = 0 and 16 < n < k: the dual form with the projector onto
+    range(L1_b); with independent token rows that projector is the identity and
+    the output is X W up to the plan's rounding."""
+    W = synth.random_weight(c1, c2, 101 + n, p=0.5)
+    X = synth.random_matrix(B * n, c1, 102 + n, dtype)
+    run_case(W, X, B, n, r, k, 0.0, dtype, check_own=False)
+
+
+def test_forward_fewer_tokens_than_rank_rank_deficient():
+    """lambda = 0, 16 < n < k, instances whose L1 rows are dependent: repeated
+    tokens (rank 10 of 30) and an all-zero instance.  The projector is then
+    onto a proper subspace; it must still match the oracle's minimum-norm
+    least-squares result."""
+    B, n, c1, c2, r, k = 3, 30, 256, 320, 32, 64
+    W = synth.random_weight(c1, c2, 111, p=0.5)
+    X = synth.random_matrix(B * n, c1, 112, "bf16")
+    X.data[n:2 * n] = np.tile(X.data[n:n + 10], (3, 1))   # instance 1: 10 distinct rows, each 3 times
+    X.data[2 * n:] = 0                                    # instance 2: zero
+    run_case(W, X, B, n, r, k, 0.0, "bf16", check_own=False)
+
+
+@pytest.mark.parametrize("B,n,c1,c2,r,k,lam", [(4, 40, 256, 384, 48, 64, 0.5), (3, 100, 512, 512, 64, 128, 0.1)])
+def test_forward_fewer_tokens_than_rank_with_ridge(B, n, c1, c2, r, k, lam):
+    """lambda > 0 and 16 < n < k: the primal form (L1^T L1 + lambda I is
+    positive definite)."""
+    W = synth.random_weight(c1, c2, 121 + n, p=0.5)
+    X = synth.random_matrix(B * n, c1, 122 + n, "bf16")
+    run_case(W, X, B, n, r, k, lam, "bf16")
+
+
+def test_forward_refuses_long_instances_below_rank_without_ridge():
+    """lambda = 0 with 64 < n < k has no supported form."""
+    import torch
+    W = synth.random_weight(512, 512, 131)
+    plan = dyra.dyra_prepare(W, 32, 128, 0.0, "bf16", 0)
+    X = torch.zeros((2 * 100, 512), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(dyra.DyraError) as e:
+        dyra.dyra_forward(X, 2, 100, plan)
+    assert e.value.status == 2
+    plan.close()
 
 
 # ------------------------------------------------------------------ workload shapes

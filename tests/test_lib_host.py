@@ -55,8 +55,9 @@ def test_prepare_rejects_bad_arguments():
     assert _prepare_status(W, 64, 64, 8, 8, dtype=7) == 3      # dtype
     W2 = np.zeros((48, 64), np.float32)
     assert _prepare_status(W2, 48, 64, 8, 8) == 2              # c1 not a multiple of 32
-    W3 = np.zeros((256, 256), np.float32)
-    assert _prepare_status(W3, 256, 256, 8, 80) == 2           # correction rank above 64
+    W3 = np.zeros((512, 512), np.float32)
+    assert _prepare_status(W3, 512, 512, 8, 264) == 2          # correction rank above 256
+    assert _prepare_status(W3, 512, 512, 8, 80, dtype=0) == 2  # float32 plans: correction rank above 64
 
 
 def test_forward_and_dense_ref_reject_bad_arguments():
@@ -181,7 +182,7 @@ def test_prepare_blast_rejects_bad_arguments():
     assert _blast_status(W, c1, c2, nb, rb, U, S, V, 8, lam=-1.0) == 1
     assert _blast_status(W, c1, c2, nb, rb, U, S, V, 8, dtype=9) == 3
     assert _blast_status(W, c1, c2, 8, rb, U, S, V, 8) == 2            # more than 4 blocks
-    assert _blast_status(W, c1, c2, nb, rb, U, S, V, 80) == 2          # k above 64
+    assert _blast_status(W, c1, c2, nb, rb, U, S, V, 80, dtype=0) == 2  # float32: k above 64
     W2 = np.zeros((192, 128), np.float32)
     assert _blast_status(W2, 192, 128, nb, rb, U, S, V, 8) == 2        # c1 not a multiple of 32 nb
     big = np.zeros((c1, 2080), np.float32)
