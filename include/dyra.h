@@ -126,7 +126,9 @@ dyra_status dyra_prepare(const float *W, int64_t c1, int64_t c2, int32_t r, int3
  * needs a larger workspace; dyra_forward runs the extra steps for instances
  * on the primal path (n > 16 tokens with n >= k, or n < k with lambda > 0) and
  * returns DYRA_ERR_SHAPE for the dual form, which carries one ALS step only.
- * als_half_steps > 2 and ns_iters > 0 take k <= 64 (DYRA_ERR_SHAPE above).
+ * als_half_steps > 2 takes k <= 64 (DYRA_ERR_SHAPE above).  With ns_iters > 0
+ * and k above 64 the correction rank is padded to a multiple of 64 and each
+ * Newton-Schulz product runs for all instances at once on float32 MFMA.
  */
 dyra_status dyra_prepare_ex(const float *W, int64_t c1, int64_t c2, int32_t r, int32_t k, float lambda,
                             dyra_dtype dtype, int device, const float *R0, int32_t als_half_steps,

@@ -137,7 +137,8 @@ Path path_for(const dyra_plan *p, int64_t n) {
 //   H      float32 [8][B][kc][kc] partial sums of R' R'^T
 //   Kp     float32 [B][kc][kc]   the L update's coefficients
 //   with the Newton-Schulz solve (ns_iters > 0):
-//   F      float32 [B][kc][kc]   G^-1/2 per instance
+//   F      float32               G^-1/2 per instance [B][kc][kc] (kc <= 64), or the
+//                                iterates of the batched solve (ns_workspace_floats)
 //   dual   decode workspace      (n <= 16 or n < k only)
 struct Layout {
     size_t flags, T, Qt, Ct, Gw, Mp, R1t, C, R1row, Sp, H, Kp, F, dual, total;
@@ -170,7 +171,7 @@ Layout workspace_layout(const dyra_plan *p, int64_t B, int64_t n) {
         off += align_up(es * B * p->c2 * p->kc);
         if (p->ns_iters > 0) {
             L.F = off;
-            off += align_up(sizeof(float) * (size_t)B * p->kc * p->kc);
+            off += align_up(sizeof(float) * dyra::ns_workspace_floats(B, p->kc));
         }
         if (p->half_steps > 2) {
             const size_t kk = (size_t)B * p->kc * p->kc;
@@ -470,9 +471,10 @@ dyra_status dyra_prepare_ex(const float *W, int64_t c1, int64_t c2, int32_t r, i
     if (!(lambda >= 0.f) || !std::isfinite(lambda)) return DYRA_ERR_ARG;
     if (c1 % 32 != 0 || c2 % 32 != 0) return DYRA_ERR_SHAPE;
     if (k > kMaxCorrection) return DYRA_ERR_SHAPE;
-    if (k > kMaxCorrectionSmall && (dtype == DYRA_F32 || als_half_steps > 2 || ns_iters > 0)) return DYRA_ERR_SHAPE;
+    if (k > kMaxCorrectionSmall && (dtype == DYRA_F32 || als_half_steps > 2)) return DYRA_ERR_SHAPE;
     const int32_t kw = r > 0 ? (int32_t)round_up(r, 32) : 0;
-    const int32_t kc = k > 0 ? (int32_t)round_up(k, 16) : 0;
+    // the Newton-Schulz products of ranks above 64 run in 64-wide tiles
+    const int32_t kc = k > 0 ? (int32_t)round_up(k, (ns_iters > 0 && k > kMaxCorrectionSmall) ? 64 : 16) : 0;
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) return DYRA_ERR_NODEVICE;
 

@@ -42,6 +42,12 @@ hipError_t launch_gram_q(E *T, int64_t ldt, int64_t off, int64_t B, int64_t n, i
 // Floats of the per-instance Gram buffer launch_gram_q<bf16> needs (0 if G
 // stays in LDS).
 size_t gram_workspace_floats(int kc);
+// G_b = L1_b^T L1_b + lambda I alone (identity on the padding past kc_real),
+// written whole to G ([B][kp][kp] float32, kp = kc rounded up to 32), for
+// kc in 80..256 (the Newton-Schulz solve of large correction ranks).
+template <typename E>
+hipError_t launch_gram_only(const E *T, int64_t ldt, int64_t off, int64_t B, int64_t n, int kc_real, int kc,
+                            float lambda, float *G, hipStream_t st);
 
 // Mp[b*kc + i][:] = (Q_b^T X_b)[i][:]: bf16 reads Q_b from T (as left by
 // launch_gram_q), float32 from Qt.
@@ -139,6 +145,10 @@ hipError_t launch_als_lupdate(const AlsArgs<E> &a, int last, float alpha, hipStr
 // [off, off + kc) (float32 plans also fill Qt as launch_gram_q does).
 // flags[b] = 1 where F is not finite (the correction is then dropped).  Two
 // kernels, each followed by mark().
+// Floats of the Newton-Schulz workspace F of launch_ns_solve: F_b [kc][kc]
+// per instance for kc <= 64; the iterates Y, Z (two each), T ([kp][kp] per
+// instance) and the scale c per instance above.
+size_t ns_workspace_floats(int64_t B, int kc);
 template <typename E>
 hipError_t launch_ns_solve(E *T, int64_t ldt, int64_t off, int64_t B, int64_t n, int64_t npad, int kc_real, int kc,
                            float lambda, int iters, float *F, int *flags, float *Qt, hipStream_t st,

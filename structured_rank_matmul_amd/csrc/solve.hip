@@ -32,9 +32,8 @@
 //   mprime (float32)  the same product from Q_b^T stored token-contiguous.
 #include "dyra_kernels.h"
 
-#include <utility>
-
 #include "elim.h"
+#include "lanes.h"
 #include "mfma_tile.h"
 
 namespace dyra {
@@ -125,7 +124,9 @@ template <int KC> constexpr int gram_tokens() { return gram_kp<KC>() <= 64 ? 256
 // 1 / C[m][m], zero above: the order q_apply_kernel reads it in.  The kernel
 // only reads T; Q is formed by a later launch, so no workgroup sees rows
 // another one rewrites.
-template <int KC>
+// GONLY: stop after G, written whole (both triangles) to Gw for the
+// Newton-Schulz solve.
+template <int KC, bool GONLY = false>
 __global__ __launch_bounds__(NT) void gram_chol_kernel(const bf16 *__restrict__ T, int64_t ldt, int64_t off,
                                                        int64_t n, int kc_real, float lambda, float *__restrict__ Ct,
                                                        float *__restrict__ Gw, int *__restrict__ flags,
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(NT) void gram_chol_kernel(const bf16 *__restrict__ 
     constexpr int VPR = KC / 8;                   // 16-byte vectors per token row
     constexpr int TOT = TT * VPR;                 // vectors per chunk
     constexpr int NL = (TOT + NT - 1) / NT;       // vectors per thread
-    constexpr bool GLDS = gram_g_in_lds<KC>();
+    constexpr bool GLDS = !GONLY && gram_g_in_lds<KC>();
     constexpr int GS = GLDS ? KP + 4 : KP;        // row stride (floats) of G
     constexpr int CBS = 36;                       // row stride (floats) of the staged panel
     __shared__ __align__(16) bf16 Lt[KP * ST];
@@ -219,10 +220,13 @@ __global__ __launch_bounds__(NT) void gram_chol_kernel(const bf16 *__restrict__ 
             for (int t = 0; t < 16; ++t) {
                 const int i = bi * 32 + acc_row(lane, t), j = bj * 32 + lr;
                 const bool real = i < kc_real && j < kc_real;
-                G[i * GS + j] = real ? acc[s][t] + (i == j ? lambda : 0.f) : (i == j ? 1.f : 0.f);
+                const float gv = real ? acc[s][t] + (i == j ? lambda : 0.f) : (i == j ? 1.f : 0.f);
+                G[i * GS + j] = gv;
+                if (GONLY && bi != bj) G[j * GS + i] = gv;
             }
         }
     }
+    if constexpr (GONLY) return;
     if (Cout) {  // its upper part stays zero; the panels fill the rest
         for (int e = tid; e < KC * KC; e += NT) Cout[b * KC * KC + e] = 0.0;
     }
@@ -311,51 +315,8 @@ __global__ __launch_bounds__(NT) void gram_chol_kernel(const bf16 *__restrict__ 
     if (tid == 0) flags[b] = fail ? 1 : 0;
 }
 
-// Broadcast within groups of G lanes (G = 1, 2 or 4) of lane q of the group,
-// by DPP quad_perm (one VALU instruction, no LDS).  q is a constant once the
-// caller's loop is unrolled, so the switch folds away.
-template <int G> __device__ __forceinline__ float group_bcast(float v, int q) {
-    if constexpr (G == 1) {
-        return v;
-    } else {
-        int ctrl;
-        if constexpr (G == 4) ctrl = q * 0x55;                                          // [q, q, q, q]
-        else ctrl = q | (q << 2) | ((2 + q) << 4) | ((2 + q) << 6);                    // [q, q, 2+q, 2+q]
-        const int iv = __float_as_int(v);
-        int r;
-        switch (ctrl) {
-#define DYRA_DPP(C) case C: r = __builtin_amdgcn_mov_dpp(iv, C, 0xf, 0xf, false); break;
-            DYRA_DPP(0x00) DYRA_DPP(0x55) DYRA_DPP(0xaa) DYRA_DPP(0xff) DYRA_DPP(0xa0) DYRA_DPP(0xf5)
-#undef DYRA_DPP
-        default: r = iv;
-        }
-        return __int_as_float(r);
-    }
-}
-
-// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, each i a
-// compile-time constant.
-template <class F, int... Is>
-__device__ __forceinline__ void unroll_seq_impl(F &&f, std::integer_sequence<int, Is...>) {
-    (f(std::integral_constant<int, Is>{}), ...);
-}
-template <int N, class F> __device__ __forceinline__ void unroll_seq(F &&f) {
-    unroll_seq_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// Lanes per token row in q_apply_kernel: each lane's share must be whole
-// 16-byte vectors.
-template <int KC> constexpr int q_lanes() { return KC % 32 == 0 ? 4 : 2; }
-// Rows of the factor staged in LDS at a time: the largest whole fraction of
-// KC that fits in 64 KB.
-template <int KC> constexpr int q_stage_rows() {
-    int d = 1;
-    while (KC % d != 0 || (KC / d) * KC * 4 > 65536) ++d;
-    return KC / d;
-}
-
 // Q_b = L1_b C^-T in place.  Each token row is spread over a group of G lanes
-// (G = q_lanes), by 8-column chunks dealt round-robin: lane p of the group
+// (G = token_lanes), by 8-column chunks dealt round-robin: lane p of the group
 // holds chunks p, p + G, p + 2G, ...  The forward substitution C q^T = l^T is
 // taken column by column: step K scales q_K by 1 / C[K][K] in the lane that
 // owns it, broadcasts it over the group (DPP), and every lane subtracts
@@ -367,14 +328,14 @@ template <int KC> constexpr int q_stage_rows() {
 // masking.  64 G threads per workgroup, one token per group; rows of a failed
 // instance become zero.
 template <int KC>
-__global__ __launch_bounds__(64 * q_lanes<KC>()) void q_apply_kernel(bf16 *__restrict__ T, int64_t ldt, int64_t off,
+__global__ __launch_bounds__(64 * token_lanes<KC>()) void q_apply_kernel(bf16 *__restrict__ T, int64_t ldt, int64_t off,
                                                                      int64_t n, const float *__restrict__ Ct,
                                                                      const int *__restrict__ flags) {
-    constexpr int G = q_lanes<KC>();
+    constexpr int G = token_lanes<KC>();
     constexpr int PW = KC / G;   // columns per lane
     constexpr int NU = PW / 8;   // chunks per lane
     constexpr int NTH = 64 * G;
-    constexpr int CH = q_stage_rows<KC>();
+    constexpr int CH = stage_rows<KC>();
     static_assert(PW % 8 == 0 && KC % CH == 0, "columns per lane");
     __shared__ __align__(16) float Cs[CH * KC];  // Cs[K][lane-order column] = C[col][K] for col > K, else 0
     __shared__ float rd[KC];                      // 1 / C[K][K]
@@ -844,11 +805,29 @@ hipError_t launch_gram_q<bf16>(bf16 *T, int64_t ldt, int64_t off, int64_t B, int
     case KC:                                                                                                         \
         hipLaunchKernelGGL(gram_chol_kernel<KC>, g1, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda, Ct, Gw, flags, \
                            Cout);                                                                                    \
-        hipLaunchKernelGGL(q_apply_kernel<KC>, g2, dim3(64 * q_lanes<KC>()), 0, st, T, ldt, off, n, Ct, flags);      \
+        hipLaunchKernelGGL(q_apply_kernel<KC>, g2, dim3(64 * token_lanes<KC>()), 0, st, T, ldt, off, n, Ct, flags);      \
         break;
         DYRA_GQ(16) DYRA_GQ(32) DYRA_GQ(48) DYRA_GQ(64) DYRA_GQ(80) DYRA_GQ(96) DYRA_GQ(112) DYRA_GQ(128)
         DYRA_GQ(144) DYRA_GQ(160) DYRA_GQ(176) DYRA_GQ(192) DYRA_GQ(208) DYRA_GQ(224) DYRA_GQ(240) DYRA_GQ(256)
 #undef DYRA_GQ
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <>
+hipError_t launch_gram_only<bf16>(const bf16 *T, int64_t ldt, int64_t off, int64_t B, int64_t n, int kc_real, int kc,
+                                  float lambda, float *G, hipStream_t st) {
+    if (B <= 0) return hipSuccess;
+    switch (kc) {
+#define DYRA_GO(KC)                                                                                                  \
+    case KC:                                                                                                         \
+        hipLaunchKernelGGL((gram_chol_kernel<KC, true>), dim3((unsigned)B), dim3(NT), 0, st, T, ldt, off, n, kc_real, \
+                           lambda, nullptr, G, nullptr, nullptr);                                                    \
+        break;
+        DYRA_GO(80) DYRA_GO(96) DYRA_GO(112) DYRA_GO(128) DYRA_GO(144) DYRA_GO(160) DYRA_GO(176) DYRA_GO(192)
+        DYRA_GO(208) DYRA_GO(224) DYRA_GO(240) DYRA_GO(256)
+#undef DYRA_GO
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -18,6 +18,11 @@ CASES = [
     (5, 37, 128, 160, 16, 12, 0.05, "bf16", 6),     # not converged: the oracle takes the same 6 steps
     (2, 300, 128, 416, 20, 40, 0.0, "f32", 30),     # k = 40 padded to 48
     (3, 201, 256, 512, 64, 64, 0.0, "bf16", 24),
+    # correction ranks above 64: batched float32 MFMA products, rank padded to 64
+    (3, 300, 512, 640, 64, 128, 0.0, "bf16", 24),
+    (2, 400, 512, 512, 32, 256, 0.1, "bf16", 24),
+    (3, 250, 384, 512, 40, 150, 0.0, "bf16", 30),
+    (4, 200, 256, 384, 32, 100, 0.05, "bf16", 8),    # not converged: the oracle takes the same 8 steps
 ]
 
 
