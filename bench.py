@@ -12,6 +12,7 @@ and the oracle's own throughput on the host cores.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -290,6 +291,52 @@ def blast_record(w, layers, args, stream, reps, t_dense, log):
     return rec, legs
 
 
+def solve_scaling_record(w, layers, args, stream, log):
+    """The two SPD solves of §2.4 side by side as the correction rank and the
+    number of instances grow: stage time of the Cholesky solve (gram_q) and of
+    the Newton-Schulz one (ns_factor + ns_apply, ns_iters steps), and the whole
+    layer call, on the first layer's weight with n = 320 tokens per instance
+    (rows of the workload's own activations) and B = 1, 8, 64."""
+    import torch
+    from structured_rank_matmul_amd import dyra
+    L = layers[0]
+    spec = L["spec"]
+    n = 320
+    iters = args.ns_scaling_iters
+    rec = {"layer": spec.name, "tokens_per_instance": n, "ns_iters": iters, "points": []}
+    for k in (64, 128, 256):
+        if spec.r + k > min(spec.c1, spec.c2):
+            continue
+        plans = {"cholesky": dyra.dyra_prepare(L["W"], spec.r, k, 0.0, w.dtype, 0),
+                 "newton_schulz": dyra.dyra_prepare_ex(L["W"], spec.r, k, 0.0, w.dtype, 0, ns_iters=iters)}
+        for B in (1, 8, 64):
+            if B * n > w.B * w.n:
+                continue
+            xd = L["xd"][:B * n]
+            y = torch.empty((B * n, spec.c2), dtype=xd.dtype, device=xd.device)
+            pt = {"k": k, "instances": B}
+            for name, plan in plans.items():
+                ws = dyra.alloc_workspace(plan, B, n)
+                names = dyra.stage_names(plan, n)
+                evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+                acc = np.zeros(len(names))
+                reps = 5
+                for it in range(reps + 1):
+                    dyra.dyra_forward_timed(xd, B, n, plan, y, ws, evs, stream)
+                    torch.cuda.synchronize()
+                    if it:
+                        acc += [evs[i].elapsed_time(evs[i + 1]) / 1e3 for i in range(len(names))]
+                per = {nm: acc[i] / reps for i, nm in enumerate(names)}
+                solve = sum(v for nm, v in per.items() if nm in ("gram_q", "ns_factor", "ns_apply"))
+                pt[name] = {"solve_us": round(solve * 1e6, 2), "layer_us": round(sum(per.values()) * 1e6, 2)}
+            rec["points"].append(pt)
+            log(f"solve scaling k={k} B={B}: cholesky {pt['cholesky']['solve_us']} us, "
+                f"newton-schulz {pt['newton_schulz']['solve_us']} us")
+        for plan in plans.values():
+            plan.close()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -308,9 +355,13 @@ def main():
     ap.add_argument("--no-blast", action="store_true",
                     help="skip the BLAST static-approximation measurement (a second weight and plan per layer)")
     ap.add_argument("--blast-blocks", type=int, default=4, help="BLAST blocks per side")
+    ap.add_argument("--no-solve-scaling", action="store_true",
+                    help="skip the Cholesky vs Newton-Schulz solve record over k = 64, 128, 256 and B = 1, 8, 64")
+    ap.add_argument("--ns-scaling-iters", type=int, default=12, help="Newton-Schulz steps in that record")
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run three forward steps and a calibration copy only (for rocprofv3 --pmc runs)")
+    ap.add_argument("--layers", default="", help="with --traffic-probe: comma-separated layer names to run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the DyRA layer path here is a "
@@ -326,6 +377,13 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = synth.workload(args.workload)
+    if args.layers:
+        # a subset of the workload's layers (profiling runs only: the bench
+        # line's step is every layer)
+        keep = [x for x in args.layers.split(",") if x]
+        w = dataclasses.replace(w, layers=tuple(spec for spec in w.layers if spec.name in keep))
+        if not args.traffic_probe:
+            ap.error("--layers is for --traffic-probe runs only")
     dual = any(dual_form(spec, w.n) for spec in w.layers)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     B, n, N = w.B, w.n, w.B * w.n
@@ -576,6 +634,11 @@ def main():
     if not args.no_blast and not dual:
         blast, blast_legs = blast_record(w, layers, args, stream, reps, t_dense, log)
 
+    # ---- §2.4's two SPD solves as k and B grow
+    solve_scaling = None
+    if not args.no_solve_scaling and not dual and w.dtype == "bf16":
+        solve_scaling = solve_scaling_record(w, layers, args, stream, log)
+
     # ---- the CPU leg, the one place this script runs the oracle: its float64
     # result on the sampled instances set beside the library's (parity, the
     # oracle's own error, the static part alone), and its throughput on the
@@ -613,6 +676,7 @@ def main():
         "flops_matched_static": matched,
         "als_steps": als_steps,
         "newton_schulz": ns,
+        "solve_scaling": solve_scaling,
         "blast": blast,
         "roofline": roofline,
         "stage_roofline": stage_roofline,

@@ -7,7 +7,9 @@ rocprofv3 writes, with ``--output-format csv``:
 * ``<prefix>_counter_collection.csv`` for ``--pmc``: one row per dispatch and
   counter.
 
-``stats`` turns the first into a short text table; ``traffic`` turns a
+``stats`` turns the first into a short text table; ``counters`` lists every
+counter of one ``--pmc`` run per kernel (means per dispatch) with the MFMA
+busy fraction and bf16 MFMA FLOPs derived from them; ``traffic`` turns a
 FETCH_SIZE run and a WRITE_SIZE run into HBM bytes per dispatch of one kernel,
 each counter scaled by what it reads for a plain copy kernel whose bytes are
 known (the copy reads and writes exactly ``--copy-bytes``).  The traffic file
@@ -155,6 +157,61 @@ def cmd_traffic(a):
     _write(a.out, "\n".join(out) + "\n")
 
 
+def counter_table(directory: str):
+    """{kernel name: {counter: (dispatches, mean value per dispatch)}} for every
+    counter of one --pmc run."""
+    path = _find(directory, "counter_collection.csv")
+    names = set()
+    with open(path, newline="") as f:
+        r = csv.DictReader(f)
+        cc = _col(r.fieldnames, "Counter_Name", "CounterName")
+        for row in r:
+            names.add(row[cc])
+    table = {}
+    for c in sorted(names):
+        for k, v in counter_means(directory, c).items():
+            table.setdefault(k, {})[c] = v
+    return table
+
+
+def cmd_counters(a):
+    table = counter_table(a.dir)
+    avg_ns = {}
+    if a.stats_dir:
+        avg_ns = {name: avg for name, _, _, avg, _, _ in kernel_stats(a.stats_dir)}
+    rx = re.compile(a.kernel) if a.kernel else None
+    counters = sorted({c for v in table.values() for c in v})
+    out = [f"# rocprofv3 counters per dispatch: {a.title}", "", "commands:"]
+    out += [f"    {c}" for c in a.command]
+    out += ["", "derived (per dispatch, where the counters are present):",
+            f"    mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {a.xcds} XCDs * {a.simds} SIMDs)",
+            f"      (GRBM_GUI_ACTIVE sums the {a.xcds} XCDs' busy cycles, SQ_VALU_MFMA_BUSY_CYCLES the SIMDs'"
+            " matrix-core cycles; gpu_clock_ghz below checks the first reading against the kernel trace)",
+            "    mfma_bf16_flop = 512 * SQ_INSTS_VALU_MFMA_MOPS_BF16",
+            "    mfma_bf16_tflops = mfma_bf16_flop / average kernel duration (kernel trace)", ""]
+    for name in sorted(table, key=lambda k: -max(v[1] for v in table[k].values())):
+        if rx and not rx.search(name):
+            continue
+        vals = table[name]
+        out.append(short_name(name, 120))
+        for c in counters:
+            if c in vals:
+                out.append(f"    {c:32s} {vals[c][1]:16.1f}   ({vals[c][0]} dispatches)")
+        busy, gui = vals.get("SQ_VALU_MFMA_BUSY_CYCLES"), vals.get("GRBM_GUI_ACTIVE")
+        if busy and gui and gui[1] > 0:
+            out.append(f"    {'mfma_busy':32s} {busy[1] / (gui[1] / a.xcds * a.simds):16.4f}")
+            if name in avg_ns and avg_ns[name] > 0:
+                out.append(f"    {'gpu_clock_ghz':32s} {gui[1] / a.xcds / avg_ns[name]:16.3f}")
+        mops = vals.get("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        if mops:
+            flop = 512.0 * mops[1]
+            out.append(f"    {'mfma_bf16_flop':32s} {flop:16.4e}")
+            if name in avg_ns and avg_ns[name] > 0:
+                out.append(f"    {'avg_duration_us':32s} {avg_ns[name] / 1e3:16.2f}")
+                out.append(f"    {'mfma_bf16_tflops':32s} {flop / avg_ns[name] / 1e3:16.1f}")
+    _write(a.out, "\n".join(out) + "\n")
+
+
 def read_traffic(path: str):
     """Traffic bytes per dispatch from a summary written by ``traffic``, or None
     if the file is missing or the kernel's sources changed since."""
@@ -208,6 +265,16 @@ def main(argv=None):
     t.add_argument("--title", default="")
     t.add_argument("--out", default="-")
     t.set_defaults(fn=cmd_traffic)
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--command", action="append", required=True, help="the command(s) that made the runs")
+    c.add_argument("--stats-dir", default=None, help="a --kernel-trace --stats run of the same command")
+    c.add_argument("--kernel", default=None, help="regex on the kernel name")
+    c.add_argument("--xcds", type=int, default=8)
+    c.add_argument("--simds", type=int, default=1024, help="SIMDs of the GPU (4 per CU)")
+    c.add_argument("--title", default="")
+    c.add_argument("--out", default="-")
+    c.set_defaults(fn=cmd_counters)
     a = ap.parse_args(argv)
     a.fn(a)
 

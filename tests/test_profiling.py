@@ -53,3 +53,28 @@ def test_traffic_calibration_and_staleness(tmp_path, monkeypatch):
     monkeypatch.setattr(profiling, "sources_sha256", lambda sources=(), root="": "0" * 64)
     assert profiling.read_traffic(str(out)) is None
     assert profiling.read_traffic(str(tmp_path / "missing.txt")) is None
+
+
+def test_counter_table_and_derived_mfma_figures(tmp_path):
+    d = tmp_path / "pmc"
+    lines = ['"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value"']
+    for did in range(2):
+        lines += [f'{did},"gemm_kernel<out>","SQ_VALU_MFMA_BUSY_CYCLES",{512000 + did * 0}',
+                  f'{did},"gemm_kernel<out>","GRBM_GUI_ACTIVE",4000',
+                  f'{did},"gemm_kernel<out>","SQ_INSTS_VALU_MFMA_MOPS_BF16",1000000']
+    _write(str(d / "run_counter_collection.csv"), "\n".join(lines) + "\n")
+    s = tmp_path / "stats"
+    _write(str(s / "run_kernel_stats.csv"),
+           '"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+           '"gemm_kernel<out>",2,200000,100000,100,100000,100000,0\n')
+    t = profiling.counter_table(str(d))
+    assert t["gemm_kernel<out>"]["GRBM_GUI_ACTIVE"] == (2, 4000.0)
+    out = tmp_path / "c.txt"
+    profiling.main(["counters", str(d), "--command", "x", "--stats-dir", str(s), "--simds", "2048",
+                    "--out", str(out)])
+    text = open(out).read()
+    # 512000 / (4000 / 8 * 1024) = 1.0 with the defaults; with 2048 SIMDs 0.5;
+    # 512 * 1e6 flop over 100 us = 5.12 TFLOP/s
+    assert "mfma_busy" in text and " 0.5000" in text
+    line = [ln for ln in text.splitlines() if ln.strip().startswith("mfma_bf16_tflops")][-1]
+    assert float(line.split()[-1]) == pytest.approx(5.12, abs=0.05)
