@@ -107,3 +107,4 @@ def test_algorithmic_bytes_count_each_layer_array_once(wname):
         assert total == es * (N * c1 + N * c2 + (r + k) * c1 + c2 * r + c1 * c2)
         op = bench.stage_operand_bytes(spec, w.B, w.n, es)
         assert all(op[s] >= by[s] for s in stages)
+

@@ -173,6 +173,40 @@ def test_vitl_qkv_large_correction_rank(k):
     plan.close()
 
 
+PANELS = [
+    # B, n, c1, c2, r, k, lambda: instance boundaries against the GEMMs' row
+    # tiles, a static rank that fills whole 32-wide K slices, a ragged last tile
+    (5, 37, 384, 512, 256, 64, 0.3),     # several instances per tile (n < k: ridge)
+    (3, 201, 384, 768, 240, 64, 0.0),    # r = 240 padded to 256; instances straddle tiles
+    (4, 64, 512, 512, 256, 64, 0.0),     # instances aligned with 64-row blocks
+    (2, 100, 320, 512, 240, 50, 0.5),    # k = 50 padded to 64, with a ridge
+    (3, 90, 320, 512, 256, 0, 0.0),      # static path: no correction
+    (1, 1000, 448, 1024, 256, 64, 0.0),  # one long instance, ragged last tile
+]
+
+
+@pytest.mark.parametrize("case", PANELS, ids=lambda c: f"B{c[0]}n{c[1]}-{c[2]}x{c[3]}-r{c[4]}k{c[5]}-lam{c[6]}")
+def test_forward_instance_boundaries(case):
+    B, n, c1, c2, r, k, lam = case
+    W = synth.random_weight(c1, c2, 141 + n, p=0.6)
+    X = synth.random_matrix(B * n, c1, 142 + n, "bf16")
+    run_case(W, X, B, n, r, k, lam, "bf16", check_own=k > 0)
+
+
+def test_forward_ex_bias_alpha_full_static_slices():
+    import torch
+    B, n, c1, c2, r, k = 4, 70, 384, 512, 256, 64
+    W = synth.random_weight(c1, c2, 151, p=0.6)
+    X = synth.random_matrix(B * n, c1, 152, "bf16")
+    bias = synth.random_matrix(1, c2, 153, "bf16", scale=2.0)
+    plan = dyra.dyra_prepare(W, r, k, 0.0, "bf16", 0)
+    Y = dyra.dyra_forward_ex(to_device(X), B, n, plan, bias=to_device(bias)[0], alpha=-0.5)
+    torch.cuda.synchronize()
+    ref = orc.inference(X.exact, B, n, oracle_plan(W, r, k, 0.0), bias=bias.exact[0], alpha=-0.5)
+    check_parity(to_host(Y), ref, n, "bf16", "bias/alpha r = 256")
+    plan.close()
+
+
 def test_forward_k_tail_on_large_tiles():
     """32 instances of 201 tokens into 4096 outputs select the 256 x 256
     output tiles with correction slices; r = 96 leaves a short last static
