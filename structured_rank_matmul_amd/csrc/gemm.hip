@@ -75,26 +75,32 @@ template <typename E> __device__ __forceinline__ typename Pack4<E>::type pack4(c
     }
 }
 
-// Epilogue functors.  fix4(v, i, j) adjusts four float32 results before they
-// are rounded to E: (i, j) is the first of four consecutive columns of row i
-// (row-major stores) or of four consecutive rows of column j (R1t stores).
-// store4 then writes the rounded four.
+// Epilogue functors.  fix4(v, i, j, ct) adjusts four float32 results before
+// they are rounded to E: (i, j) is the first of four consecutive columns of row
+// i (row-major stores) or of four consecutive rows of column j (R1t stores);
+// ct, for functors with kColumnTerms, points at the four columns' additive
+// terms as the kernel staged them in LDS (null when there are none).  store4
+// then writes the rounded four.
 
 // Row-major D: store4(i, j, p) writes columns j..j+3 of row i, as a
 // non-temporal store (the outputs of these products are not read again by the
 // kernel; streaming them keeps them from evicting cached operands).  With a bias
 // (the fused linear layer of §2.4: Y = X_tmp A^T + b + alpha L R) every row
-// gets bias[j] added to column j before rounding.
+// gets bias[j] added to column j before rounding; the kernel reads the tile's
+// bias columns once per tile into LDS (read per element from global memory,
+// each of the epilogue's loads waited in turn and cost more than the tile's
+// MFMAs).
 template <typename E> struct RowStore {
+    static constexpr bool kColumnTerms = true;
     E *D;
     int64_t ldd;
     const E *bias = nullptr;  // [ncols] or null
     int64_t ncols = 0;
-    __device__ __forceinline__ void fix4(float (&v)[4], int64_t, int64_t j) const {
-        if (bias) {
+    __device__ __forceinline__ void fix4(float (&v)[4], int64_t, int64_t, const float *ct) const {
+        if (ct) {
+            const f32x4 b = *reinterpret_cast<const f32x4 *>(ct);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (j + q < ncols) v[q] += (float)bias[j + q];
+            for (int q = 0; q < 4; ++q) v[q] += b[q];
         }
     }
     __device__ __forceinline__ void store4(int64_t i, int64_t j, const typename Pack4<E>::type &p) const {
@@ -113,10 +119,11 @@ template <typename E> struct RowStore {
 // instance b = r / kc) of column c, stored as R1t[b][c][kk..kk+3], scaled by
 // alpha (the correction's weight in §2.4's fused output; 1 in Eq. 6).
 template <typename E> struct R1tStore {
+    static constexpr bool kColumnTerms = false;
     E *R1t;
     int64_t kc, c2;
     float alpha = 1.f;
-    __device__ __forceinline__ void fix4(float (&v)[4], int64_t, int64_t) const {
+    __device__ __forceinline__ void fix4(float (&v)[4], int64_t, int64_t, const float *) const {
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] *= alpha;
     }
@@ -154,6 +161,16 @@ template <typename E> struct Corr {
     int gcols = 0;
     int64_t gstride = 0;
 };
+
+template <typename E, int BM, int BN, int NS, int SB, bool ROWS> constexpr size_t gemm_smem() {
+    return (epi_staged<E, BM, BN, ROWS>() && epi_bytes<E, BM, BN, ROWS>() > stage_bytes<BM, BN, NS, SB>())
+               ? epi_bytes<E, BM, BN, ROWS>()
+               : stage_bytes<BM, BN, NS, SB>();
+}
+// ... plus BN floats of per-column terms after it for functors that have them
+template <typename E, int BM, int BN, int NS, int SB, bool ROWS, class Epi> constexpr size_t gemm_smem_total() {
+    return gemm_smem<E, BM, BN, NS, SB, ROWS>() + (Epi::kColumnTerms ? sizeof(float) * BN : 0);
+}
 
 // ROWS = true: the epilogue receives four consecutive columns of one row (the
 // MFMA is issued with the operands swapped, so a lane holds a row of the
@@ -208,6 +225,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+    // the tile's per-column terms, requested now (ahead of the K slices' loads,
+    // so they have landed by the first slice) and staged in LDS at the epilogue
+    float cterm = 0.f;
+    if constexpr (Epi::kColumnTerms) {
+        static_assert(ROWS, "per-column terms with row-major stores");
+        if (epi.bias != nullptr && tid < BN) {
+            const int64_t c = col0 + tid;
+            cterm = c < epi.ncols ? to_f32(epi.bias[c]) : 0.f;
+        }
+    }
 
     // static slices, then SC correction slices per instance of the tile
     const int64_t S0 = (K + BK - 1) / BK;
@@ -381,6 +408,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
     if constexpr (CORR) {
         for (; s < S; ++s) slice(s, std::integral_constant<int, 2>{});
     }
+    float *const cts = reinterpret_cast<float *>(smem + gemm_smem<E, BM, BN, NS, SB, ROWS>());
+    bool has_ct = false;
+    if constexpr (Epi::kColumnTerms) {
+        has_ct = epi.bias != nullptr;
+        if (has_ct && tid < BN) cts[tid] = cterm;
+    }
     __syncthreads();
     // ---- epilogue.  A lane holds four consecutive elements of the store's
     // contiguous direction (columns for ROWS, rows otherwise).  When the tile
@@ -402,7 +435,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
                     const int ti = (wm * TM + i) * 32, tj = (wn * TN + j) * 32;
                     const int lrow = ROWS ? ti + lr : tj + lr;              // LDS row
                     const int lcol = (ROWS ? tj : ti) + acc_row(lane, 4 * g);  // 4 consecutive
-                    epi.fix4(v, row0 + (ROWS ? lrow : lcol), col0 + (ROWS ? lcol : lrow));
+                    epi.fix4(v, row0 + (ROWS ? lrow : lcol), col0 + (ROWS ? lcol : lrow), has_ct ? cts + lcol : nullptr);
                     *reinterpret_cast<P *>(lds + lrow * OS + lcol) = pack4<E>(v);
                 }
         __syncthreads();
@@ -426,7 +459,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
                     const int64_t rb = row0 + wm * TM * 32 + i * 32, cb0 = col0 + wn * TN * 32 + j * 32;
                     const int64_t r = ROWS ? rb + lr : rb + acc_row(lane, 4 * g);
                     const int64_t c = ROWS ? cb0 + acc_row(lane, 4 * g) : cb0 + lr;
-                    epi.fix4(v, r, c);
+                    epi.fix4(v, r, c, has_ct ? cts + (c - col0) : nullptr);
                     if (r < M && c < N) epi.store4(r, c, pack4<E>(v));
                 }
     }
@@ -435,11 +468,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const E *__restrict_
     }
 }
 
-template <typename E, int BM, int BN, int NS, int SB, bool ROWS> constexpr size_t gemm_smem() {
-    return (epi_staged<E, BM, BN, ROWS>() && epi_bytes<E, BM, BN, ROWS>() > stage_bytes<BM, BN, NS, SB>())
-               ? epi_bytes<E, BM, BN, ROWS>()
-               : stage_bytes<BM, BN, NS, SB>();
-}
 
 // One-time host set-up of a kernel instantiation on the current device: its
 // dynamic LDS limit and the number of workgroups resident per CU (the
@@ -475,9 +503,9 @@ template <typename E, int BM, int BN, int WM, int WN, int NS, int SB, bool ROWS,
           class Epi>
 hipError_t gemm_launch(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N, int64_t K,
                        const Corr<E> &corr, Epi epi, hipStream_t st, bool setup_only = false) {
-    static_assert(gemm_smem<E, BM, BN, NS, SB, ROWS>() <= kLdsBytes, "LDS");
+    static_assert(gemm_smem_total<E, BM, BN, NS, SB, ROWS, Epi>() <= kLdsBytes, "LDS");
     auto kfn = gemm_kernel<E, BM, BN, WM, WN, NS, SB, ROWS, CORR, Epi, GROUPED>;
-    constexpr size_t smem = gemm_smem<E, BM, BN, NS, SB, ROWS>();
+    constexpr size_t smem = gemm_smem_total<E, BM, BN, NS, SB, ROWS, Epi>();
     static LaunchSetup ls;
     hipError_t e = ensure_setup(ls, kfn, 64 * WM * WN, smem);
     if (e != hipSuccess || setup_only) return e;
