@@ -188,7 +188,10 @@ def cmd_counters(a):
             f"      (GRBM_GUI_ACTIVE sums the {a.xcds} XCDs' busy cycles, SQ_VALU_MFMA_BUSY_CYCLES the SIMDs'"
             " matrix-core cycles; gpu_clock_ghz below checks the first reading against the kernel trace)",
             "    mfma_bf16_flop = 512 * SQ_INSTS_VALU_MFMA_MOPS_BF16",
-            "    mfma_bf16_tflops = mfma_bf16_flop / average kernel duration (kernel trace)", ""]
+            "    mfma_bf16_tflops = mfma_bf16_flop / average kernel duration (kernel trace)",
+            f"    mfma_bf16_frac = mfma_bf16_tflops / {a.peak_tflops:g} (the dense bf16 MFMA peak); the counter"
+            " runs and the trace run are separate processes, so mfma_busy (one run's cycles) and this"
+            " (both runs) can disagree; the implied clock shows by how much", ""]
     for name in sorted(table, key=lambda k: -max(v[1] for v in table[k].values())):
         if rx and not rx.search(name):
             continue
@@ -209,6 +212,7 @@ def cmd_counters(a):
             if name in avg_ns and avg_ns[name] > 0:
                 out.append(f"    {'avg_duration_us':32s} {avg_ns[name] / 1e3:16.2f}")
                 out.append(f"    {'mfma_bf16_tflops':32s} {flop / avg_ns[name] / 1e3:16.1f}")
+                out.append(f"    {'mfma_bf16_frac':32s} {flop / avg_ns[name] / 1e3 / a.peak_tflops:16.4f}")
     _write(a.out, "\n".join(out) + "\n")
 
 
@@ -272,6 +276,7 @@ def main(argv=None):
     c.add_argument("--kernel", default=None, help="regex on the kernel name")
     c.add_argument("--xcds", type=int, default=8)
     c.add_argument("--simds", type=int, default=1024, help="SIMDs of the GPU (4 per CU)")
+    c.add_argument("--peak-tflops", type=float, default=2500.0, help="dense bf16 MFMA peak (MI355X)")
     c.add_argument("--title", default="")
     c.add_argument("--out", default="-")
     c.set_defaults(fn=cmd_counters)
