@@ -126,8 +126,12 @@ template <int KC> constexpr int gram_tokens() { return gram_kp<KC>() <= 64 ? 256
 // another one rewrites.
 // GONLY: stop after G, written whole (both triangles) to Gw for the
 // Newton-Schulz solve.
-template <int KC, bool GONLY = false>
-__global__ __launch_bounds__(NT) void gram_chol_kernel(const bf16 *__restrict__ T, int64_t ldt, int64_t off,
+// FUSE (n <= 256, KC <= 64): the instance's tokens are one chunk, still in LDS
+// after G, so the workgroup also forms Q = L1 C^-T (a token per thread,
+// forward substitution against C kept row-major in LDS) and writes it over
+// L1: one launch instead of two, and no other workgroup reads these rows.
+template <int KC, bool GONLY = false, bool FUSE = false>
+__global__ __launch_bounds__(NT) void gram_chol_kernel(const bf16 *T, int64_t ldt, int64_t off,
                                                        int64_t n, int kc_real, float lambda, float *__restrict__ Ct,
                                                        float *__restrict__ Gw, int *__restrict__ flags,
                                                        double *__restrict__ Cout) {
@@ -147,7 +151,13 @@ __global__ __launch_bounds__(NT) void gram_chol_kernel(const bf16 *__restrict__ 
     __shared__ __align__(16) bf16 Lt[KP * ST];
     __shared__ __align__(16) float Gsh[GLDS ? KP * GS : 4];
     __shared__ __align__(16) float Cb[(KP > 32 ? KP - 32 : 1) * CBS];
+    // FUSE: C row-major (Cs[i][m] = C[i][m] below the diagonal, 1 / C[i][i] on
+    // it) for the in-kernel substitution
+    static_assert(!FUSE || (KP <= 64 && TT >= NT && !GONLY), "fused Q: one token chunk, one token per thread");
+    constexpr int CSS = KP + 4;
+    __shared__ __align__(16) float Cs[FUSE ? KP * CSS : 4];
     __shared__ float sh_dmax;
+    __shared__ int sh_fail;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 31, lk = (lane >> 5) * 8;
@@ -277,6 +287,7 @@ __global__ __launch_bounds__(NT) void gram_chol_kernel(const bf16 *__restrict__ 
                     if (p0 + m < KC) {
                         const float c = m < lane ? g[m] : (m == lane ? __builtin_amdgcn_rcpf(g[m]) : 0.f);
                         Cb_[(p0 + m) * KC + i] = c;
+                        if constexpr (FUSE) Cs[i * CSS + p0 + m] = c;
                         if (Cout && m <= lane) Cout[(b * KC + i) * KC + p0 + m] = (double)g[m];
                     }
                 }
@@ -287,6 +298,7 @@ __global__ __launch_bounds__(NT) void gram_chol_kernel(const bf16 *__restrict__ 
                     for (int m = 0; m < 32; ++m) {
                         if (p0 + m < KC) {
                             Cb_[(p0 + m) * KC + rl] = l[m];
+                            if constexpr (FUSE) Cs[rl * CSS + p0 + m] = l[m];
                             if (Cout) Cout[(b * KC + rl) * KC + p0 + m] = (double)l[m];
                         }
                     }
@@ -313,6 +325,47 @@ __global__ __launch_bounds__(NT) void gram_chol_kernel(const bf16 *__restrict__ 
         __syncthreads();
     }
     if (tid == 0) flags[b] = fail ? 1 : 0;
+    if constexpr (FUSE) {
+        // Q = L1 C^-T by forward substitution, one token per thread: the
+        // instance's L1 is still in LDS (one chunk, transposed) and C in Cs;
+        // every thread reads the same row of C at a time (LDS broadcasts)
+        if (tid == 0) sh_fail = fail ? 1 : 0;
+        __syncthreads();
+        const bool dead = sh_fail != 0;
+        const int t = tid;
+        if (t < n) {
+            float q[KC];
+#pragma unroll
+            for (int m = 0; m < KC; ++m) q[m] = (float)Lt[m * ST + t];
+            // row by row: q_i = (l_i - sum_{m < i} C[i][m] q_m) / C[i][i], row i
+            // of C read as 16-byte broadcasts, two partial sums
+            unroll_seq<KC>([&](auto I) __attribute__((always_inline)) {
+                constexpr int i = decltype(I)::value;
+                float s0 = q[i], s1 = 0.f;
+                const float *ci = Cs + i * CSS;
+#pragma unroll
+                for (int m0 = 0; m0 < i; m0 += 4) {
+                    const f32x4 c4 = *reinterpret_cast<const f32x4 *>(ci + m0);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        if (m0 + u < i) {
+                            if (u & 1) s1 = fmaf(-c4[u], q[m0 + u], s1);
+                            else s0 = fmaf(-c4[u], q[m0 + u], s0);
+                        }
+                    }
+                }
+                q[i] = (s0 + s1) * ci[i];
+            });
+            bf16 *dst = const_cast<bf16 *>(Tb) + (int64_t)t * ldt;
+#pragma unroll
+            for (int v = 0; v < KC / 8; ++v) {
+                union { u32x4 u; bf16 h[8]; } w;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) w.h[e] = dead ? bf16(0.f) : (bf16)q[8 * v + e];
+                *reinterpret_cast<u32x4 *>(dst + 8 * v) = w.u;
+            }
+        }
+    }
 }
 
 // Q_b = L1_b C^-T in place.  Each token row is spread over a group of G lanes
@@ -800,6 +853,20 @@ hipError_t launch_gram_q<bf16>(bf16 *T, int64_t ldt, int64_t off, int64_t B, int
                                hipStream_t st) {
     if (B <= 0) return hipSuccess;
     const dim3 g1((unsigned)B), g2((unsigned)((n + 63) / 64), (unsigned)B);
+    if (kc <= 64 && n <= NT) {
+        // one launch: the workgroup of an instance holds all its tokens, so it
+        // forms Q itself once C is done (no other workgroup reads its rows)
+        switch (kc) {
+#define DYRA_GQF(KC)                                                                                                 \
+    case KC:                                                                                                         \
+        hipLaunchKernelGGL((gram_chol_kernel<KC, false, true>), g1, dim3(NT), 0, st, T, ldt, off, n, kc_real, lambda,  \
+                           Ct, Gw, flags, Cout);                                                                     \
+        return hipGetLastError();
+            DYRA_GQF(16) DYRA_GQF(32) DYRA_GQF(48) DYRA_GQF(64)
+#undef DYRA_GQF
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (kc) {
 #define DYRA_GQ(KC)                                                                                                  \
     case KC:                                                                                                         \
