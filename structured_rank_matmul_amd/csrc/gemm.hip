@@ -533,9 +533,12 @@ bool pick_shape(int64_t M, int64_t N, int gcols, Shape &best) {
     best = Shape::T64x64;
     const bool fits64 = gcols <= 0 || gcols % 64 == 0;
     if (N <= 64) return fits64;
+    // 64 x 64 tiles only win where the whole product is a round or less of
+    // them (a single instance of a few hundred tokens): there a large tile
+    // leaves all but a few CUs idle and its K loop is the whole time
     struct C { Shape s; int bm, bn; double w; } cands[] = {
         {Shape::T256x256, 256, 256, 1.0}, {Shape::T256x160, 256, 160, 1.2}, {Shape::T256x128, 256, 128, 1.16},
-        {Shape::T128x128, 128, 128, 1.3}};
+        {Shape::T128x128, 128, 128, 1.3}, {Shape::T64x64, 64, 64, 2.5}};
     best = Shape::T128x128;
     double best_cost = 1e300;
     bool found = false;
