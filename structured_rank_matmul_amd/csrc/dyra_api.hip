@@ -188,7 +188,7 @@ Layout workspace_layout(const dyra_plan *p, int64_t B, int64_t n) {
         }
     } else if (path_for(p, n) == Path::Dual) {
         L.dual = off;
-        off += align_up(dyra::decode_workspace_bytes(B, n, p->c1, p->kw, p->kc));
+        off += align_up(dyra::decode_workspace_bytes(B, n, p->c1, p->c2, p->kw, p->kc));
     }
     L.total = off;
     return L;

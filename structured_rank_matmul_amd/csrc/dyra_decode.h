@@ -30,13 +30,14 @@ template <typename E> struct DecodeArgs {
     float alpha;      // weight of the correction term (1 in Eq. 6)
 };
 
-size_t decode_workspace_bytes(int64_t B, int64_t n, int64_t c1, int kw, int kc);
+size_t decode_workspace_bytes(int64_t B, int64_t n, int64_t c1, int64_t c2, int kw, int kc);
 
 // T = X [A_s | P_L]^T as float32 partial sums over splits of c1.
 template <typename E> hipError_t launch_decode_project(const DecodeArgs<E> &a, hipStream_t st);
 // Sums the partials into T and forms C_b per instance.
 template <typename E> hipError_t launch_decode_coef(const DecodeArgs<E> &a, hipStream_t st);
-// Y = T_s V_s^T + bias + alpha blockdiag(C_b) (X W_res), streaming W_res and V_s once.
+// Y = T_s V_s^T + bias + alpha blockdiag(C_b) (X W_res), streaming W_res and V_s once:
+// X W_res in split-K parts first (decode_z_kernel), then the rest in one pass.
 template <typename E> hipError_t launch_decode_output(const DecodeArgs<E> &a, hipStream_t st);
 
 }  // namespace dyra

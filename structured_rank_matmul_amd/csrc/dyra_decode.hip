@@ -4,8 +4,10 @@
 // DNNs", Algorithm 1 Inference lines 10-13 and Eq. 5-7, evaluated through the
 // push-through identity so that it stays defined when an instance has fewer
 // tokens than the correction rank (token-by-token decode).  These shapes are
-// bound by HBM: W_res and V_s are streamed once per call, 32 output columns
-// per workgroup, and the small operands (X, T) are re-read from L2.
+// bound by HBM: W_res and V_s are streamed once per call (W_res by
+// decode_z_kernel in split-K parts of 64 output columns, V_s by
+// decode_output_kernel, 32 columns per workgroup), and the small operands
+// (X, T) are re-read from L2.
 #include "dyra_decode.h"
 
 #include <algorithm>
@@ -30,16 +32,29 @@ int decode_splits(int64_t c1) {
 
 int64_t rows_per_block(int64_t n) { return (kRowBlock / n) * n; }
 
+// Split-K parts of the W_res stream (decode_z_kernel): enough 64-column
+// workgroups to cover the compute units about twice, each wavefront's share
+// of a split at least 128 deep and a whole number of 16-deep steps.
+constexpr int kZCols = 64;         // output columns per decode_z workgroup
+constexpr int kZTargetBlocks = 512;
+int z_splits(int64_t c1, int64_t c2) {
+    const int64_t cb = (c2 + kZCols - 1) / kZCols;
+    int s = 1;
+    while (s < 16 && cb * 2 * s <= kZTargetBlocks && c1 % (64 * 2 * s) == 0 && c1 / (2 * s) >= 512) s *= 2;
+    return s;
+}
+
 struct DualLayout {
-    size_t partial, T, coef, total;
-    int splits;
+    size_t partial, T, coef, zpart, total;
+    int splits, zsplits;
 };
 
-DualLayout dual_layout(int64_t B, int64_t n, int64_t c1, int kw, int kc) {
+DualLayout dual_layout(int64_t B, int64_t n, int64_t c1, int64_t c2, int kw, int kc) {
     DualLayout L{};
     const int64_t N = B * n;
     const int64_t K1 = kw + kc;
     L.splits = decode_splits(c1);
+    L.zsplits = z_splits(c1, c2);
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
     size_t off = 0;
     L.partial = off;
@@ -48,6 +63,8 @@ DualLayout dual_layout(int64_t B, int64_t n, int64_t c1, int kw, int kc) {
     off += al(sizeof(float) * (size_t)N * K1);
     L.coef = off;
     off += al(sizeof(float) * (size_t)B * n * n);
+    L.zpart = off;
+    off += al(sizeof(float) * (size_t)L.zsplits * N * c2);
     L.total = off;
     return L;
 }
@@ -386,21 +403,128 @@ __global__ __launch_bounds__(NT) void decode_coef_wide_kernel(const float *__res
     if (tid == 0) flags[b] = 0;
 }
 
-// Y[rows][col0..col0+32) = T_s V_s^T + bias + alpha blockdiag(C_b) (X W_res)
-// (§2.4's fused output with bias and correction weight alpha).  Grid (c2/32,
-// row blocks of whole instances).  Each wavefront takes a contiguous quarter of
-// both contractions (measured 11-15 % faster per decode step than dealing the
-// 16-deep steps round-robin, whose loads touch 32 bytes of 32 lines each), and
-// the quarters are reduced in LDS.
+// Z = X W_res in split-K parts: Zp[s][row][col] = sum over the s-th of S
+// equal splits of c1 of X[row][k] W_res[k][col] (W_res stored transposed,
+// [c2][c1]).  Grid (c2 / 64, S, row blocks of 64).  Each wavefront streams a
+// contiguous quarter of the split for all 64 columns of the block and every
+// row of it: its W_res loads cover whole 128-byte lines, and the small X
+// operand is read from L2 once per 64 output columns.  The wavefronts'
+// partial sums meet in LDS.  Bound by the single pass over W_res (HBM); the
+// split keeps every compute unit streaming when c2 is narrow (the down
+// projection).
 template <typename E, bool TWO>
-__global__ __launch_bounds__(NT) void decode_output_kernel(const E *__restrict__ X, const float *__restrict__ T,
+__global__ __launch_bounds__(NT) void decode_z_kernel(const E *__restrict__ X, const E *__restrict__ Wres_t,
+                                                      int64_t N, int64_t c1, int64_t c2, int splits,
+                                                      float *__restrict__ Zp) {
+    __shared__ float red[2][kRowBlock * kZCols];  // two wavefronts' partials [row][col]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 31, lk = (lane >> 5) * 8;
+    const int64_t col0 = (int64_t)blockIdx.x * kZCols;
+    const int s = blockIdx.y;
+    const int64_t row0 = (int64_t)blockIdx.z * kRowBlock;
+    typedef typename Frag<E>::type F;
+    const int64_t c0 = col0 + lr, c1b = col0 + 32 + lr;
+    const bool c0_ok = c0 < c2, c1_ok = c1b < c2;
+    const int64_t ra = row0 + lr, rb = row0 + 32 + lr;
+    const bool a_ok = ra < N, b_ok = rb < N;
+    const E *pb0 = Wres_t + (c0_ok ? c0 : 0) * c1 + lk, *pb1 = Wres_t + (c1_ok ? c1b : 0) * c1 + lk;
+    const E *pa0 = X + (a_ok ? ra : row0) * c1 + lk, *pa1 = X + (b_ok ? rb : row0) * c1 + lk;
+    // this wavefront's contiguous quarter of split s (whole 16-deep steps)
+    const int64_t ks = c1 / splits, kbeg = (int64_t)s * ks;
+    const int64_t q4 = ((ks + 63) / 64) * 16;
+    const int64_t kb = kbeg + (wave * q4 < ks ? wave * q4 : ks);
+    const int64_t ke = kbeg + ((wave + 1) * q4 < ks ? (wave + 1) * q4 : ks);
+    f32x16 z00 = f32x16{}, z01 = f32x16{}, z10 = f32x16{}, z11 = f32x16{};
+    // two register sets: the next batch's loads are requested before the
+    // current batch's MFMAs; loads are unconditional (steps past ke reread
+    // kbeg) and zeroed at the MFMA
+    constexpr int U = kUnrollRes;
+    auto load = [&](int64_t k0, F (&b0)[U], F (&b1)[U], F (&a0)[U], F (&a1)[U]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t k = k0 + 16 * u;
+            const int64_t kk = k < ke ? k : kbeg;
+            b0[u] = ld_frag(pb0 + kk);
+            b1[u] = ld_frag(pb1 + kk);
+            a0[u] = ld_frag(pa0 + kk);
+            if constexpr (TWO) a1[u] = ld_frag(pa1 + kk);
+        }
+    };
+    auto mma = [&](int64_t k0, const F (&b0)[U], const F (&b1)[U], const F (&a0)[U], const F (&a1)[U])
+                   __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool kin = k0 + 16 * u < ke;
+            const F x0 = keep_if(kin && a_ok, a0[u]);
+            const F w0 = keep_if(c0_ok, b0[u]), w1 = keep_if(c1_ok, b1[u]);
+            z00 = mma16(z00, x0, w0);
+            z01 = mma16(z01, x0, w1);
+            if constexpr (TWO) {
+                const F x1 = keep_if(kin && b_ok, a1[u]);
+                z10 = mma16(z10, x1, w0);
+                z11 = mma16(z11, x1, w1);
+            }
+        }
+    };
+    {
+        F sb0[U], sb1[U], sa0[U], sa1[U], tb0[U], tb1[U], ta0[U], ta1[U];
+        constexpr int64_t BS = 16 * U;  // K advance of one batch
+        int64_t k0 = kb;
+        load(k0, sb0, sb1, sa0, sa1);
+        __builtin_amdgcn_sched_barrier(0);
+        for (; k0 < ke; k0 += 2 * BS) {
+            load(k0 + BS, tb0, tb1, ta0, ta1);
+            mma(k0, sb0, sb1, sa0, sa1);
+            __builtin_amdgcn_sched_barrier(0);
+            load(k0 + 2 * BS, sb0, sb1, sa0, sa1);
+            mma(k0 + BS, tb0, tb1, ta0, ta1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // wavefronts 0 and 1 write their sums, 2 and 3 add theirs, then the two
+    // buffers are summed on the way out
+    auto put = [&](float *buf, bool add) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int r = acc_row(lane, t);
+            float *p00 = buf + r * kZCols + lr, *p01 = p00 + 32;
+            float *p10 = buf + (32 + r) * kZCols + lr, *p11 = p10 + 32;
+            *p00 = add ? *p00 + z00[t] : z00[t];
+            *p01 = add ? *p01 + z01[t] : z01[t];
+            if constexpr (TWO) {
+                *p10 = add ? *p10 + z10[t] : z10[t];
+                *p11 = add ? *p11 + z11[t] : z11[t];
+            }
+        }
+    };
+    if (wave < 2) put(red[wave], false);
+    __syncthreads();
+    if (wave >= 2) put(red[wave - 2], true);
+    __syncthreads();
+    const int rows = TWO ? kRowBlock : 32;
+    for (int e = tid; e < rows * kZCols; e += NT) {
+        const int r = e / kZCols, c = e % kZCols;
+        if (row0 + r < N && col0 + c < c2) Zp[((int64_t)s * N + row0 + r) * c2 + col0 + c] = red[0][e] + red[1][e];
+    }
+}
+
+// Y[rows][col0..col0+32) = T_s V_s^T + bias + alpha blockdiag(C_b) Z with
+// Z = X W_res summed over decode_z_kernel's splits (§2.4's fused output with
+// bias and correction weight alpha).  Grid (c2/32, row blocks of whole
+// instances).  Each wavefront takes a contiguous quarter of the V_s
+// contraction (measured 11-15 % faster per decode step than dealing the
+// 16-deep steps round-robin, whose loads touch 32 bytes of 32 lines each),
+// and the quarters are reduced in LDS.
+template <typename E, bool TWO>
+__global__ __launch_bounds__(NT) void decode_output_kernel(const float *__restrict__ Zp, int zsplits,
+                                                           const float *__restrict__ T,
                                                            const float *__restrict__ coef,
-                                                           const E *__restrict__ Vs, const E *__restrict__ Wres_t,
-                                                           int64_t N, int64_t n, int64_t c1, int64_t c2, int K1,
-                                                           int kw, int64_t rows_blk, const E *__restrict__ bias,
-                                                           float alpha, E *__restrict__ Y) {
+                                                           const E *__restrict__ Vs, int64_t N, int64_t n,
+                                                           int64_t c2, int K1, int kw, int64_t rows_blk,
+                                                           const E *__restrict__ bias, float alpha,
+                                                           E *__restrict__ Y) {
     __shared__ float part[NT / 64][kRowBlock * 32];  // each wavefront's partial [row][col]
-    __shared__ float Zs[kRowBlock][33];              // X W_res of the block, summed
+    __shared__ float Zs[kRowBlock][33];              // Z of the block's rows
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 31, lk = (lane >> 5) * 8;
     const int64_t col0 = (int64_t)blockIdx.x * 32;
@@ -411,55 +535,17 @@ __global__ __launch_bounds__(NT) void decode_output_kernel(const E *__restrict__
     const bool col_ok = col < c2;
     const int64_t ra = row0 + lr, rb = row0 + 32 + lr;
     const bool a_ok = ra < row_end, b_ok = rb < row_end;
-    f32x16 z0 = f32x16{}, z1 = f32x16{}, s0 = f32x16{}, s1 = f32x16{};
-    // both contractions request kUnroll steps' loads of the streamed W_res /
-    // V_s columns before their MFMAs
-    const int64_t colc = col_ok ? col : 0, rac = a_ok ? ra : row0, rbc = b_ok ? rb : row0;
-    {
-        // W_res is the long stream: two register sets, the next batch's loads
-        // requested before the current batch's MFMAs.  Loads are unconditional
-        // (steps past c1 reread step 0); the zeroing happens at the MFMA, so a
-        // batch's data is waited for only there.
-        constexpr int U = kUnrollRes;
-        const E *pb = Wres_t + colc * c1 + lk, *pa0 = X + rac * c1 + lk, *pa1 = X + rbc * c1 + lk;
-        // each wavefront streams its own contiguous quarter of c1
-        const int64_t q4 = ((c1 + 63) / 64) * 16;
-        const int64_t kb = wave * q4 < c1 ? wave * q4 : c1;
-        const int64_t ke = (wave + 1) * q4 < c1 ? (wave + 1) * q4 : c1;
-        auto load = [&](int64_t k0, F (&fb)[U], F (&fa0)[U], F (&fa1)[U]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t k = k0 + 16 * u;
-                const int64_t kk = k < ke ? k : 0;
-                fb[u] = ld_frag(pb + kk);
-                fa0[u] = ld_frag(pa0 + kk);
-                if constexpr (TWO) fa1[u] = ld_frag(pa1 + kk);
-            }
-        };
-        auto mma = [&](int64_t k0, const F (&fb)[U], const F (&fa0)[U], const F (&fa1)[U])
-                       __attribute__((always_inline)) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const bool kin = k0 + 16 * u < ke;
-                const F b = keep_if(kin && col_ok, fb[u]);
-                z0 = mma16(z0, keep_if(a_ok, fa0[u]), b);
-                if constexpr (TWO) z1 = mma16(z1, keep_if(b_ok, fa1[u]), b);
-            }
-        };
-        F ab[U], a0[U], a1[U], bb[U], b0[U], b1[U];
-        constexpr int64_t BS = 16 * U;  // K advance of one batch
-        int64_t k0 = kb;
-        load(k0, ab, a0, a1);
-        __builtin_amdgcn_sched_barrier(0);
-        for (; k0 < ke; k0 += 2 * BS) {
-            load(k0 + BS, bb, b0, b1);
-            mma(k0, ab, a0, a1);
-            __builtin_amdgcn_sched_barrier(0);
-            load(k0 + 2 * BS, ab, a0, a1);
-            mma(k0 + BS, bb, b0, b1);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+    // Z of the block, summed over the splits (read before the V_s stream so
+    // that its latency hides behind it)
+    for (int e = tid; e < kRowBlock * 32; e += NT) {
+        const int r = e >> 5, c = e & 31;
+        float z = 0.f;
+        if (row0 + r < row_end && col0 + c < c2)
+            for (int q = 0; q < zsplits; ++q) z += Zp[((int64_t)q * N + row0 + r) * c2 + col0 + c];
+        Zs[r][c] = z;
     }
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    const int64_t colc = col_ok ? col : 0, rac = a_ok ? ra : row0, rbc = b_ok ? rb : row0;
     {
         const E *pb = Vs + colc * kw + lk;
         const float *pa0 = T + rac * K1 + lk, *pa1 = T + rbc * K1 + lk;
@@ -483,22 +569,6 @@ __global__ __launch_bounds__(NT) void decode_output_kernel(const E *__restrict__
             }
         }
     }
-    // Z = X W_res summed over the wavefronts' steps into Zs
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-        const int r = acc_row(lane, t);
-        part[wave][r * 32 + lr] = z0[t];
-        part[wave][(32 + r) * 32 + lr] = z1[t];
-    }
-    __syncthreads();
-    for (int e = tid; e < kRowBlock * 32; e += NT) {
-        float v = 0.f;
-#pragma unroll
-        for (int w = 0; w < NT / 64; ++w) v += part[w][e];
-        Zs[e >> 5][e & 31] = v;
-    }
-    __syncthreads();
-    // S = T_s V_s^T partials in the same buffer (its Z reads are done)
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
         const int r = acc_row(lane, t);
@@ -527,12 +597,12 @@ __global__ __launch_bounds__(NT) void decode_output_kernel(const E *__restrict__
 
 }  // namespace
 
-size_t decode_workspace_bytes(int64_t B, int64_t n, int64_t c1, int kw, int kc) {
-    return dual_layout(B, n, c1, kw, kc).total;
+size_t decode_workspace_bytes(int64_t B, int64_t n, int64_t c1, int64_t c2, int kw, int kc) {
+    return dual_layout(B, n, c1, c2, kw, kc).total;
 }
 
 template <typename E> hipError_t launch_decode_project(const DecodeArgs<E> &a, hipStream_t st) {
-    const DualLayout L = dual_layout(a.B, a.n, a.c1, a.kw, a.kc);
+    const DualLayout L = dual_layout(a.B, a.n, a.c1, a.c2, a.kw, a.kc);
     const int64_t N = a.B * a.n;
     const int K1 = a.kw + a.kc;
     dim3 grid((unsigned)((K1 + 31) / 32), (unsigned)L.splits, (unsigned)((N + kRowBlock - 1) / kRowBlock));
@@ -546,7 +616,7 @@ template <typename E> hipError_t launch_decode_project(const DecodeArgs<E> &a, h
 }
 
 template <typename E> hipError_t launch_decode_coef(const DecodeArgs<E> &a, hipStream_t st) {
-    const DualLayout L = dual_layout(a.B, a.n, a.c1, a.kw, a.kc);
+    const DualLayout L = dual_layout(a.B, a.n, a.c1, a.c2, a.kw, a.kc);
     const int64_t N = a.B * a.n;
     if (a.n > 16) {
         if (a.n > kWideTokens || a.lambda != 0.f || a.kc > kMaxCorr) return hipErrorInvalidValue;
@@ -562,19 +632,31 @@ template <typename E> hipError_t launch_decode_coef(const DecodeArgs<E> &a, hipS
 }
 
 template <typename E> hipError_t launch_decode_output(const DecodeArgs<E> &a, hipStream_t st) {
-    const DualLayout L = dual_layout(a.B, a.n, a.c1, a.kw, a.kc);
+    const DualLayout L = dual_layout(a.B, a.n, a.c1, a.c2, a.kw, a.kc);
     const int64_t N = a.B * a.n;
+    float *const Zp = (float *)(a.ws + L.zpart);
+    // Z = X W_res by splits; the second 32-row MFMA block only when N needs it
+    const dim3 zgrid((unsigned)((a.c2 + kZCols - 1) / kZCols), (unsigned)L.zsplits,
+                     (unsigned)((N + kRowBlock - 1) / kRowBlock));
+    if (N > 32)
+        hipLaunchKernelGGL((decode_z_kernel<E, true>), zgrid, dim3(NT), 0, st, a.X, a.Wres_t, N, a.c1, a.c2,
+                           L.zsplits, Zp);
+    else
+        hipLaunchKernelGGL((decode_z_kernel<E, false>), zgrid, dim3(NT), 0, st, a.X, a.Wres_t, N, a.c1, a.c2,
+                           L.zsplits, Zp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     const int64_t rb = rows_per_block(a.n);
     dim3 grid((unsigned)((a.c2 + 31) / 32), (unsigned)((N + rb - 1) / rb));
     // the second 32-row MFMA block only when some row block has rows there
     if (std::min<int64_t>(rb, N) > 32)
-        hipLaunchKernelGGL((decode_output_kernel<E, true>), grid, dim3(NT), 0, st, a.X,
-                           (const float *)(a.ws + L.T), (const float *)(a.ws + L.coef), a.Vs, a.Wres_t, N, a.n,
-                           a.c1, a.c2, a.kw + a.kc, a.kw, rb, a.bias, a.alpha, a.Y);
+        hipLaunchKernelGGL((decode_output_kernel<E, true>), grid, dim3(NT), 0, st, (const float *)Zp, L.zsplits,
+                           (const float *)(a.ws + L.T), (const float *)(a.ws + L.coef), a.Vs, N, a.n, a.c2,
+                           a.kw + a.kc, a.kw, rb, a.bias, a.alpha, a.Y);
     else
-        hipLaunchKernelGGL((decode_output_kernel<E, false>), grid, dim3(NT), 0, st, a.X,
-                           (const float *)(a.ws + L.T), (const float *)(a.ws + L.coef), a.Vs, a.Wres_t, N, a.n,
-                           a.c1, a.c2, a.kw + a.kc, a.kw, rb, a.bias, a.alpha, a.Y);
+        hipLaunchKernelGGL((decode_output_kernel<E, false>), grid, dim3(NT), 0, st, (const float *)Zp, L.zsplits,
+                           (const float *)(a.ws + L.T), (const float *)(a.ws + L.coef), a.Vs, N, a.n, a.c2,
+                           a.kw + a.kc, a.kw, rb, a.bias, a.alpha, a.Y);
     return hipGetLastError();
 }
 

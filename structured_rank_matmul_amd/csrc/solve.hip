@@ -126,10 +126,15 @@ template <int KC> constexpr int gram_tokens() { return gram_kp<KC>() <= 64 ? 256
 // another one rewrites.
 // GONLY: stop after G, written whole (both triangles) to Gw for the
 // Newton-Schulz solve.
-// FUSE (n <= 256, KC <= 64): the instance's tokens are one chunk, still in LDS
-// after G, so the workgroup also forms Q = L1 C^-T (a token per thread,
-// forward substitution against C kept row-major in LDS) and writes it over
-// L1: one launch instead of two, and no other workgroup reads these rows.
+// FUSE (n <= 256, KC <= 64): no other workgroup reads the instance's rows,
+// so the workgroup also forms Q = L1 C^-T and writes it over L1: one launch
+// instead of two.  C^-1 comes out of the elimination itself: wavefront 0's
+// lanes 32..63, idle as pivot rows, carry identity rows through each 32-wide
+// panel and leave the rows of the diagonal block's C_pp^-T; with two panels
+// the block below the diagonal of C^-1 is -C_11^-1 C_10 C_00^-1.  Then
+// Q^T = C^-1 L1^T on MFMA, C^-1 split into two bf16 terms (high part and
+// rounding remainder) against the exact bf16 L1 rows, each wavefront taking
+// 64 tokens.
 template <int KC, bool GONLY = false, bool FUSE = false>
 __global__ __launch_bounds__(NT) void gram_chol_kernel(const bf16 *T, int64_t ldt, int64_t off,
                                                        int64_t n, int kc_real, float lambda, float *__restrict__ Ct,
@@ -153,9 +158,13 @@ __global__ __launch_bounds__(NT) void gram_chol_kernel(const bf16 *T, int64_t ld
     __shared__ __align__(16) float Cb[(KP > 32 ? KP - 32 : 1) * CBS];
     // FUSE: C row-major (Cs[i][m] = C[i][m] below the diagonal, 1 / C[i][i] on
     // it) for the in-kernel substitution
-    static_assert(!FUSE || (KP <= 64 && TT >= NT && !GONLY), "fused Q: one token chunk, one token per thread");
+    static_assert(!FUSE || (KP <= 64 && TT >= NT && !GONLY), "fused Q: one token chunk, 64 tokens per wavefront");
     constexpr int CSS = KP + 4;
     __shared__ __align__(16) float Cs[FUSE ? KP * CSS : 4];
+    // FUSE: C^-1 row-major (Ci[j][m]; its upper-right 32 x 32 block is never
+    // written nor read) and, with two panels, C_10 C_00^-1
+    __shared__ __align__(16) float Ci[FUSE ? KP * CSS : 4];
+    __shared__ float Pm[FUSE && KP == 64 ? 32 * 33 : 1];
     __shared__ float sh_dmax;
     __shared__ int sh_fail;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -264,13 +273,16 @@ __global__ __launch_bounds__(NT) void gram_chol_kernel(const bf16 *T, int64_t ld
             const int rg = p0 + (lane < 32 ? lane : 0);
             const int rl = p0 + 32 + 64 * wave + lane;
             const bool lin = rl < KP;
+            // FUSE: wavefront 0's lanes 32..63 hold identity rows (data rows
+            // that the elimination turns into rows of C_pp^-T)
+            const bool idrow = FUSE && wave == 0 && lane >= 32;
 #pragma unroll
             for (int m = 0; m < 32; m += 4) {
                 const f32x4 x = *reinterpret_cast<const f32x4 *>(&G[rg * GS + p0 + m]);
                 const f32x4 y = *reinterpret_cast<const f32x4 *>(&G[(lin ? rl : rg) * GS + p0 + m]);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    g[m + u] = lane < 32 ? x[u] : 0.f;
+                    g[m + u] = lane < 32 ? x[u] : (idrow && m + u == lane - 32 ? 1.f : 0.f);
                     l[m + u] = lin ? y[u] : 0.f;
                 }
             }
@@ -291,6 +303,12 @@ __global__ __launch_bounds__(NT) void gram_chol_kernel(const bf16 *T, int64_t ld
                         if (Cout && m <= lane) Cout[(b * KC + i) * KC + p0 + m] = (double)g[m];
                     }
                 }
+            }
+            if (idrow) {
+                // lane 32 + i holds row i of C_pp^-T: column i of C_pp^-1
+                const int i = lane - 32;
+#pragma unroll
+                for (int m = 0; m < 32; ++m) Ci[(p0 + m) * CSS + p0 + i] = g[m];
             }
             if (has_l && lin) {
                 if (rl < KC) {
@@ -326,45 +344,96 @@ __global__ __launch_bounds__(NT) void gram_chol_kernel(const bf16 *T, int64_t ld
     }
     if (tid == 0) flags[b] = fail ? 1 : 0;
     if constexpr (FUSE) {
-        // Q = L1 C^-T by forward substitution, one token per thread: the
-        // instance's L1 is still in LDS (one chunk, transposed) and C in Cs;
-        // every thread reads the same row of C at a time (LDS broadcasts)
         if (tid == 0) sh_fail = fail ? 1 : 0;
         __syncthreads();
+        if constexpr (KP == 64) {
+            // lower-left block of C^-1: -C_11^-1 (C_10 C_00^-1).  Thread tid
+            // takes column m = tid % 32 of rows i = tid / 32 + 8 u; the
+            // diagonal blocks of Ci hold their zeros above the diagonal, so
+            // the sums run over all 32 terms, fully unrolled (LDS reads in
+            // batches, not one latency per term)
+            const int m = tid & 31, i0 = tid >> 5;
+            float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < 32; ++k) {
+                const float c = Ci[k * CSS + m];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) a[u] = fmaf(Cs[(32 + i0 + 8 * u) * CSS + k], c, a[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) Pm[(i0 + 8 * u) * 33 + m] = a[u];
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < 4; ++u) a[u] = 0.f;
+#pragma unroll
+            for (int k = 0; k < 32; ++k) {
+                const float pk = Pm[k * 33 + m];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) a[u] = fmaf(Ci[(32 + i0 + 8 * u) * CSS + 32 + k], pk, a[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) Ci[(32 + i0 + 8 * u) * CSS + m] = -a[u];
+            __syncthreads();
+        }
         const bool dead = sh_fail != 0;
-        const int t = tid;
-        if (t < n) {
-            float q[KC];
+        // Q^T = C^-1 L1^T: wavefront w takes tokens 64 w .. 64 w + 63 (two
+        // 32-token blocks), the L1 rows as stored (8 consecutive features of a
+        // token per lane: an MFMA fragment as is)
+        constexpr int NJB = KP / 32;
+        f32x16 acc[NJB][2];
 #pragma unroll
-            for (int m = 0; m < KC; ++m) q[m] = (float)Lt[m * ST + t];
-            // row by row: q_i = (l_i - sum_{m < i} C[i][m] q_m) / C[i][i], row i
-            // of C read as 16-byte broadcasts, two partial sums
-            unroll_seq<KC>([&](auto I) __attribute__((always_inline)) {
-                constexpr int i = decltype(I)::value;
-                float s0 = q[i], s1 = 0.f;
-                const float *ci = Cs + i * CSS;
+        for (int jb = 0; jb < NJB; ++jb) acc[jb][0] = acc[jb][1] = f32x16{};
+        const bf16 *lrow[2];
+        bool tok[2];
 #pragma unroll
-                for (int m0 = 0; m0 < i; m0 += 4) {
-                    const f32x4 c4 = *reinterpret_cast<const f32x4 *>(ci + m0);
+        for (int tb = 0; tb < 2; ++tb) {
+            const int64_t t = 64 * wave + 32 * tb + lr;
+            tok[tb] = t < n;
+            lrow[tb] = Tb + (tok[tb] ? t : 0) * ldt;
+        }
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        if (m0 + u < i) {
-                            if (u & 1) s1 = fmaf(-c4[u], q[m0 + u], s1);
-                            else s0 = fmaf(-c4[u], q[m0 + u], s0);
-                        }
-                    }
+        for (int ks = 0; ks < KP / 16; ++ks) {
+            const int m0 = ks * 16 + lk;
+            bf16x8 bl[2];
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) bl[tb] = (tok[tb] && m0 < KC) ? ld_frag(lrow[tb] + m0) : bf16x8{};
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) {
+                if (NJB == 2 && jb == 0 && ks >= 2) continue;  // C^-1 is lower triangular
+                const float *cr = Ci + (jb * 32 + lr) * CSS + m0;
+                const f32x4 v0 = *reinterpret_cast<const f32x4 *>(cr);
+                const f32x4 v1 = *reinterpret_cast<const f32x4 *>(cr + 4);
+                bf16x8 hi, lo;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float v = e < 4 ? v0[e] : v1[e - 4];
+                    hi[e] = (bf16)v;
+                    lo[e] = (bf16)(v - (float)hi[e]);
                 }
-                q[i] = (s0 + s1) * ci[i];
-            });
-            bf16 *dst = const_cast<bf16 *>(Tb) + (int64_t)t * ldt;
 #pragma unroll
-            for (int v = 0; v < KC / 8; ++v) {
-                union { u32x4 u; bf16 h[8]; } w;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) w.h[e] = dead ? bf16(0.f) : (bf16)q[8 * v + e];
-                *reinterpret_cast<u32x4 *>(dst + 8 * v) = w.u;
+                for (int tb = 0; tb < 2; ++tb) {
+                    acc[jb][tb] = mma16(acc[jb][tb], hi, bl[tb]);
+                    acc[jb][tb] = mma16(acc[jb][tb], lo, bl[tb]);
+                }
             }
         }
+        // lane: token lr of the block, four consecutive features per group
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                if (!tok[tb]) continue;
+                bf16 *dst = const_cast<bf16 *>(lrow[tb]);
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int j0 = jb * 32 + acc_row(lane, 4 * g4);
+                    if (j0 >= KC) continue;
+                    union { uint2 u; bf16 h[4]; } w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w.h[e] = dead ? bf16(0.f) : (bf16)acc[jb][tb][4 * g4 + e];
+                    *reinterpret_cast<uint2 *>(dst + j0) = w.u;
+                }
+            }
     }
 }
 
@@ -462,6 +531,222 @@ __global__ __launch_bounds__(64 * token_lanes<KC>()) void q_apply_kernel(bf16 *_
 }
 
 // ------------------------------------------------------------- float32 path
+// Correction ranks 16 and 32 (KP = kc): one workgroup per instance, every
+// step that decides Q_b in float64, none of it serial beyond the k pivots.
+//  1. G = L1_b^T L1_b: token chunks of 256 rows staged in LDS as stored;
+//     thread tid owns the entries tid + 256 u of G (row-major), summing their
+//     products over the chunk (a product of two float32 values is exact in
+//     float64).
+//  2. Cholesky G + lambda I = C C^T, right-looking: column m of the trailing
+//     matrix goes through LDS, one barrier per column.
+//  3. Q_b = L1_b C^-T by forward substitution, one token per thread, the
+//     rows of C read from LDS (one address per wavefront: broadcasts);
+//     written in place over L1_b and, transposed, into Qt (zero for tokens
+//     n..npad-1).
+template <int KP>
+__global__ __launch_bounds__(NT) void gram_q_f32_small_kernel(float *__restrict__ T, int64_t ldt, int64_t off,
+                                                              int64_t n, int64_t npad, int kc_real, float lambda,
+                                                              float *__restrict__ Qt, int *__restrict__ flags,
+                                                              double *__restrict__ Cout) {
+    static_assert(KP == 16 || KP == 32, "correction rank");
+    constexpr int TC = 256;            // tokens per staged chunk
+    constexpr int EPT = KP * KP / NT;  // entries of G per thread
+    constexpr int V4 = KP / 4;         // 16-byte pieces of a token row
+    __shared__ __align__(16) float Ls[TC * KP];
+    __shared__ double Cs[KP][KP + 1];  // C, its diagonal replaced by 1 / C[i][i]
+    __shared__ double colv[2][KP];
+    __shared__ double diag[KP];
+    __shared__ double sh_th;
+    __shared__ int sh_fail;
+    const int tid = threadIdx.x;
+    const int64_t b = blockIdx.x;
+    float *const Lb = T + b * n * ldt + off;
+    const int j = tid % KP;
+    int iu[EPT];
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) iu[u] = (tid + NT * u) / KP;
+    double g[EPT], g2[EPT];
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) g[u] = g2[u] = 0.0;
+    if (tid == 0) sh_fail = 0;
+
+    // ---- 1. G
+    for (int64_t t0 = 0; t0 < n; t0 += TC) {
+        __syncthreads();  // the previous chunk's reads are done
+        for (int e = tid; e < TC * V4; e += NT) {
+            const int tok = e / V4, q = e % V4;
+            const bool ok = t0 + tok < n;
+            f32x4 v = *reinterpret_cast<const f32x4 *>(Lb + (ok ? t0 + tok : n - 1) * ldt + 4 * q);
+            if (!ok) v = f32x4{0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<f32x4 *>(&Ls[tok * KP + 4 * q]) = v;
+        }
+        __syncthreads();
+        // tokens past n were staged as zeros: whole groups of 8, two sums per
+        // entry, so that LDS reads are batched and the float64 FMAs of
+        // consecutive tokens do not wait on each other
+        const int tc = (int)(n - t0 < TC ? n - t0 : TC);
+        for (int t = 0; t < tc; t += 8) {
+#pragma unroll
+            for (int h = 0; h < 8; ++h) {
+                const float *row = Ls + (t + h) * KP;
+                const double lj = (double)row[j];
+#pragma unroll
+                for (int u = 0; u < EPT; ++u) {
+                    if (h & 1) g2[u] = fma((double)row[iu[u]], lj, g2[u]);
+                    else g[u] = fma((double)row[iu[u]], lj, g[u]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) g[u] += g2[u];
+    // lambda on the real diagonal, identity on the padding
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+        const int i = iu[u];
+        if (i < kc_real && j < kc_real) g[u] += (i == j) ? (double)lambda : 0.0;
+        else g[u] = (i == j) ? 1.0 : 0.0;
+        if (i == j) diag[i] = g[u];
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double dmax = 0.0;
+        for (int i = 0; i < kc_real; ++i) dmax = dmax > diag[i] ? dmax : diag[i];
+        // a pivot at or below the working precision times the largest
+        // diagonal marks a numerically singular G (possible only for lambda = 0)
+        sh_th = lambda > 0.f ? 0.0 : (double)KP * 2.3e-16 * dmax;
+        if (!(dmax > 0.0)) sh_fail = 1;
+    }
+    // ---- 2. Cholesky, column m of the trailing matrix broadcast through colv[m & 1]
+    for (int m = 0; m < KP; ++m) {
+        double *cm = colv[m & 1];
+#pragma unroll
+        for (int u = 0; u < EPT; ++u)
+            if (j == m) cm[iu[u]] = g[u];
+        __syncthreads();
+        double pk = cm[m];
+        if (m < kc_real && !(pk > sh_th)) {
+            if (tid == 0) sh_fail = 1;
+            pk = 1.0;
+        }
+        const double d = sqrt(pk), rp = 1.0 / pk;
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            const int i = iu[u];
+            if (j == m && i >= m) g[u] = (i == m) ? d : g[u] / d;    // C[i][m]
+            else if (j > m && i >= j) g[u] -= cm[i] * cm[j] * rp;   // trailing update
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+        const int i = iu[u];
+        if (j > i) g[u] = 0.0;
+        Cs[i][j] = (i == j) ? 1.0 / g[u] : g[u];
+        if (Cout) Cout[(b * KP + i) * KP + j] = g[u];
+    }
+    __syncthreads();
+    const bool dead = sh_fail != 0;
+    if (tid == 0) flags[b] = dead ? 1 : 0;
+
+    // ---- 3. q_t = C^-1 l_t, one token per thread
+    float *const Qb = Qt + b * KP * npad;
+    for (int64_t t = tid; t < npad; t += NT) {
+        double q[KP];
+        const bool in = t < n;
+#pragma unroll
+        for (int v = 0; v < V4; ++v) {
+            f32x4 x = *reinterpret_cast<const f32x4 *>(Lb + (in ? t : n - 1) * ldt + 4 * v);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) q[4 * v + e] = in ? (double)x[e] : 0.0;
+        }
+#pragma unroll
+        for (int i = 0; i < KP; ++i) {
+            double s0 = q[i], s1 = 0.0;
+#pragma unroll
+            for (int c = 0; c < i; ++c) {
+                if (c & 1) s1 = fma(-Cs[i][c], q[c], s1);
+                else s0 = fma(-Cs[i][c], q[c], s0);
+            }
+            q[i] = dead ? 0.0 : (s0 + s1) * Cs[i][i];
+        }
+#pragma unroll
+        for (int i = 0; i < KP; ++i) Qb[i * npad + t] = (float)q[i];
+        if (in) {
+#pragma unroll
+            for (int v = 0; v < V4; ++v)
+                *reinterpret_cast<f32x4 *>(Lb + t * ldt + 4 * v) =
+                    f32x4{(float)q[4 * v], (float)q[4 * v + 1], (float)q[4 * v + 2], (float)q[4 * v + 3]};
+        }
+    }
+}
+
+// M'_b = Q_b^T X_b for float32 at correction ranks 16 and 32: workgroup (64
+// input features, instance b).  Thread (feature f, part p) sums tokens p,
+// p + 4, ... of its feature into all KP rows; per 256-token chunk it requests
+// its 64 entries of X at once (one memory latency per chunk), while Q_b's
+// rows of the chunk are staged token by token in LDS (every lane of a
+// wavefront reads the same token: broadcasts).  The four parts meet in LDS.
+template <int KP>
+__global__ __launch_bounds__(NT) void mprime_f32_small_kernel(const float *__restrict__ X, const float *__restrict__ Qt,
+                                                              int64_t n, int64_t npad, int64_t c1,
+                                                              float *__restrict__ Mp) {
+    static_assert(KP == 16 || KP == 32, "correction rank");
+    constexpr int TC = 256;     // tokens per staged chunk
+    constexpr int TP = TC / (NT / 64);  // tokens of a part per chunk
+    constexpr int QS = KP + 4;  // row stride (floats) of a staged token
+    __shared__ __align__(16) float Qs[TC * QS];
+    __shared__ float red[NT / 64][KP][64];
+    const int tid = threadIdx.x, f = tid & 63, p = tid >> 6;
+    const int64_t b = blockIdx.y;
+    const int64_t col = (int64_t)blockIdx.x * 64 + f;
+    const bool col_ok = col < c1;
+    const float *const Xb = X + b * n * c1 + (col_ok ? col : 0);
+    const float *const Qb = Qt + b * KP * npad;
+    float acc[KP];
+#pragma unroll
+    for (int i = 0; i < KP; ++i) acc[i] = 0.f;
+    for (int64_t t0 = 0; t0 < n; t0 += TC) {
+        // this part's tokens of the chunk (past n: token n - 1, weighted by
+        // the zero rows of Qt or skipped)
+        float x[TP];
+#pragma unroll
+        for (int u = 0; u < TP; ++u) {
+            const int64_t t = t0 + p + (NT / 64) * u;
+            x[u] = Xb[(t < n ? t : n - 1) * c1];
+        }
+        __syncthreads();  // the previous chunk's reads are done
+        for (int e = tid; e < TC * KP; e += NT) {
+            const int i = e / TC, tt = e % TC;  // consecutive threads: consecutive tokens of row i
+            Qs[tt * QS + i] = t0 + tt < npad ? Qb[i * npad + t0 + tt] : 0.f;
+        }
+        __syncthreads();
+        const int tc = (int)(n - t0 < TC ? n - t0 : TC);
+#pragma unroll
+        for (int u = 0; u < TP; ++u) {
+            const int t = p + (NT / 64) * u;
+            if (t >= tc) break;
+            const float *qr = Qs + t * QS;
+#pragma unroll
+            for (int v = 0; v < KP / 4; ++v) {
+                const f32x4 q = *reinterpret_cast<const f32x4 *>(qr + 4 * v);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[4 * v + e] = fmaf(q[e], x[u], acc[4 * v + e]);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < KP; ++i) red[p][i][f] = acc[i];
+    __syncthreads();
+    for (int e = tid; e < KP * 64; e += NT) {
+        const int i = e / 64, ff = e % 64;
+        const int64_t c = (int64_t)blockIdx.x * 64 + ff;
+        float s = 0.f;
+#pragma unroll
+        for (int q = 0; q < NT / 64; ++q) s += red[q][i][ff];
+        if (c < c1) Mp[(b * KP + i) * c1 + c] = s;
+    }
+}
+
 __global__ __launch_bounds__(NT) void gram_q_f32_kernel(float *__restrict__ T, int64_t ldt, int64_t off, int64_t n,
                                                         int64_t npad, int kc_real, int kc, float lambda,
                                                         float *__restrict__ Qt, int *__restrict__ flags,
@@ -911,6 +1196,15 @@ hipError_t launch_gram_q<float>(float *T, int64_t ldt, int64_t off, int64_t B, i
                                 hipStream_t st) {
     if (B <= 0) return hipSuccess;
     if (kc < 1 || kc > 64) return hipErrorInvalidValue;
+    if (kc == 16 || kc == 32) {
+        if (kc == 16)
+            hipLaunchKernelGGL(gram_q_f32_small_kernel<16>, dim3((unsigned)B), dim3(NT), 0, st, T, ldt, off, n, npad,
+                               kc_real, lambda, Qt, flags, Cout);
+        else
+            hipLaunchKernelGGL(gram_q_f32_small_kernel<32>, dim3((unsigned)B), dim3(NT), 0, st, T, ldt, off, n, npad,
+                               kc_real, lambda, Qt, flags, Cout);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(gram_q_f32_kernel, dim3((unsigned)B), dim3(NT), 0, st, T, ldt, off, n, npad, kc_real, kc,
                        lambda, Qt, flags, Cout);
     return hipGetLastError();
@@ -945,6 +1239,14 @@ template <>
 hipError_t launch_mprime<float>(const float *X, const float *, int64_t, int64_t, const float *Qt, int64_t B,
                                 int64_t n, int64_t npad, int64_t c1, int kc, float *Mp, hipStream_t st) {
     if (B <= 0) return hipSuccess;
+    if (kc == 16 || kc == 32) {
+        const dim3 grid((unsigned)((c1 + 63) / 64), (unsigned)B);
+        if (kc == 16)
+            hipLaunchKernelGGL(mprime_f32_small_kernel<16>, grid, dim3(NT), 0, st, X, Qt, n, npad, c1, Mp);
+        else
+            hipLaunchKernelGGL(mprime_f32_small_kernel<32>, grid, dim3(NT), 0, st, X, Qt, n, npad, c1, Mp);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((mprime_kernel<float>), dim3((unsigned)((c1 + 255) / 256), (unsigned)B), dim3(NT), 0, st, X,
                        Qt, n, npad, c1, kc, Mp);
     return hipGetLastError();
