@@ -30,6 +30,11 @@ struct dyra_plan {
     void *Vs;         // [c2][kw]: V_s
     void *Wres_t;     // [c2][c1]: W_res transposed
     void *Wres;       // [c1][c2]: W_res (only with half_steps > 2, for the L updates)
+    // The dual form's streamed operands in MFMA fragment order (frag_tile):
+    // W_res^T and V_s (only for correction ranks above 0 and no BLAST W_hat)
+    void *Wdec;       // tiled [c2][c1]
+    void *Vdec;       // tiled [c2][kw]
+    void *Adec;       // tiled Aext, rows padded with zeros to a multiple of 32
     // BLAST W_hat (Appendix B), nb > 0: kw = nb * rbp, Aext holds P_L alone
     // ([kc][c1]) and Vs is V [c2][rbp]
     int32_t nb;       // blocks per side (0: truncated-SVD W_hat)
@@ -192,6 +197,26 @@ Layout workspace_layout(const dyra_plan *p, int64_t B, int64_t n) {
     }
     L.total = off;
     return L;
+}
+
+// A row-major [rows][K] matrix (rows a multiple of 32, K of 16) in MFMA
+// fragment order: the 32 x 16 block (row block rb, 16-deep step ks) is 512
+// consecutive elements, lane l = 32 h + r of a wavefront holding row
+// 32 rb + r, columns 16 ks + 8 h .. + 7.  Blocks follow each other step by
+// step within a row block, so a wavefront that walks the contraction of one
+// row block reads one contiguous run, 1 KB (bf16) per load instruction,
+// each lane's piece already an MFMA operand.
+std::vector<double> frag_tile(const std::vector<double> &src, int64_t rows, int64_t K) {
+    std::vector<double> dst(src.size());
+    const int64_t steps = K / 16;
+    for (int64_t rb = 0; rb < rows / 32; ++rb)
+        for (int64_t ks = 0; ks < steps; ++ks)
+            for (int l = 0; l < 64; ++l) {
+                const int64_t row = 32 * rb + (l & 31), col = 16 * ks + 8 * (l >> 5);
+                double *d = &dst[(size_t)(((rb * steps + ks) * 64 + l) * 8)];
+                for (int e = 0; e < 8; ++e) d[e] = src[(size_t)(row * K + col + e)];
+            }
+    return dst;
 }
 
 // A device copy of `src` rounded to `dtype` (round to nearest even); the
@@ -384,7 +409,8 @@ dyra_status run_forward(const E *X, int64_t B, int64_t n, const dyra_plan *p, co
         }
         if ((s = mark()) != DYRA_OK) return s;
     } else {
-        dyra::DecodeArgs<E> a{X, B, n, p->c1, p->c2, p->kw, p->kc, p->k, p->lambda, Aext, Vs, Wres_t, Y,
+        dyra::DecodeArgs<E> a{X, B, n, p->c1, p->c2, p->kw, p->kc, p->k, p->lambda, (const E *)p->Adec,
+                              (const E *)p->Vdec, (const E *)p->Wdec, Y,
                               ws + L.dual, flags, bias, alpha};
         if ((s = hip_status(dyra::launch_decode_project<E>(a, st))) != DYRA_OK) return s;
         if ((s = mark()) != DYRA_OK) return s;
@@ -516,6 +542,13 @@ dyra_status dyra_prepare_ex(const float *W, int64_t c1, int64_t c2, int32_t r, i
     if ((s = upload(A, &p->Aext)) == DYRA_OK && (s = upload(V, &p->Vs)) == DYRA_OK)
         s = upload(Rt, &p->Wres_t);
     if (s == DYRA_OK && p->half_steps > 2) s = upload(f.W_res, &p->Wres);
+    if (s == DYRA_OK && kc > 0 && (s = upload(frag_tile(Rt, c2, c1), &p->Wdec)) == DYRA_OK &&
+        (s = upload(frag_tile(V, c2, kw), &p->Vdec)) == DYRA_OK) {
+        const int64_t rows = (kw + kc + 31) / 32 * 32;
+        std::vector<double> Ap(A);
+        Ap.resize((size_t)rows * c1, 0.0);
+        s = upload(frag_tile(Ap, rows, c1), &p->Adec);
+    }
     if (s == DYRA_OK) s = prepare_launches(dtype, device);
     if (prev >= 0) (void)hipSetDevice(prev);
     if (s != DYRA_OK) {
@@ -613,6 +646,9 @@ void dyra_plan_destroy(dyra_plan *plan) {
     if (plan->Vs) (void)hipFree(plan->Vs);
     if (plan->Wres_t) (void)hipFree(plan->Wres_t);
     if (plan->Wres) (void)hipFree(plan->Wres);
+    if (plan->Wdec) (void)hipFree(plan->Wdec);
+    if (plan->Vdec) (void)hipFree(plan->Vdec);
+    if (plan->Adec) (void)hipFree(plan->Adec);
     if (plan->Ublk) (void)hipFree(plan->Ublk);
     if (plan->Smix) (void)hipFree(plan->Smix);
     if (prev >= 0) (void)hipSetDevice(prev);

@@ -20,9 +20,9 @@ template <typename E> struct DecodeArgs {
     int64_t B, n, c1, c2;
     int kw, kc, k_real;
     float lambda;
-    const E *Aext;    // [kw + kc][c1]
-    const E *Vs;      // [c2][kw]
-    const E *Wres_t;  // [c2][c1]
+    const E *Aext;    // [kw + kc][c1] in MFMA fragment order, rows padded with zeros to a multiple of 32
+    const E *Vs;      // [c2][kw] V_s in MFMA fragment order (512-element blocks of 32 rows x 16 deep)
+    const E *Wres_t;  // [c2][c1] W_res^T in the same order
     E *Y;             // [B*n][c2]
     char *ws;         // dual-form workspace (decode_workspace_bytes)
     int *flags;       // [B]

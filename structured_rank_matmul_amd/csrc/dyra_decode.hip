@@ -45,7 +45,7 @@ int z_splits(int64_t c1, int64_t c2) {
 }
 
 struct DualLayout {
-    size_t partial, T, coef, zpart, total;
+    size_t partial, T, coef, zpart, Xt, Tt, total;
     int splits, zsplits;
 };
 
@@ -65,8 +65,24 @@ DualLayout dual_layout(int64_t B, int64_t n, int64_t c1, int64_t c2, int kw, int
     off += al(sizeof(float) * (size_t)B * n * n);
     L.zpart = off;
     off += al(sizeof(float) * (size_t)L.zsplits * N * c2);
+    // X and T_s in MFMA fragment order (frag_index), whole 32-row blocks, at
+    // most 4 bytes per element
+    const size_t rows32 = (size_t)((N + 31) / 32) * 32;
+    L.Xt = off;
+    off += al(sizeof(float) * rows32 * (size_t)c1);
+    L.Tt = off;
+    off += al(sizeof(float) * rows32 * (size_t)kw);
     L.total = off;
     return L;
+}
+
+// Element (row, col) of a [rows][K] matrix stored in MFMA fragment order: the
+// 32 x 16 block (row block, 16-deep step) is 512 consecutive elements, lane
+// 32 h + r holding row r of the block, columns 8 h .. 8 h + 7 of the step.
+// A wavefront that walks the contraction of one row block then reads one
+// contiguous run, each lane's 8 elements already an MFMA operand.
+__device__ __forceinline__ int64_t frag_index(int64_t row, int64_t col, int64_t K) {
+    return ((row >> 5) * (K >> 4) + (col >> 4)) * 512 + (((col >> 3) & 1) * 32 + (row & 31)) * 8 + (col & 7);
 }
 
 // Fragment of 8 consecutive elements from a float32 row, converted to E.
@@ -94,7 +110,7 @@ template <typename F> __device__ __forceinline__ F keep_if(bool ok, const F &f) 
 template <typename E, bool TWO>
 __global__ __launch_bounds__(NT) void decode_project_kernel(const E *__restrict__ X, const E *__restrict__ Aext,
                                                             int64_t N, int64_t c1, int K1, int splits,
-                                                            float *__restrict__ partial) {
+                                                            float *__restrict__ partial, E *__restrict__ Xt) {
     __shared__ float red[NT / 64][kRowBlock * 32];  // each wavefront's partial [row][col]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 31, lk = (lane >> 5) * 8;
@@ -108,7 +124,8 @@ __global__ __launch_bounds__(NT) void decode_project_kernel(const E *__restrict_
     const bool col_ok = col < K1;
     const int64_t ra = row0 + lr, rb = row0 + 32 + lr;
     const bool a_ok = ra < N, b_ok = rb < N;
-    const E *pb = Aext + (int64_t)(col_ok ? col : 0) * c1 + lk;
+    // [A_s | P_L] in fragment order: the 32-column block's run, 1 KB per load
+    const E *pb = Aext + (int64_t)(col0 / 32) * 32 * c1 + 8 * lane;
     const E *pa0 = X + (a_ok ? ra : row0) * c1 + lk;
     const E *pa1 = X + (b_ok ? rb : row0) * c1 + lk;
     typedef typename Frag<E>::type F;
@@ -124,7 +141,7 @@ __global__ __launch_bounds__(NT) void decode_project_kernel(const E *__restrict_
             const int64_t k = k0 + 16 * u;
             const bool kin = k < we;
             const int64_t kk = kin ? k : kbeg;
-            fb[u] = keep_if(kin && col_ok, ld_frag(pb + kk));
+            fb[u] = keep_if(kin && col_ok, ld_frag(pb + 32 * kk));
             fa0[u] = keep_if(kin && a_ok, ld_frag(pa0 + kk));
             if constexpr (TWO) fa1[u] = keep_if(kin && b_ok, ld_frag(pa1 + kk));
         }
@@ -132,6 +149,17 @@ __global__ __launch_bounds__(NT) void decode_project_kernel(const E *__restrict_
         for (int u = 0; u < kUnroll; ++u) {
             acc[0] = mma16(acc[0], fa0[u], fb[u]);
             if constexpr (TWO) acc[1] = mma16(acc[1], fa1[u], fb[u]);
+        }
+        // the first column block also leaves X in fragment order for the
+        // W_res stream (decode_z_kernel): every element once
+        if (blockIdx.x == 0) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t k = k0 + 16 * u;
+                if (k >= we) continue;
+                if (a_ok) *reinterpret_cast<F *>(Xt + frag_index(ra, k + lk, c1)) = fa0[u];
+                if (TWO && b_ok) *reinterpret_cast<F *>(Xt + frag_index(rb, k + lk, c1)) = fa1[u];
+            }
         }
     }
 #pragma unroll
@@ -157,7 +185,7 @@ __global__ __launch_bounds__(NT) void decode_project_kernel(const E *__restrict_
 template <typename E>
 __global__ __launch_bounds__(NT) void decode_coef_kernel(const float *__restrict__ partial, int64_t N, int64_t n,
                                                          int K1, int kw, int k_real, int splits, float lambda,
-                                                         float *__restrict__ T, float *__restrict__ coef,
+                                                         float *__restrict__ T, E *__restrict__ Tt, float *__restrict__ coef,
                                                          int *__restrict__ flags) {
     __shared__ double K[16][16];
     __shared__ double V[16][16];
@@ -190,6 +218,7 @@ __global__ __launch_bounds__(NT) void decode_coef_kernel(const float *__restrict
             for (int q = 0; q < kMaxSplits; ++q) s += q < splits ? v[j][q] : 0.f;
             T[(r0 + i) * K1 + c] = s;
             if (c >= kw) Ls[i][c - kw] = s;
+            else Tt[frag_index(r0 + i, c, kw)] = to_elem<E>(s);
         }
     }
     __syncthreads();
@@ -277,7 +306,7 @@ constexpr int kWideTokens = 64;
 template <typename E>
 __global__ __launch_bounds__(NT) void decode_coef_wide_kernel(const float *__restrict__ partial, int64_t N,
                                                               int64_t n, int K1, int kw, int k_real, int splits,
-                                                              float *__restrict__ T, float *__restrict__ coef,
+                                                              float *__restrict__ T, E *__restrict__ Tt, float *__restrict__ coef,
                                                               int *__restrict__ flags) {
     constexpr int KS = kMaxCorr + 1;
     constexpr int MS = kWideTokens + 1;
@@ -302,6 +331,7 @@ __global__ __launch_bounds__(NT) void decode_coef_wide_kernel(const float *__res
         for (int q = 0; q < splits; ++q) s += partial[((int64_t)q * N + r0 + i) * K1 + c];
         T[(r0 + i) * K1 + c] = s;
         if (c >= kw) Ls[i][c - kw] = s;
+        else Tt[frag_index(r0 + i, c, kw)] = to_elem<E>(s);
     }
     if (tid < kWideTokens) done[tid] = 0;
     __syncthreads();
@@ -404,12 +434,12 @@ __global__ __launch_bounds__(NT) void decode_coef_wide_kernel(const float *__res
 }
 
 // Z = X W_res in split-K parts: Zp[s][row][col] = sum over the s-th of S
-// equal splits of c1 of X[row][k] W_res[k][col] (W_res stored transposed,
-// [c2][c1]).  Grid (c2 / 64, S, row blocks of 64).  Each wavefront streams a
-// contiguous quarter of the split for all 64 columns of the block and every
-// row of it: its W_res loads cover whole 128-byte lines, and the small X
-// operand is read from L2 once per 64 output columns.  The wavefronts'
-// partial sums meet in LDS.  Bound by the single pass over W_res (HBM); the
+// equal splits of c1 of X[row][k] W_res[k][col] (W_res^T in fragment order,
+// see DecodeArgs).  Grid (c2 / 64, S, row blocks of 64).  Each wavefront
+// streams a contiguous quarter of the split for all 64 columns of the block
+// and every row of it: each load of W_res, and of the small X operand (in
+// fragment order too, read from L2 once per 64 output columns), reads 1 KB of
+// consecutive bytes.  The wavefronts' partial sums meet in LDS.  Bound by the single pass over W_res (HBM); the
 // split keeps every compute unit streaming when c2 is narrow (the down
 // projection).
 template <typename E, bool TWO>
@@ -427,8 +457,16 @@ __global__ __launch_bounds__(NT) void decode_z_kernel(const E *__restrict__ X, c
     const bool c0_ok = c0 < c2, c1_ok = c1b < c2;
     const int64_t ra = row0 + lr, rb = row0 + 32 + lr;
     const bool a_ok = ra < N, b_ok = rb < N;
-    const E *pb0 = Wres_t + (c0_ok ? c0 : 0) * c1 + lk, *pb1 = Wres_t + (c1_ok ? c1b : 0) * c1 + lk;
-    const E *pa0 = X + (a_ok ? ra : row0) * c1 + lk, *pa1 = X + (b_ok ? rb : row0) * c1 + lk;
+    // W_res^T in fragment order: block (32-column block cb, 16-deep step ks)
+    // at element 512 (cb c1 / 16 + ks); this lane's 8 elements at 8 lane
+    const int64_t cb0 = col0 / 32, cb1 = c1_ok ? cb0 + 1 : cb0;
+    const E *pb0 = Wres_t + cb0 * 32 * c1 + 8 * lane, *pb1 = Wres_t + cb1 * 32 * c1 + 8 * lane;
+    // X in fragment order (left by decode_project_kernel): the block's two
+    // 32-row blocks, the second clamped to the last one stored (its rows are
+    // masked)
+    const int64_t rblk = row0 / 32, nrb = (N + 31) / 32;
+    const E *pa0 = X + rblk * 32 * c1 + 8 * lane;
+    const E *pa1 = X + (rblk + 1 < nrb ? rblk + 1 : rblk) * 32 * c1 + 8 * lane;
     // this wavefront's contiguous quarter of split s (whole 16-deep steps)
     const int64_t ks = c1 / splits, kbeg = (int64_t)s * ks;
     const int64_t q4 = ((ks + 63) / 64) * 16;
@@ -444,10 +482,10 @@ __global__ __launch_bounds__(NT) void decode_z_kernel(const E *__restrict__ X, c
         for (int u = 0; u < U; ++u) {
             const int64_t k = k0 + 16 * u;
             const int64_t kk = k < ke ? k : kbeg;
-            b0[u] = ld_frag(pb0 + kk);
-            b1[u] = ld_frag(pb1 + kk);
-            a0[u] = ld_frag(pa0 + kk);
-            if constexpr (TWO) a1[u] = ld_frag(pa1 + kk);
+            b0[u] = ld_frag(pb0 + 32 * kk);
+            b1[u] = ld_frag(pb1 + 32 * kk);
+            a0[u] = ld_frag(pa0 + 32 * kk);
+            if constexpr (TWO) a1[u] = ld_frag(pa1 + 32 * kk);
         }
     };
     auto mma = [&](int64_t k0, const F (&b0)[U], const F (&b1)[U], const F (&a0)[U], const F (&a1)[U])
@@ -517,10 +555,10 @@ __global__ __launch_bounds__(NT) void decode_z_kernel(const E *__restrict__ X, c
 // and the quarters are reduced in LDS.
 template <typename E, bool TWO>
 __global__ __launch_bounds__(NT) void decode_output_kernel(const float *__restrict__ Zp, int zsplits,
-                                                           const float *__restrict__ T,
+                                                           const E *__restrict__ Tt,
                                                            const float *__restrict__ coef,
                                                            const E *__restrict__ Vs, int64_t N, int64_t n,
-                                                           int64_t c2, int K1, int kw, int64_t rows_blk,
+                                                           int64_t c2, int kw, int64_t rows_blk,
                                                            const E *__restrict__ bias, float alpha,
                                                            E *__restrict__ Y) {
     __shared__ float part[NT / 64][kRowBlock * 32];  // each wavefront's partial [row][col]
@@ -545,10 +583,15 @@ __global__ __launch_bounds__(NT) void decode_output_kernel(const float *__restri
         Zs[r][c] = z;
     }
     f32x16 s0 = f32x16{}, s1 = f32x16{};
-    const int64_t colc = col_ok ? col : 0, rac = a_ok ? ra : row0, rbc = b_ok ? rb : row0;
+    const int64_t rac = a_ok ? ra : row0, rbc = b_ok ? rb : row0;
     {
-        const E *pb = Vs + colc * kw + lk;
-        const float *pa0 = T + rac * K1 + lk, *pa1 = T + rbc * K1 + lk;
+        // V_s in fragment order: block (32-column block, 16-deep step k / 16)
+        // at element 512 (col0 / 32 * kw / 16 + k / 16)
+        const E *pb = Vs + (col0 / 32) * 32 * kw + 8 * lane;
+        // T_s in fragment order (left by the coefficient kernel); a row block
+        // of whole instances need not start on a 32-row boundary, so each
+        // lane addresses its own row
+        const E *pa0 = Tt + frag_index(rac, lk, kw), *pa1 = Tt + frag_index(rbc, lk, kw);
         const int q4 = ((kw + 63) / 64) * 16;
         const int vb = wave * q4 < kw ? wave * q4 : kw, ve = (wave + 1) * q4 < kw ? (wave + 1) * q4 : kw;
         for (int k0 = vb; k0 < ve; k0 += 16 * kUnroll) {
@@ -558,9 +601,9 @@ __global__ __launch_bounds__(NT) void decode_output_kernel(const float *__restri
                 const int k = k0 + 16 * u;
                 const bool kin = k < ve;
                 const int kk = kin ? k : 0;
-                fb[u] = keep_if(kin && col_ok, ld_frag(pb + kk));
-                fa0[u] = keep_if(kin && a_ok, frag_from_f32(pa0 + kk, E{}));
-                if constexpr (TWO) fa1[u] = keep_if(kin && b_ok, frag_from_f32(pa1 + kk, E{}));
+                fb[u] = keep_if(kin && col_ok, ld_frag(pb + 32 * kk));
+                fa0[u] = keep_if(kin && a_ok, ld_frag(pa0 + 32 * kk));
+                if constexpr (TWO) fa1[u] = keep_if(kin && b_ok, ld_frag(pa1 + 32 * kk));
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
@@ -608,10 +651,10 @@ template <typename E> hipError_t launch_decode_project(const DecodeArgs<E> &a, h
     dim3 grid((unsigned)((K1 + 31) / 32), (unsigned)L.splits, (unsigned)((N + kRowBlock - 1) / kRowBlock));
     if (N > 32)
         hipLaunchKernelGGL((decode_project_kernel<E, true>), grid, dim3(NT), 0, st, a.X, a.Aext, N, a.c1, K1,
-                           L.splits, (float *)(a.ws + L.partial));
+                           L.splits, (float *)(a.ws + L.partial), (E *)(a.ws + L.Xt));
     else
         hipLaunchKernelGGL((decode_project_kernel<E, false>), grid, dim3(NT), 0, st, a.X, a.Aext, N, a.c1, K1,
-                           L.splits, (float *)(a.ws + L.partial));
+                           L.splits, (float *)(a.ws + L.partial), (E *)(a.ws + L.Xt));
     return hipGetLastError();
 }
 
@@ -622,12 +665,12 @@ template <typename E> hipError_t launch_decode_coef(const DecodeArgs<E> &a, hipS
         if (a.n > kWideTokens || a.lambda != 0.f || a.kc > kMaxCorr) return hipErrorInvalidValue;
         hipLaunchKernelGGL((decode_coef_wide_kernel<E>), dim3((unsigned)a.B), dim3(NT), 0, st,
                            (const float *)(a.ws + L.partial), N, a.n, a.kw + a.kc, a.kw, a.k_real, L.splits,
-                           (float *)(a.ws + L.T), (float *)(a.ws + L.coef), a.flags);
+                           (float *)(a.ws + L.T), (E *)(a.ws + L.Tt), (float *)(a.ws + L.coef), a.flags);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((decode_coef_kernel<E>), dim3((unsigned)a.B), dim3(NT), 0, st,
                        (const float *)(a.ws + L.partial), N, a.n, a.kw + a.kc, a.kw, a.k_real, L.splits, a.lambda,
-                       (float *)(a.ws + L.T), (float *)(a.ws + L.coef), a.flags);
+                       (float *)(a.ws + L.T), (E *)(a.ws + L.Tt), (float *)(a.ws + L.coef), a.flags);
     return hipGetLastError();
 }
 
@@ -639,11 +682,11 @@ template <typename E> hipError_t launch_decode_output(const DecodeArgs<E> &a, hi
     const dim3 zgrid((unsigned)((a.c2 + kZCols - 1) / kZCols), (unsigned)L.zsplits,
                      (unsigned)((N + kRowBlock - 1) / kRowBlock));
     if (N > 32)
-        hipLaunchKernelGGL((decode_z_kernel<E, true>), zgrid, dim3(NT), 0, st, a.X, a.Wres_t, N, a.c1, a.c2,
-                           L.zsplits, Zp);
+        hipLaunchKernelGGL((decode_z_kernel<E, true>), zgrid, dim3(NT), 0, st, (const E *)(a.ws + L.Xt), a.Wres_t,
+                           N, a.c1, a.c2, L.zsplits, Zp);
     else
-        hipLaunchKernelGGL((decode_z_kernel<E, false>), zgrid, dim3(NT), 0, st, a.X, a.Wres_t, N, a.c1, a.c2,
-                           L.zsplits, Zp);
+        hipLaunchKernelGGL((decode_z_kernel<E, false>), zgrid, dim3(NT), 0, st, (const E *)(a.ws + L.Xt),
+                           a.Wres_t, N, a.c1, a.c2, L.zsplits, Zp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t rb = rows_per_block(a.n);
@@ -651,12 +694,12 @@ template <typename E> hipError_t launch_decode_output(const DecodeArgs<E> &a, hi
     // the second 32-row MFMA block only when some row block has rows there
     if (std::min<int64_t>(rb, N) > 32)
         hipLaunchKernelGGL((decode_output_kernel<E, true>), grid, dim3(NT), 0, st, (const float *)Zp, L.zsplits,
-                           (const float *)(a.ws + L.T), (const float *)(a.ws + L.coef), a.Vs, N, a.n, a.c2,
-                           a.kw + a.kc, a.kw, rb, a.bias, a.alpha, a.Y);
+                           (const E *)(a.ws + L.Tt), (const float *)(a.ws + L.coef), a.Vs, N, a.n, a.c2,
+                           a.kw, rb, a.bias, a.alpha, a.Y);
     else
         hipLaunchKernelGGL((decode_output_kernel<E, false>), grid, dim3(NT), 0, st, (const float *)Zp, L.zsplits,
-                           (const float *)(a.ws + L.T), (const float *)(a.ws + L.coef), a.Vs, N, a.n, a.c2,
-                           a.kw + a.kc, a.kw, rb, a.bias, a.alpha, a.Y);
+                           (const E *)(a.ws + L.Tt), (const float *)(a.ws + L.coef), a.Vs, N, a.n, a.c2,
+                           a.kw, rb, a.bias, a.alpha, a.Y);
     return hipGetLastError();
 }
 
