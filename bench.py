@@ -97,13 +97,13 @@ def dual_form(spec, n):
 # kernel behind each stage of the primal path (for the roofline record)
 STAGE_KERNEL = {
     "left": "gemm_kernel (T = X [A_s | P_L])",
-    "gram_q": "gram_chol_kernel + q_apply_kernel",
+    "gram_q": "gram_chol_kernel (+ q_apply_kernel for n > 256 or k > 64)",
     "mprime": "mprime_tr_kernel",
     "right": "gemm_kernel (R1 = M' W_res, R1t store)",
     "output": "gemm_kernel with correction slices (Y = T_s V_s^T + Q R1_b)",
     "decode_project": "decode_project_kernel ([X A_s | L1], split-K)",
     "decode_coef": "decode_coef_kernel (n x n Gram and eigen-solve per instance)",
-    "decode_output": "decode_output_kernel (Y = T_s V_s^T + blockdiag(C) X W_res)",
+    "decode_output": "decode_z_kernel + decode_output_kernel (Y = T_s V_s^T + blockdiag(C) X W_res)",
 }
 TRAFFIC_FILE = {"output": "profiles/output_gemm_{workload}_traffic.txt"}
 

@@ -121,7 +121,8 @@ template <int KC> constexpr int gram_tokens() { return gram_kp<KC>() <= 64 ? 256
 //     loses C_below C_below^T, formed on float32 MFMA from the panel staged in
 //     LDS.
 // C is stored column by column, Ct[b][m][i] = C[i][m] (i > m), Ct[b][m][m] =
-// 1 / C[m][m], zero above: the order q_apply_kernel reads it in.  The kernel
+// 1 / C[m][m], zero above: the order q_apply_kernel reads it in (not with FUSE,
+// which needs no second launch).  The kernel
 // only reads T; Q is formed by a later launch, so no workgroup sees rows
 // another one rewrites.
 // GONLY: stop after G, written whole (both triangles) to Gw for the
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(NT) void gram_chol_kernel(const bf16 *T, int64_t ld
                 for (int m = 0; m < 32; ++m) {
                     if (p0 + m < KC) {
                         const float c = m < lane ? g[m] : (m == lane ? __builtin_amdgcn_rcpf(g[m]) : 0.f);
-                        Cb_[(p0 + m) * KC + i] = c;
+                        if constexpr (!FUSE) Cb_[(p0 + m) * KC + i] = c;  // for q_apply_kernel
                         if constexpr (FUSE) Cs[i * CSS + p0 + m] = c;
                         if (Cout && m <= lane) Cout[(b * KC + i) * KC + p0 + m] = (double)g[m];
                     }
@@ -315,7 +316,7 @@ __global__ __launch_bounds__(NT) void gram_chol_kernel(const bf16 *T, int64_t ld
 #pragma unroll
                     for (int m = 0; m < 32; ++m) {
                         if (p0 + m < KC) {
-                            Cb_[(p0 + m) * KC + rl] = l[m];
+                            if constexpr (!FUSE) Cb_[(p0 + m) * KC + rl] = l[m];
                             if constexpr (FUSE) Cs[rl * CSS + p0 + m] = l[m];
                             if (Cout) Cout[(b * KC + rl) * KC + p0 + m] = (double)l[m];
                         }
