@@ -21,12 +21,14 @@ namespace {
 constexpr int NT = 256;
 constexpr int kRowBlock = 64;  // rows (tokens) per workgroup, two 32-row MFMA blocks
 
-constexpr int kMaxSplits = 4;  // split-K parts of the projection (16 measured slower overall)
+constexpr int kMaxSplits = 8;  // split-K parts of the projection (16 measured slower overall)
 constexpr int kMaxCorr = 256;   // largest padded correction rank
 
 int decode_splits(int64_t c1) {
     int s = 1;
-    while (s < kMaxSplits && c1 % (32 * 2 * s) == 0 && c1 / (2 * s) >= 256) s *= 2;
+    // eight parts only for long contractions (c1 >= 8192: the down projection,
+    // whose 34 column blocks leave most compute units idle at four)
+    while (s < kMaxSplits && c1 % (32 * 2 * s) == 0 && c1 / (2 * s) >= (s < 4 ? 256 : 1024)) s *= 2;
     return s;
 }
 
@@ -150,16 +152,15 @@ __global__ __launch_bounds__(NT) void decode_project_kernel(const E *__restrict_
             acc[0] = mma16(acc[0], fa0[u], fb[u]);
             if constexpr (TWO) acc[1] = mma16(acc[1], fa1[u], fb[u]);
         }
-        // the first column block also leaves X in fragment order for the
-        // W_res stream (decode_z_kernel): every element once
-        if (blockIdx.x == 0) {
+        // X also goes to the workspace in fragment order for the W_res stream
+        // (decode_z_kernel): each 16-deep step by one column block (dealt
+        // round-robin, so the stores spread over the grid), every element once
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int64_t k = k0 + 16 * u;
-                if (k >= we) continue;
-                if (a_ok) *reinterpret_cast<F *>(Xt + frag_index(ra, k + lk, c1)) = fa0[u];
-                if (TWO && b_ok) *reinterpret_cast<F *>(Xt + frag_index(rb, k + lk, c1)) = fa1[u];
-            }
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t k = k0 + 16 * u;
+            if (k >= we || (k >> 4) % gridDim.x != blockIdx.x) continue;
+            if (a_ok) *reinterpret_cast<F *>(Xt + frag_index(ra, k + lk, c1)) = fa0[u];
+            if (TWO && b_ok) *reinterpret_cast<F *>(Xt + frag_index(rb, k + lk, c1)) = fa1[u];
         }
     }
 #pragma unroll

@@ -245,23 +245,24 @@ def test_forward_empty_batch_is_noop():
     assert Y.shape == (0, 64)
 
 
-def test_failed_solve_is_flagged():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_failed_solve_is_flagged(dtype):
     """lambda = 0 and an all-zero instance: L1 = 0, the Gram matrix is singular;
     that instance is flagged and gets no correction (its exact output is 0)."""
     import torch
     B, n, c1, c2, r, k = 4, 20, 64, 96, 8, 8
     W = synth.random_weight(c1, c2, 42)
-    X = synth.random_matrix(B * n, c1, 43, "bf16")
+    X = synth.random_matrix(B * n, c1, 43, dtype)
     X.data[n:2 * n] = 0
     X.data[3 * n:] = 0
-    plan = dyra.dyra_prepare(W, r, k, 0.0, "bf16", 0)
+    plan = dyra.dyra_prepare(W, r, k, 0.0, dtype, 0)
     ws = dyra.alloc_workspace(plan, B, n)
     Y = dyra.dyra_forward(to_device(X), B, n, plan, workspace=ws)
     assert dyra.dyra_forward_status(plan, B, n, ws) == 2
     y = to_host(Y)
     assert np.all(y[n:2 * n] == 0) and np.all(y[3 * n:] == 0)
     ref = orc.inference(X.exact, B, n, oracle_plan(W, r, k, 0.0))
-    check_parity(y, ref, n, "bf16", "zero instances")
+    check_parity(y, ref, n, dtype, "zero instances")
     torch.cuda.synchronize()
 
 
