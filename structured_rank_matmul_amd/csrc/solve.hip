@@ -630,11 +630,11 @@ __global__ __launch_bounds__(NT) void gram_q_f32_small_kernel(float *__restrict_
             if (tid == 0) sh_fail = 1;
             pk = 1.0;
         }
-        const double d = sqrt(pk), rp = 1.0 / pk;
+        const double d = sqrt(pk), rd = 1.0 / d, rp = rd * rd;
 #pragma unroll
         for (int u = 0; u < EPT; ++u) {
             const int i = iu[u];
-            if (j == m && i >= m) g[u] = (i == m) ? d : g[u] / d;    // C[i][m]
+            if (j == m && i >= m) g[u] = (i == m) ? d : g[u] * rd;   // C[i][m]
             else if (j > m && i >= j) g[u] -= cm[i] * cm[j] * rp;   // trailing update
         }
     }
@@ -708,17 +708,24 @@ __global__ __launch_bounds__(NT) void mprime_f32_small_kernel(const float *__res
     for (int i = 0; i < KP; ++i) acc[i] = 0.f;
     for (int64_t t0 = 0; t0 < n; t0 += TC) {
         // this part's tokens of the chunk (past n: token n - 1, weighted by
-        // the zero rows of Qt or skipped)
-        float x[TP];
+        // the zero rows of Qt or skipped), and the chunk's Q_b entries for the
+        // stage, all requested before any is used (one memory latency per chunk)
+        float x[TP], qv[TC * KP / NT];
 #pragma unroll
         for (int u = 0; u < TP; ++u) {
             const int64_t t = t0 + p + (NT / 64) * u;
             x[u] = Xb[(t < n ? t : n - 1) * c1];
         }
+#pragma unroll
+        for (int u = 0; u < TC * KP / NT; ++u) {
+            const int e = u * NT + tid, i = e / TC, tt = e % TC;  // consecutive threads: consecutive tokens
+            qv[u] = Qb[i * npad + (t0 + tt < npad ? t0 + tt : 0)];
+        }
         __syncthreads();  // the previous chunk's reads are done
-        for (int e = tid; e < TC * KP; e += NT) {
-            const int i = e / TC, tt = e % TC;  // consecutive threads: consecutive tokens of row i
-            Qs[tt * QS + i] = t0 + tt < npad ? Qb[i * npad + t0 + tt] : 0.f;
+#pragma unroll
+        for (int u = 0; u < TC * KP / NT; ++u) {
+            const int e = u * NT + tid, i = e / TC, tt = e % TC;
+            Qs[tt * QS + i] = t0 + tt < npad ? qv[u] : 0.f;
         }
         __syncthreads();
         const int tc = (int)(n - t0 < TC ? n - t0 : TC);
