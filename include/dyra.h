@@ -93,7 +93,10 @@ dyra_status dyra_factorize_host(const float *W, int64_t c1, int64_t c2, int32_t 
  * r + k <= min(c1, c2) and k <= 256 (k <= 64 for DYRA_F32; DYRA_ERR_SHAPE
  * otherwise); k = 0 gives the weight-only product X A_s V_s^T, and
  * r = min(c1, c2), k = 0 the exact product up to rounding.
- * On success *plan_out owns device memory until dyra_plan_destroy.
+ * On success *plan_out owns device memory until dyra_plan_destroy: for k > 0,
+ * W_res^T, V_s and [A_s | P_L] twice (row-major for the primal path, and in
+ * MFMA fragment order for the dual form of short instances), about
+ * 2 (c1 c2 + (r + k) c1 + c2 r) elements of `dtype`.
  */
 dyra_status dyra_prepare(const float *W, int64_t c1, int64_t c2, int32_t r, int32_t k,
                          float lambda, dyra_dtype dtype, int device, dyra_plan **plan_out);
