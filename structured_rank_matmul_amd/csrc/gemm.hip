@@ -584,9 +584,85 @@ hipError_t launch_shape(Shape shape, const E *A, int64_t lda, const E *B, int64_
     return hipErrorInvalidValue;
 }
 
+// Float32 products of only a few tiles (a single instance of a few hundred
+// tokens).  There a 64 x 64 tile's wavefronts each run the whole contraction
+// through one chain of v_mfma_f32_32x32x2f32 (64 cycles each, K / 2 of them),
+// so the product takes that chain's time on a handful of CUs.  Here a
+// workgroup owns one 32 x 32 block and its four wavefronts split the 16-deep
+// steps between them (step s to wavefront s % 4); their partial blocks meet in
+// LDS and wavefront 0 applies the epilogue.  Operands are read straight from
+// global memory in fragment form, kSmallGroup steps requested at once.
+constexpr int kSmallWaves = 4;
+constexpr int kSmallGroup = 3;
+
+template <bool ROWS, class Epi>
+__global__ __launch_bounds__(64 * kSmallWaves) void small_gemm_f32_kernel(const float *__restrict__ A, int64_t lda,
+                                                                          const float *__restrict__ B, int64_t ldb,
+                                                                          int64_t M, int64_t N, int64_t K, Epi epi) {
+    __shared__ float red[kSmallWaves - 1][16][64];  // partial blocks of wavefronts 1..3, [register][lane]
+    __shared__ __align__(16) float cts[32];         // the block's per-column terms
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 31, hf = lane >> 5;
+    const int64_t row0 = (int64_t)blockIdx.y * 32, col0 = (int64_t)blockIdx.x * 32;
+    // rows past M or N are read from the last row and never stored
+    const int64_t ra = row0 + lr < M ? row0 + lr : M - 1, rb = col0 + lr < N ? col0 + lr : N - 1;
+    const float *pa = A + ra * lda + 8 * hf, *pb = B + rb * ldb + 8 * hf;
+    bool has_ct = false;
+    if constexpr (Epi::kColumnTerms) {
+        has_ct = epi.bias != nullptr;
+        if (has_ct && tid < 32) cts[tid] = col0 + tid < epi.ncols ? to_f32(epi.bias[col0 + tid]) : 0.f;
+    }
+    const int S = (int)(K / 16);
+    f32x16 acc = f32x16{};
+    for (int s0 = wave; s0 < S; s0 += kSmallWaves * kSmallGroup) {
+        f32x8 fa[kSmallGroup], fb[kSmallGroup];
+#pragma unroll
+        for (int u = 0; u < kSmallGroup; ++u) {
+            const int s = s0 + kSmallWaves * u;
+            const int64_t k = 16 * (int64_t)(s < S ? s : s0);  // a step past the end re-reads s0 and is skipped
+            fa[u] = ld_frag(pa + k);
+            fb[u] = ld_frag(pb + k);
+        }
+#pragma unroll
+        for (int u = 0; u < kSmallGroup; ++u)
+            if (s0 + kSmallWaves * u < S) acc = ROWS ? mma16(acc, fb[u], fa[u]) : mma16(acc, fa[u], fb[u]);
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) red[wave - 1][t][lane] = acc[t];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < kSmallWaves - 1; ++w)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) acc[t] += red[w][t][lane];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        float v[4] = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+        const int64_t r = ROWS ? row0 + lr : row0 + acc_row(lane, 4 * g);
+        const int64_t c = ROWS ? col0 + acc_row(lane, 4 * g) : col0 + lr;
+        epi.fix4(v, r, c, has_ct ? cts + (c - col0) : nullptr);
+        if (r < M && c < N) epi.store4(r, c, pack4<float>(v));
+    }
+}
+
+// The 64 x 64 tiles of a product that leaves most CUs idle take the small
+// kernel instead (float32 only: a bf16 MFMA's chain is eight times shorter).
+constexpr int64_t kSmallMaxTiles = 32;
+
 template <typename E, bool ROWS, bool CORR, bool GROUPED = false, class Epi>
 hipError_t gemm_dispatch(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N, int64_t K,
                          const Corr<E> &corr, Epi epi, hipStream_t st) {
+    if constexpr (sizeof(E) == 4 && !CORR && !GROUPED) {
+        if (((M + 63) / 64) * ((N + 63) / 64) <= kSmallMaxTiles) {
+            if (K % 16 != 0) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((small_gemm_f32_kernel<ROWS, Epi>), dim3((unsigned)((N + 31) / 32), (unsigned)((M + 31) / 32)),
+                               dim3(64 * kSmallWaves), 0, st, A, lda, B, ldb, M, N, K, epi);
+            return hipGetLastError();
+        }
+    }
     Shape shape;
     if (!pick_shape(M, N, GROUPED ? corr.gcols : 0, shape)) return hipErrorInvalidValue;
     return launch_shape<E, ROWS, CORR, GROUPED>(shape, A, lda, B, ldb, M, N, K, corr, epi, st, false);
