@@ -681,77 +681,70 @@ __global__ __launch_bounds__(NT) void gram_q_f32_small_kernel(float *__restrict_
     }
 }
 
-// M'_b = Q_b^T X_b for float32 at correction ranks 16 and 32: workgroup (64
-// input features, instance b).  Thread (feature f, part p) sums tokens p,
-// p + 4, ... of its feature into all KP rows; per 256-token chunk it requests
-// its 64 entries of X at once (one memory latency per chunk), while Q_b's
-// rows of the chunk are staged token by token in LDS (every lane of a
-// wavefront reads the same token: broadcasts).  The four parts meet in LDS.
+// M'_b = Q_b^T X_b for float32 at correction ranks 16 and 32, on MFMA:
+// workgroup (32 input features, instance b) forms the 32-feature slab of
+// M'_b as one 32 x 32 block (correction rows i >= KP of it unused).  Its four
+// wavefronts take the 16-token steps s = w, w + 4, ... (tokens past n are X's
+// last row against Q_b's zero padding) and their partial blocks meet in LDS.
+// A lane's X fragment is 8 tokens of one feature (consecutive lanes take
+// consecutive features: one 128-byte segment of a token row per load); its Q
+// fragment is 8 consecutive tokens of one row of Q_b^T as stored.  The single
+// instance of a few hundred tokens is a latency problem: the scalar form (one
+// thread per feature and token part) left 6 workgroups each a 64-token chain
+// of 16 or 32 FMAs per token.
 template <int KP>
-__global__ __launch_bounds__(NT) void mprime_f32_small_kernel(const float *__restrict__ X, const float *__restrict__ Qt,
-                                                              int64_t n, int64_t npad, int64_t c1,
-                                                              float *__restrict__ Mp) {
+__global__ __launch_bounds__(NT) void mprime_f32_mfma_kernel(const float *__restrict__ X, const float *__restrict__ Qt,
+                                                             int64_t n, int64_t npad, int64_t c1,
+                                                             float *__restrict__ Mp) {
     static_assert(KP == 16 || KP == 32, "correction rank");
-    constexpr int TC = 256;     // tokens per staged chunk
-    constexpr int TP = TC / (NT / 64);  // tokens of a part per chunk
-    constexpr int QS = KP + 4;  // row stride (floats) of a staged token
-    __shared__ __align__(16) float Qs[TC * QS];
-    __shared__ float red[NT / 64][KP][64];
-    const int tid = threadIdx.x, f = tid & 63, p = tid >> 6;
+    constexpr int NW = NT / 64;
+    constexpr int G = 3;  // steps whose loads are requested together
+    __shared__ float red[NW - 1][16][64];  // partial blocks of wavefronts 1.., [register][lane]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 31, hf = lane >> 5;
     const int64_t b = blockIdx.y;
-    const int64_t col = (int64_t)blockIdx.x * 64 + f;
-    const bool col_ok = col < c1;
-    const float *const Xb = X + b * n * c1 + (col_ok ? col : 0);
-    const float *const Qb = Qt + b * KP * npad;
-    float acc[KP];
+    const int64_t c0 = (int64_t)blockIdx.x * 32;
+    // features past c1 read the last one, rows past KP the last row of Q_b^T:
+    // neither is stored
+    const float *const px = X + b * n * c1 + (c0 + lr < c1 ? c0 + lr : c1 - 1);
+    const float *const pq = Qt + (b * KP + (lr < KP ? lr : KP - 1)) * npad + 8 * hf;
+    const int S = (int)(npad / 16);
+    f32x16 acc = f32x16{};
+    for (int s0 = wave; s0 < S; s0 += NW * G) {
+        f32x8 fx[G], fq[G];
 #pragma unroll
-    for (int i = 0; i < KP; ++i) acc[i] = 0.f;
-    for (int64_t t0 = 0; t0 < n; t0 += TC) {
-        // this part's tokens of the chunk (past n: token n - 1, weighted by
-        // the zero rows of Qt or skipped), and the chunk's Q_b entries for the
-        // stage, all requested before any is used (one memory latency per chunk)
-        float x[TP], qv[TC * KP / NT];
+        for (int u = 0; u < G; ++u) {
+            const int s = s0 + NW * u;
+            const int64_t t0 = 16 * (int64_t)(s < S ? s : s0) + 8 * hf;  // a step past the end is skipped
 #pragma unroll
-        for (int u = 0; u < TP; ++u) {
-            const int64_t t = t0 + p + (NT / 64) * u;
-            x[u] = Xb[(t < n ? t : n - 1) * c1];
-        }
-#pragma unroll
-        for (int u = 0; u < TC * KP / NT; ++u) {
-            const int e = u * NT + tid, i = e / TC, tt = e % TC;  // consecutive threads: consecutive tokens
-            qv[u] = Qb[i * npad + (t0 + tt < npad ? t0 + tt : 0)];
-        }
-        __syncthreads();  // the previous chunk's reads are done
-#pragma unroll
-        for (int u = 0; u < TC * KP / NT; ++u) {
-            const int e = u * NT + tid, i = e / TC, tt = e % TC;
-            Qs[tt * QS + i] = t0 + tt < npad ? qv[u] : 0.f;
-        }
-        __syncthreads();
-        const int tc = (int)(n - t0 < TC ? n - t0 : TC);
-#pragma unroll
-        for (int u = 0; u < TP; ++u) {
-            const int t = p + (NT / 64) * u;
-            if (t >= tc) break;
-            const float *qr = Qs + t * QS;
-#pragma unroll
-            for (int v = 0; v < KP / 4; ++v) {
-                const f32x4 q = *reinterpret_cast<const f32x4 *>(qr + 4 * v);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[4 * v + e] = fmaf(q[e], x[u], acc[4 * v + e]);
+            for (int e = 0; e < 8; ++e) {
+                const int64_t t = t0 + e;
+                fx[u][e] = px[(t < n ? t : n - 1) * c1];
             }
+            fq[u] = ld_frag(pq + (t0 - 8 * hf));
         }
+        // output row: feature c0 + acc_row; output column: correction row lr
+#pragma unroll
+        for (int u = 0; u < G; ++u)
+            if (s0 + NW * u < S) acc = mma16(acc, fx[u], fq[u]);
     }
+    if (wave > 0) {
 #pragma unroll
-    for (int i = 0; i < KP; ++i) red[p][i][f] = acc[i];
+        for (int t = 0; t < 16; ++t) red[wave - 1][t][lane] = acc[t];
+    }
     __syncthreads();
-    for (int e = tid; e < KP * 64; e += NT) {
-        const int i = e / 64, ff = e % 64;
-        const int64_t c = (int64_t)blockIdx.x * 64 + ff;
-        float s = 0.f;
+    if (wave != 0 || lr >= KP) return;
 #pragma unroll
-        for (int q = 0; q < NT / 64; ++q) s += red[q][i][ff];
-        if (c < c1) Mp[(b * KP + i) * c1 + c] = s;
+    for (int w = 0; w < NW - 1; ++w)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) acc[t] += red[w][t][lane];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int64_t c = c0 + acc_row(lane, 4 * g);  // four consecutive features of row lr
+        if (c < c1)
+            *reinterpret_cast<f32x4 *>(Mp + (b * KP + lr) * c1 + c) =
+                f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
     }
 }
 
@@ -1248,11 +1241,12 @@ hipError_t launch_mprime<float>(const float *X, const float *, int64_t, int64_t,
                                 int64_t n, int64_t npad, int64_t c1, int kc, float *Mp, hipStream_t st) {
     if (B <= 0) return hipSuccess;
     if (kc == 16 || kc == 32) {
-        const dim3 grid((unsigned)((c1 + 63) / 64), (unsigned)B);
+        if (npad % 16 != 0) return hipErrorInvalidValue;
+        const dim3 grid((unsigned)((c1 + 31) / 32), (unsigned)B);
         if (kc == 16)
-            hipLaunchKernelGGL(mprime_f32_small_kernel<16>, grid, dim3(NT), 0, st, X, Qt, n, npad, c1, Mp);
+            hipLaunchKernelGGL(mprime_f32_mfma_kernel<16>, grid, dim3(NT), 0, st, X, Qt, n, npad, c1, Mp);
         else
-            hipLaunchKernelGGL(mprime_f32_small_kernel<32>, grid, dim3(NT), 0, st, X, Qt, n, npad, c1, Mp);
+            hipLaunchKernelGGL(mprime_f32_mfma_kernel<32>, grid, dim3(NT), 0, st, X, Qt, n, npad, c1, Mp);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((mprime_kernel<float>), dim3((unsigned)((c1 + 255) / 256), (unsigned)B), dim3(NT), 0, st, X,
