@@ -595,10 +595,15 @@ hipError_t launch_shape(Shape shape, const E *A, int64_t lda, const E *B, int64_
 constexpr int kSmallWaves = 4;
 constexpr int kSmallGroup = 3;
 
-template <bool ROWS, class Epi>
+//
+// With CORR the output product's correction steps follow the static ones as
+// in gemm_kernel: for each instance b with rows in the block, kc / 16 steps of
+// A's correction columns (rows of other instances zeroed) against R1_b.
+template <bool ROWS, bool CORR, class Epi>
 __global__ __launch_bounds__(64 * kSmallWaves) void small_gemm_f32_kernel(const float *__restrict__ A, int64_t lda,
                                                                           const float *__restrict__ B, int64_t ldb,
-                                                                          int64_t M, int64_t N, int64_t K, Epi epi) {
+                                                                          int64_t M, int64_t N, int64_t K,
+                                                                          Corr<float> corr, Epi epi) {
     __shared__ float red[kSmallWaves - 1][16][64];  // partial blocks of wavefronts 1..3, [register][lane]
     __shared__ __align__(16) float cts[32];         // the block's per-column terms
     const int tid = threadIdx.x, lane = tid & 63;
@@ -613,16 +618,34 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_gemm_f32_kernel(const 
         has_ct = epi.bias != nullptr;
         if (has_ct && tid < 32) cts[tid] = col0 + tid < epi.ncols ? to_f32(epi.bias[col0 + tid]) : 0.f;
     }
-    const int S = (int)(K / 16);
+    const int S0 = (int)(K / 16);
+    int S = S0, SC = 1;
+    int64_t b_first = 0;
+    if constexpr (CORR) {
+        const int64_t rend = row0 + 32 < M ? row0 + 32 : M;
+        b_first = row0 / corr.n;
+        SC = corr.kc / 16;
+        S = S0 + (int)((rend - 1) / corr.n - b_first + 1) * SC;
+    }
     f32x16 acc = f32x16{};
     for (int s0 = wave; s0 < S; s0 += kSmallWaves * kSmallGroup) {
         f32x8 fa[kSmallGroup], fb[kSmallGroup];
 #pragma unroll
         for (int u = 0; u < kSmallGroup; ++u) {
             const int s = s0 + kSmallWaves * u;
-            const int64_t k = 16 * (int64_t)(s < S ? s : s0);  // a step past the end re-reads s0 and is skipped
-            fa[u] = ld_frag(pa + k);
-            fb[u] = ld_frag(pb + k);
+            const int sl = s < S ? s : s0;  // a step past the end re-reads s0 and is skipped
+            if (!CORR || sl < S0) {
+                fa[u] = ld_frag(pa + 16 * (int64_t)sl);
+                fb[u] = ld_frag(pb + 16 * (int64_t)sl);
+            } else {
+                const int q = sl - S0, j = q % SC;
+                const int64_t b = b_first + q / SC;
+                const int64_t kk = 16 * (int64_t)j + 8 * hf;
+                fa[u] = ld_frag(A + ra * lda + corr.kcol + kk);
+                const int64_t r = row0 + lr;
+                if (!(r >= b * corr.n && r < (b + 1) * corr.n)) fa[u] = f32x8{};
+                fb[u] = ld_frag(corr.R1t + b * corr.rstride + rb * corr.kc + kk);
+            }
         }
 #pragma unroll
         for (int u = 0; u < kSmallGroup; ++u)
@@ -655,11 +678,13 @@ constexpr int64_t kSmallMaxTiles = 32;
 template <typename E, bool ROWS, bool CORR, bool GROUPED = false, class Epi>
 hipError_t gemm_dispatch(const E *A, int64_t lda, const E *B, int64_t ldb, int64_t M, int64_t N, int64_t K,
                          const Corr<E> &corr, Epi epi, hipStream_t st) {
-    if constexpr (sizeof(E) == 4 && !CORR && !GROUPED) {
+    if constexpr (sizeof(E) == 4 && !GROUPED) {
         if (((M + 63) / 64) * ((N + 63) / 64) <= kSmallMaxTiles) {
-            if (K % 16 != 0) return hipErrorInvalidValue;
-            hipLaunchKernelGGL((small_gemm_f32_kernel<ROWS, Epi>), dim3((unsigned)((N + 31) / 32), (unsigned)((M + 31) / 32)),
-                               dim3(64 * kSmallWaves), 0, st, A, lda, B, ldb, M, N, K, epi);
+            if (K % 16 != 0 || (CORR && (corr.n < 1 || corr.kc < 16 || corr.kc % 16 != 0)))
+                return hipErrorInvalidValue;
+            hipLaunchKernelGGL((small_gemm_f32_kernel<ROWS, CORR, Epi>),
+                               dim3((unsigned)((N + 31) / 32), (unsigned)((M + 31) / 32)), dim3(64 * kSmallWaves), 0,
+                               st, A, lda, B, ldb, M, N, K, corr, epi);
             return hipGetLastError();
         }
     }

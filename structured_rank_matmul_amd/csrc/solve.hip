@@ -649,14 +649,17 @@ __global__ __launch_bounds__(NT) void gram_q_f32_small_kernel(float *__restrict_
     const bool dead = sh_fail != 0;
     if (tid == 0) flags[b] = dead ? 1 : 0;
 
-    // ---- 3. q_t = C^-1 l_t, one token per thread
+    // ---- 3. q_t = C^-1 l_t, one token per thread (from the staged rows when
+    // the instance was one chunk: npad <= TC then, and rows past n are zeros)
     float *const Qb = Qt + b * KP * npad;
+    const bool staged = n <= TC && npad <= TC;
     for (int64_t t = tid; t < npad; t += NT) {
         double q[KP];
         const bool in = t < n;
 #pragma unroll
         for (int v = 0; v < V4; ++v) {
-            f32x4 x = *reinterpret_cast<const f32x4 *>(Lb + (in ? t : n - 1) * ldt + 4 * v);
+            f32x4 x = staged ? *reinterpret_cast<const f32x4 *>(&Ls[t * KP + 4 * v])
+                             : *reinterpret_cast<const f32x4 *>(Lb + (in ? t : n - 1) * ldt + 4 * v);
 #pragma unroll
             for (int e = 0; e < 4; ++e) q[4 * v + e] = in ? (double)x[e] : 0.0;
         }
