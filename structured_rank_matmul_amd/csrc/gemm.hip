@@ -592,13 +592,12 @@ hipError_t launch_shape(Shape shape, const E *A, int64_t lda, const E *B, int64_
 // steps between them (step s to wavefront s % 4); their partial blocks meet in
 // LDS and wavefront 0 applies the epilogue.  Operands are read straight from
 // global memory in fragment form, kSmallGroup steps requested at once.
-constexpr int kSmallWaves = 4;
-constexpr int kSmallGroup = 3;
-
-//
 // With CORR the output product's correction steps follow the static ones as
 // in gemm_kernel: for each instance b with rows in the block, kc / 16 steps of
 // A's correction columns (rows of other instances zeroed) against R1_b.
+constexpr int kSmallWaves = 4;
+constexpr int kSmallGroup = 3;
+
 template <bool ROWS, bool CORR, class Epi>
 __global__ __launch_bounds__(64 * kSmallWaves) void small_gemm_f32_kernel(const float *__restrict__ A, int64_t lda,
                                                                           const float *__restrict__ B, int64_t ldb,
@@ -672,7 +671,8 @@ __global__ __launch_bounds__(64 * kSmallWaves) void small_gemm_f32_kernel(const 
 }
 
 // The 64 x 64 tiles of a product that leaves most CUs idle take the small
-// kernel instead (float32 only: a bf16 MFMA's chain is eight times shorter).
+// kernel instead (float32 only: a 16-deep bf16 step is one MFMA where float32
+// needs eight).
 constexpr int64_t kSmallMaxTiles = 32;
 
 template <typename E, bool ROWS, bool CORR, bool GROUPED = false, class Epi>
