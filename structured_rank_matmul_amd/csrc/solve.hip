@@ -535,9 +535,10 @@ __global__ __launch_bounds__(64 * token_lanes<KC>()) void q_apply_kernel(bf16 *_
 // Correction ranks 16 and 32 (KP = kc): one workgroup per instance, every
 // step that decides Q_b in float64, none of it serial beyond the k pivots.
 //  1. G = L1_b^T L1_b: token chunks of 256 rows staged in LDS as stored;
-//     thread tid owns the entries tid + 256 u of G (row-major), summing their
-//     products over the chunk (a product of two float32 values is exact in
-//     float64).
+//     each thread sums one 4 x 4 block of G over every (256 / blocks)-th
+//     token of the chunk, and the partial G's are added in LDS, thread tid
+//     then owning the entries tid + 256 u of G (row-major) (a product of two
+//     float32 values is exact in float64).
 //  2. Cholesky G + lambda I = C C^T, right-looking: column m of the trailing
 //     matrix goes through LDS, one barrier per column.
 //  3. Q_b = L1_b C^-T by forward substitution, one token per thread, the
@@ -566,9 +567,15 @@ __global__ __launch_bounds__(NT) void gram_q_f32_small_kernel(float *__restrict_
     int iu[EPT];
 #pragma unroll
     for (int u = 0; u < EPT; ++u) iu[u] = (tid + NT * u) / KP;
-    double g[EPT], g2[EPT];
+    // G by 4 x 4 blocks: thread (token group tg, block (bi, bj)) sums its block
+    // over tokens tg, tg + TG, ... of each staged chunk, two 16-byte LDS reads
+    // per token for 16 independent float64 FMAs; the TG partial G's meet in LDS
+    constexpr int NB4 = KP / 4, NBLK = NB4 * NB4, TG = NT / NBLK;
+    __shared__ double part[TG][KP * KP];
+    const int blk = tid % NBLK, tg = tid / NBLK, bi = blk / NB4, bj = blk % NB4;
+    double gb[16];
 #pragma unroll
-    for (int u = 0; u < EPT; ++u) g[u] = g2[u] = 0.0;
+    for (int e = 0; e < 16; ++e) gb[e] = 0.0;
     if (tid == 0) sh_fail = 0;
 
     // ---- 1. G
@@ -582,25 +589,30 @@ __global__ __launch_bounds__(NT) void gram_q_f32_small_kernel(float *__restrict_
             *reinterpret_cast<f32x4 *>(&Ls[tok * KP + 4 * q]) = v;
         }
         __syncthreads();
-        // tokens past n were staged as zeros: whole groups of 8, two sums per
-        // entry, so that LDS reads are batched and the float64 FMAs of
-        // consecutive tokens do not wait on each other
         const int tc = (int)(n - t0 < TC ? n - t0 : TC);
-        for (int t = 0; t < tc; t += 8) {
+#pragma unroll 4
+        for (int t = tg; t < tc; t += TG) {
+            const f32x4 ri = *reinterpret_cast<const f32x4 *>(&Ls[t * KP + 4 * bi]);
+            const f32x4 rj = *reinterpret_cast<const f32x4 *>(&Ls[t * KP + 4 * bj]);
 #pragma unroll
-            for (int h = 0; h < 8; ++h) {
-                const float *row = Ls + (t + h) * KP;
-                const double lj = (double)row[j];
+            for (int a = 0; a < 4; ++a)
 #pragma unroll
-                for (int u = 0; u < EPT; ++u) {
-                    if (h & 1) g2[u] = fma((double)row[iu[u]], lj, g2[u]);
-                    else g[u] = fma((double)row[iu[u]], lj, g[u]);
-                }
-            }
+                for (int c = 0; c < 4; ++c) gb[4 * a + c] = fma((double)ri[a], (double)rj[c], gb[4 * a + c]);
         }
     }
 #pragma unroll
-    for (int u = 0; u < EPT; ++u) g[u] += g2[u];
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) part[tg][(4 * bi + a) * KP + 4 * bj + c] = gb[4 * a + c];
+    __syncthreads();
+    double g[EPT];
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+        double sum = 0.0;
+#pragma unroll
+        for (int q = 0; q < TG; ++q) sum += part[q][tid + NT * u];
+        g[u] = sum;
+    }
     // lambda on the real diagonal, identity on the padding
 #pragma unroll
     for (int u = 0; u < EPT; ++u) {
